@@ -1,0 +1,375 @@
+"""Pins of the fp64 oracle against what the pages and the mathematics fix.
+
+Each test checks the oracle against something other than itself: a closed
+form, an equation printed on the pages evaluated by a different route, a
+brute-force solve, a hand-derived example, or an invariant the pages state.
+"""
+import os
+
+import numpy as np
+import pytest
+from scipy.linalg import solve_triangular
+
+import oracle
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rand_spd(d, rng, cond=1e3):
+    Q, _ = np.linalg.qr(rng.standard_normal((d, d)))
+    ev = np.geomspace(1.0, cond, d)
+    return (Q * ev) @ Q.T
+
+
+def _tiny_X(d=16, n=64, seed=0):
+    rng = np.random.default_rng(seed)
+    X = (rng.standard_normal((n, 4)) @ rng.standard_normal((4, d)) + 0.1 * rng.standard_normal((n, d)))
+    return X.astype(np.float16)
+
+
+# ---------------------------------------------------------------- H = 2XX^T
+def test_hessian_equals_sum_of_token_outer_products():
+    """Closed form: H[i,j] = 2 * sum_t x_t[i] x_t[j], written as an explicit
+    per-token, per-entry loop (no matrix product)."""
+    X = _tiny_X(d=6, n=20)
+    d = X.shape[1]
+    ref = [[0.0] * d for _ in range(d)]
+    for t in range(X.shape[0]):
+        row = [float(v) for v in X[t]]
+        for i in range(d):
+            for j in range(d):
+                ref[i][j] += 2.0 * row[i] * row[j]
+    chunks = [X[:7], X[7:8], X[8:20]]
+    H = oracle.hessian(chunks, d)
+    np.testing.assert_allclose(H, np.array(ref), rtol=1e-12, atol=0)
+    assert H.shape == (d, d)
+
+
+def test_hessian_additive_over_chunks_and_alpha():
+    X = _tiny_X(d=8, n=40, seed=1)
+    H1 = oracle.hessian([X], 8)
+    H2 = oracle.hessian([X[:13], X[13:13], X[13:]], 8)
+    np.testing.assert_allclose(H1, H2, rtol=1e-13)
+    np.testing.assert_allclose(oracle.hessian([X], 8, alpha=1.0) * 2.0, H1, rtol=1e-15)
+    assert np.all(oracle.hessian([], 8) == 0)
+
+
+# ---------------------------------------------------------------- damping
+def test_damping_adds_lambda_to_the_diagonal_only():
+    rng = np.random.default_rng(2)
+    H = _rand_spd(10, rng)
+    H[3, :] = 0
+    H[:, 3] = 0  # a dead channel
+    Hd, lam = oracle.damp(H, 0.01)
+    assert lam == pytest.approx(0.01 * np.trace(H) / 10, rel=1e-15)
+    off = ~np.eye(10, dtype=bool)
+    assert np.array_equal(Hd[off], H[off])
+    np.testing.assert_allclose(np.diag(Hd) - np.diag(H), lam, rtol=1e-12)
+    assert Hd[3, 3] == lam
+
+
+def test_not_pd_reports_first_dead_channel():
+    rng = np.random.default_rng(3)
+    H = _rand_spd(12, rng)
+    for c in (5, 9):
+        H[c, :] = 0
+        H[:, c] = 0
+    with pytest.raises(oracle.NotPositiveDefinite) as ei:
+        oracle.hinv_upper(H, 0.0)
+    assert ei.value.info == 6
+    U, lam = oracle.hinv_upper(H, 0.01)  # damping repairs it
+    assert np.all(np.diag(U) > 0)
+    Hn = H.copy()
+    Hn[0, 0] = np.nan
+    with pytest.raises(oracle.NotPositiveDefinite) as ei:
+        oracle.hinv_upper(Hn, 0.01)
+    assert ei.value.info == 1
+
+
+# ---------------------------------------------------------------- Hinv
+@pytest.mark.parametrize("d", [1, 5, 64])
+def test_hinv_is_upper_factor_of_inverse(d):
+    rng = np.random.default_rng(d)
+    H = _rand_spd(d, rng, cond=1e4)
+    U, lam = oracle.hinv_upper(H, 0.01)
+    Hd = H + lam * np.eye(d)
+    assert np.all(np.tril(U, -1) == 0)
+    assert np.all(np.diag(U) > 0)
+    kappa = np.linalg.cond(Hd)
+    # U^T U = Hd^{-1}  <=>  U^T U Hd = I
+    assert np.abs(U.T @ U @ Hd - np.eye(d)).max() <= 1e-13 * kappa * d
+
+
+def test_hinv_of_diagonal_hessian_is_inverse_sqrt():
+    h = np.array([4.0, 1.0, 9.0, 0.25])
+    U, lam = oracle.hinv_upper(np.diag(h), 0.0)
+    np.testing.assert_allclose(U, np.diag(1 / np.sqrt(h)), rtol=1e-15)
+
+
+def test_hinv_rows_are_the_successive_downdated_inverses():
+    """Page "GPTQ: fixing errors as you go", section "The OBQ update": removing
+    q from the inverse is one Gaussian-elimination step, and the sequence of
+    downdated inverses is given by the rows of the Cholesky factor. Run the
+    elimination literally and compare row q with U[q,q] * U[q, q:]."""
+    rng = np.random.default_rng(7)
+    d = 9
+    H = _rand_spd(d, rng, cond=50)
+    U, lam = oracle.hinv_upper(H, 0.01)
+    M = np.linalg.inv(H + lam * np.eye(d))  # general inverse, not Cholesky
+    for q in range(d):
+        np.testing.assert_allclose(M[0, :], U[q, q] * U[q, q:], rtol=1e-10, atol=1e-14)
+        M = (M - np.outer(M[:, 0], M[0, :]) / M[0, 0])[1:, 1:]
+
+
+def test_hinv_matches_reversed_cholesky_route():
+    """An independent route: H_d = V V^T with V upper (Cholesky of the index-
+    reversed matrix) gives H_d^{-1} = V^{-T} V^{-1}, so U = V^{-1}."""
+    rng = np.random.default_rng(11)
+    d = 40
+    H = _rand_spd(d, rng, cond=1e3)
+    U, lam = oracle.hinv_upper(H, 0.01)
+    Hd = H + lam * np.eye(d)
+    V = np.linalg.cholesky(Hd[::-1, ::-1])[::-1, ::-1]
+    assert np.allclose(np.tril(V, -1), 0)
+    U2 = solve_triangular(V, np.eye(d), lower=False)
+    np.testing.assert_allclose(U, U2, rtol=1e-10, atol=1e-12 * np.abs(U).max())
+
+
+# ---------------------------------------------------------------- quantizer
+def test_quantizer_hand_cases():
+    # one row: min -1, max 2, 2 bits -> s = 1, z = 1
+    s, z = oracle.group_params(np.array([[-1.0, 0.5, 2.0]]), 2)
+    assert s[0] == 1.0 and z[0] == 1.0
+    # ties go to even: 0.5/1 + 1 = 1.5 -> 2 ; -0.5 + 1 = 0.5 -> 0 ; 1.5 + 1 = 2.5 -> 2
+    q = [oracle.quantize(np.array([w]), s, z, 2)[0] for w in (0.5, -0.5, 1.5)]
+    assert q == [2.0, 0.0, 2.0]
+    # clamping to [0, qmax]
+    assert oracle.quantize(np.array([10.0]), s, z, 2)[0] == 3
+    assert oracle.quantize(np.array([-10.0]), s, z, 2)[0] == 0
+    # min > 0: zero point clamps to 0, grid [0, 3s] does not reach max
+    s, z = oracle.group_params(np.array([[3.0, 6.0]]), 2)
+    assert s[0] == 1.0 and z[0] == 0.0
+    assert oracle.quantize(np.array([6.0]), s, z, 2)[0] == 3
+    # max < 0: zero point clamps to qmax
+    s, z = oracle.group_params(np.array([[-9.0, -6.0]]), 2)
+    assert s[0] == 1.0 and z[0] == 3.0
+    assert oracle.quantize(np.array([-9.0]), s, z, 2)[0] == 0
+    # constant group: scale floors at 1e-8
+    for prec in ("f64", "f32"):
+        s, z = oracle.group_params(np.array([[0.0, 0.0, 0.0]]), 4, prec)
+        assert s[0] == pytest.approx(1e-8, rel=1e-7) and z[0] == 0.0
+
+
+def test_quantizer_f32_decision_uses_ieee_single():
+    """In f32 mode the grid position is the IEEE single-precision w/s + z."""
+    rng = np.random.default_rng(5)
+    G = rng.standard_normal((200, 16)) * 0.02
+    s, z = oracle.group_params(G, 4, "f32")
+    s32 = ((G.astype(np.float32).max(1) - G.astype(np.float32).min(1)) / np.float32(15))
+    assert np.array_equal(s, np.maximum(s32, np.float32(1e-8)).astype(np.float64))
+    w = G[:, 3]
+    t = (w.astype(np.float32) / s.astype(np.float32) + z.astype(np.float32))
+    assert np.array_equal(oracle.quantize(w, s, z, 4, "f32"), np.clip(np.rint(t), 0, 15))
+
+
+# ---------------------------------------------------------------- the sweep
+def _load_golden():
+    vals = {}
+    with open(os.path.join(GOLDEN, "gptq_3col.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            k, *v = line.split()
+            vals[k] = [float(x) for x in v]
+    return vals
+
+
+@pytest.mark.parametrize("precision", ["f64", "f32"])
+@pytest.mark.parametrize("B", [1, 2, 3, 128])
+def test_hand_derived_three_column_example(precision, B):
+    g = _load_golden()
+    H = np.array(g["H"]).reshape(3, 3)
+    W = np.array([g["W"]])
+    U, lam = oracle.hinv_upper(H, 0.0)
+    assert lam == 0
+    np.testing.assert_allclose(U, np.array(g["U"]).reshape(3, 3), rtol=1e-14, atol=1e-15)
+    r = oracle.gptq(W, U, bits=2, groupsize=3, blocksize=B, precision=precision)
+    assert r["codes"][0].tolist() == [int(c) for c in g["codes"]]
+    assert r["scales"][0, 0] == pytest.approx(g["scale"][0], rel=1e-7 if precision == "f32" else 1e-15)
+    assert r["zeros"][0, 0] == g["zero"][0]
+    np.testing.assert_allclose(r["losses"], g["losses"], rtol=1e-5 if precision == "f32" else 1e-12)
+    assert r["losses"].sum() == pytest.approx(g["loss_total"][0], rel=1e-5 if precision == "f32" else 1e-12)
+    rt = oracle.rtn(W, bits=2, groupsize=3, precision=precision)
+    assert rt["codes"][0].tolist() == [int(c) for c in g["rtn_codes"]]
+
+
+def test_compensation_matches_bruteforce_obs_solve():
+    """For d <= 4: after columns P = {0..q} are fixed at their quantized
+    values, the remaining weights must equal the exact minimizer of the
+    quadratic 1/2 (w - w0) H_d (w - w0)^T over the free columns F:
+        w_F = w0_F - H_FF^{-1} H_FP (w_hat_P - w0_P).
+    Solved with a general linear solve, not through the Cholesky factor."""
+    rng = np.random.default_rng(13)
+    for d in (2, 3, 4):
+        for trial in range(5):
+            H = _rand_spd(d, rng, cond=30)
+            U, lam = oracle.hinv_upper(H, 0.01)
+            Hd = H + lam * np.eye(d)
+            W = rng.standard_normal((6, d))
+            for B in (1, 128):
+                r = oracle.gptq(W, U, bits=2, groupsize=d, blocksize=B, trace=True)
+                What = oracle.dequantize(r["codes"], r["scales"], r["zeros"], d)
+                for q in range(d - 1):
+                    P = list(range(q + 1))
+                    F = list(range(q + 1, d))
+                    dP = What[:, P] - W[:, P]
+                    wF = W[:, F] - np.linalg.solve(Hd[np.ix_(F, F)], Hd[np.ix_(F, P)] @ dP.T).T
+                    np.testing.assert_allclose(r["trace"][q][:, F], wF, rtol=1e-10, atol=1e-12)
+
+
+def test_first_step_is_the_obq_delta():
+    """Page "GPTQ: fixing errors as you go", OBQ update: the change of the free
+    weights after quantizing w_q is -(w_q - quant(w_q)) / [H^-1]_qq * H^-1[:, q]."""
+    rng = np.random.default_rng(17)
+    d = 5
+    H = _rand_spd(d, rng, cond=20)
+    U, lam = oracle.hinv_upper(H, 0.01)
+    Hi = np.linalg.inv(H + lam * np.eye(d))
+    W = rng.standard_normal((3, d))
+    r = oracle.gptq(W, U, bits=3, groupsize=d, blocksize=128, trace=True)
+    What0 = (r["codes"][:, 0] - r["zeros"][:, 0]) * r["scales"][:, 0]
+    delta = -np.outer((W[:, 0] - What0) / Hi[0, 0], Hi[1:, 0])
+    np.testing.assert_allclose(r["trace"][0][:, 1:] - W[:, 1:], delta, rtol=1e-10, atol=1e-13)
+
+
+def test_losses_sum_to_damped_objective():
+    """Sum of per-column OBS increases = 1/2 dw H_d dw^T, and that equals
+    ||dW X^T||^2 + lambda/2 ||dW||^2 for H = 2 X^T X (token-major X)."""
+    L = synth.LAYERS["tiny"]
+    X = synth.activations(L.x)
+    W = synth.weights(L.w)
+    H = oracle.hessian([X], L.x.d)
+    U, lam = oracle.hinv_upper(H, 0.01)
+    r = oracle.gptq(W, U, 4, 128, 128)
+    What = oracle.dequantize(r["codes"], r["scales"], r["zeros"], 128)
+    Hd = H + lam * np.eye(L.x.d)
+    obj = oracle.layer_objective(W, What, Hd).sum()
+    assert r["losses"].sum() == pytest.approx(obj, rel=1e-10)
+    dW = W.astype(np.float64) - What
+    direct = np.sum((dW @ X.astype(np.float64).T) ** 2) + 0.5 * lam * np.sum(dW ** 2)
+    assert obj == pytest.approx(direct, rel=1e-9)
+    assert oracle.output_error(W, What, H) == pytest.approx(np.sum((dW @ X.astype(np.float64).T) ** 2), rel=1e-9)
+
+
+@pytest.mark.parametrize("precision", ["f64", "f32"])
+def test_diagonal_hessian_gives_rtn(precision):
+    rng = np.random.default_rng(19)
+    d = 256
+    H = np.diag(rng.uniform(0.1, 10.0, d))
+    W = rng.standard_normal((32, d)) * 0.02
+    U, _ = oracle.hinv_upper(H, 0.01)
+    r = oracle.gptq(W, U, 4, 128, 128, precision=precision)
+    rt = oracle.rtn(W, 4, 128, precision=precision)
+    assert np.array_equal(r["codes"], rt["codes"])
+    assert np.array_equal(r["scales"], rt["scales"])
+    assert np.array_equal(r["zeros"], rt["zeros"])
+
+
+@pytest.mark.parametrize("d,g", [(64, 32), (256, 32), (256, 128), (200, 32)])
+def test_blocksize_does_not_change_the_result(d, g):
+    """Page "GPTQ, Line by Line", blocks-of-128 question: the blocksize is an
+    efficiency device only; in exact arithmetic the result is the same."""
+    L = synth.LAYERS["tiny"]
+    x = L.x.scaled(d=d, n=4 * d, rank=16)
+    X = synth.activations(x)
+    W = synth.weights(L.w.scaled(rows=24, cols=d))
+    U, _ = oracle.hinv_upper(oracle.hessian([X], d), 0.01)
+    ref = oracle.gptq(W, U, 3, g, 128)
+    for B in (1, 2, 4, 8, 32):
+        r = oracle.gptq(W, U, 3, g, B)
+        assert np.array_equal(r["codes"], ref["codes"]), B
+        np.testing.assert_allclose(r["scales"], ref["scales"], rtol=1e-9)
+        np.testing.assert_allclose(r["zeros"], ref["zeros"], rtol=1e-9)
+        np.testing.assert_allclose(r["losses"], ref["losses"], rtol=1e-9, atol=1e-18)
+
+
+def test_dead_channel_is_plain_rounding_and_passes_nothing_on():
+    L = synth.LAYERS["tiny"]
+    X = synth.activations(L.x).copy()
+    dead = 37
+    X[:, dead] = 0
+    W = synth.weights(L.w)
+    H = oracle.hessian([X], 256)
+    U, lam = oracle.hinv_upper(H, 0.01)
+    assert np.count_nonzero(U[dead, dead + 1:]) == 0 and np.count_nonzero(U[:dead, dead]) == 0
+    r = oracle.gptq(W, U, 4, 128, 128, trace=True)
+    s, z = r["scales"][:, 0], r["zeros"][:, 0]
+    # the dead column never receives compensation: its value when quantized is the original
+    np.testing.assert_array_equal(r["trace"][dead - 1][:, dead], W[:, dead].astype(np.float64))
+    assert np.array_equal(r["codes"][:, dead], oracle.quantize(W[:, dead], s, z, 4))
+    # and it pushes nothing to later columns
+    np.testing.assert_array_equal(r["trace"][dead][:, dead + 1:], r["trace"][dead - 1][:, dead + 1:])
+
+
+def test_positive_rescaling_of_H_keeps_codes():
+    L = synth.LAYERS["tiny"]
+    X = synth.activations(L.x)
+    W = synth.weights(L.w)
+    H = oracle.hessian([X], 256)
+    U, _ = oracle.hinv_upper(H, 0.01)
+    ref = oracle.gptq(W, U, 4, 128, 128)
+    for c in (0.25, 1 / 512.0, 3.7):
+        Uc, _ = oracle.hinv_upper(c * H, 0.01)
+        r = oracle.gptq(W, Uc, 4, 128, 128)
+        assert np.array_equal(r["codes"], ref["codes"])
+        np.testing.assert_allclose(r["scales"], ref["scales"], rtol=1e-12)
+        np.testing.assert_allclose(r["losses"] / c, ref["losses"], rtol=1e-9)
+
+
+def test_gptq_beats_rtn_on_the_tiny_layer():
+    """Not a theorem; the pages' point (page "GPTQ: fixing errors as you go",
+    sections "Try it" and "a 4-bit Llama layer") is that compensation lowers
+    the layer-output error versus plain rounding."""
+    L = synth.LAYERS["tiny"]
+    X = synth.activations(L.x)
+    W = synth.weights(L.w)
+    H = oracle.hessian([X], 256)
+    U, _ = oracle.hinv_upper(H, 0.01)
+    r = oracle.gptq(W, U, 4, 128, 128)
+    rt = oracle.rtn(W, 4, 128)
+    e_g = oracle.output_error(W, oracle.dequantize(r["codes"], r["scales"], r["zeros"], 128), H)
+    e_r = oracle.output_error(W, oracle.dequantize(rt["codes"], rt["scales"], rt["zeros"], 128), H)
+    assert e_g < e_r
+
+
+def test_ragged_last_group_and_block():
+    L = synth.LAYERS["tiny"]
+    d = 200
+    x = L.x.scaled(d=d, n=800, rank=16)
+    X = synth.activations(x)
+    W = synth.weights(L.w.scaled(rows=8, cols=d))
+    U, _ = oracle.hinv_upper(oracle.hessian([X], d), 0.01)
+    r = oracle.gptq(W, U, 4, 128, 128, trace=True)
+    assert r["scales"].shape == (8, 2)
+    assert np.all(r["codes"] >= 0) and np.all(r["codes"] <= 15)
+    # the short group's statistics come from its 72 current columns
+    G = r["trace"][127][:, 128:]
+    s, z = oracle.group_params(G, 4)
+    np.testing.assert_array_equal(r["scales"][:, 1], s)
+    np.testing.assert_array_equal(r["zeros"][:, 1], z)
+
+
+def test_tie_distance_marks_exact_ties():
+    # identity Hinv: no compensation. s = 1, z = 1: grid positions 0, 1.5, 3
+    r = oracle.gptq(np.array([[-1.0, 0.5, 2.0]]), np.eye(3), bits=2, groupsize=3, tie_distance=True)
+    np.testing.assert_allclose(r["tie_distance"][0], [0.5, 0.0, 0.5])
+
+
+@pytest.mark.parametrize("precision", ["f64", "f32"])
+def test_sweep_rounds_exact_ties_to_even(precision):
+    # identity Hinv (no compensation): s = 1, z = 1, grid positions 0, .5, 1.5, 2.5, 3
+    r = oracle.gptq(np.array([[-1.0, -0.5, 0.5, 1.5, 2.0]]), np.eye(5), bits=2, groupsize=5,
+                    precision=precision)
+    assert r["codes"][0].tolist() == [0, 0, 2, 2, 3]
