@@ -1,0 +1,182 @@
+/*
+ * gptq.h -- C ABI of the MI355X (gfx950) GPTQ one-layer library.
+ *
+ * GPTQ quantizes one linear layer's weights W (rows x cols, output x input
+ * features) column by column and, after each column, moves the columns not
+ * yet quantized so that the layer output on calibration inputs X changes as
+ * little as possible.  The library exposes the three stages of that path:
+ *
+ *   gptq_hessian_accumulate  H += alpha * X^T X     (alpha = 2 gives H = 2XX^T)
+ *   gptq_prepare_hinv        damp H, Cholesky, inverse, upper Cholesky -> Hinv
+ *   gptq_quantize_layer      blocked column sweep + lazy updates -> codes,
+ *                            scales, zeros, per-column losses
+ *
+ * Sources (page titles and sections):
+ *   "GPTQ: fixing errors as you go": "The algorithm, in words", "Objective",
+ *       "The OBQ update", "The tricks that make it fast".
+ *   "GPTQ > The GPTQ Algorithm": column-wise processing, lazy batch updates,
+ *       Cholesky-based inverse updates, the step-by-step procedure.
+ *   "GPTQ-style round-to-nearest with Hessian weighting": the
+ *       gptq_quantize_layer listing (quantizer) and collect_hessian listing.
+ *   "GPTQ, Line by Line: Hessian-Based Weight Quantization": Hessian,
+ *       percdamp, blocks of 128 and Cholesky questions.
+ *
+ * Conventions (all entry points):
+ *   - Matrices are row-major.  Every matrix pointer is a DEVICE pointer owned
+ *     by the caller; the library never allocates, frees or keeps a pointer
+ *     past the call.  Scalars and `info` are host values.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Work is enqueued on it in order; only gptq_prepare_hinv synchronizes it
+ *     (once, to read the pivot flag).
+ *   - `workspace` is caller-owned device memory of at least
+ *     gptq_workspace_bytes(op, ...) bytes, 256-byte aligned.  Its contents on
+ *     entry are ignored and on return undefined.  NULL is accepted when the
+ *     required size is 0.
+ *   - Every argument is validated on the host before any HIP call; an invalid
+ *     call returns an error status and enqueues nothing.  HIP launch errors
+ *     return GPTQ_ERR_HIP.
+ *   - No global mutable state: calls on different streams with different
+ *     buffers may run concurrently.  Calls that share a buffer must be ordered
+ *     by the caller.
+ */
+#ifndef GPTQ_MI355X_H
+#define GPTQ_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum gptq_status {
+  GPTQ_OK = 0,
+  GPTQ_ERR_INVALID_ARG = 1, /* null pointer, bad size, bad stride, bad bits ... */
+  GPTQ_ERR_WORKSPACE = 2,   /* workspace smaller than gptq_workspace_bytes()   */
+  GPTQ_ERR_NOT_PD = 3,      /* a Cholesky pivot was <= 0 or NaN (see *info)     */
+  GPTQ_ERR_HIP = 4,         /* a HIP runtime call or kernel launch failed       */
+  GPTQ_ERR_UNSUPPORTED = 5  /* valid request outside what the kernels handle    */
+} gptq_status;
+
+enum gptq_dtype { GPTQ_DTYPE_F16 = 0, GPTQ_DTYPE_F32 = 1 };
+
+enum gptq_op {
+  GPTQ_OP_ACCUMULATE = 0, /* sizes: rows ignored, cols = d, n = tokens         */
+  GPTQ_OP_PREPARE = 1,    /* sizes: rows ignored, cols = d, n ignored          */
+  GPTQ_OP_QUANTIZE = 2    /* sizes: rows, cols, n ignored                       */
+};
+
+/* Library version (major*10000 + minor*100 + patch). */
+int gptq_version(void);
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* gptq_status_string(int status);
+
+/* Bytes of device workspace the given operation needs at these sizes
+ * (0 if none).  Deterministic in its arguments; returns 0 for sizes the
+ * operation would reject. */
+size_t gptq_workspace_bytes(int op, int64_t rows, int64_t cols, int64_t n);
+
+/*
+ * gptq_hessian_accumulate -- H += alpha * X^T X.
+ *
+ * The Hessian of the layer-output error ||W X - W_hat X||^2 with respect to a
+ * row of W is 2 X X^T for X feature-major ("GPTQ: fixing errors as you go",
+ * "Objective"); calibration inputs are summed batch by batch
+ * ("GPTQ-style round-to-nearest ...", collect_hessian listing).  Here X is
+ * token-major, as a forward hook records it, so the same matrix is
+ * alpha * X^T X with alpha = 2.  H is NOT divided by the token count.
+ *
+ *   H      d x d fp32, both triangles updated (the result stays exactly
+ *          symmetric if H was).  The caller zero-initializes H before the
+ *          first chunk; successive calls add further token chunks.
+ *   d      number of input channels, >= 1.
+ *   X      n x d fp16 (IEEE binary16), row t at X + t*ldx.
+ *   n      tokens in this chunk, >= 0 (0 is a no-op).
+ *   ldx    row stride of X in elements, >= d.
+ *   alpha  scale applied to X^T X (2.0 for H = 2XX^T).
+ *   Products of fp16 values are exact in fp32; sums are accumulated in fp32
+ *   in an order that depends only on (d, n), so results are bitwise
+ *   reproducible.
+ */
+gptq_status gptq_hessian_accumulate(float* H, int64_t d, const void* X, int64_t n,
+                                    int64_t ldx, float alpha, void* workspace,
+                                    size_t workspace_bytes, void* stream);
+
+/*
+ * gptq_prepare_hinv -- Hinv = upper Cholesky factor of (H + lambda I)^{-1},
+ * lambda = percdamp * mean(diag H).
+ *
+ * Damping: "GPTQ, Line by Line", percdamp question (percdamp times the mean
+ * Hessian diagonal added to every diagonal entry).  The three-step route
+ * (Cholesky factor L of H_d, H_d^{-1} = L^{-T} L^{-1}, then the upper
+ * Cholesky factor of H_d^{-1}) follows the Cholesky question of the same page
+ * and the cholesky / cholesky_inverse / cholesky(upper) calls of the
+ * "GPTQ-style round-to-nearest ..." listing.  Row q of Hinv from column q on
+ * is the direction the error of column q is pushed along, and Hinv[q,q] its
+ * divisor ("GPTQ: fixing errors as you go", "The OBQ update").
+ *
+ *   H         d x d fp32 symmetric (only the lower triangle is read); not
+ *             modified.
+ *   percdamp  >= 0 (0.01 is the pages' default).
+ *   Hinv      d x d fp32 output: upper triangular, strict lower part set to 0.
+ *   info      host int64 out: 0 on success; on GPTQ_ERR_NOT_PD the 1-based
+ *             index of the first failing pivot, in [1, d] for the factor of
+ *             the damped H and in [d+1, 2d] for the factor of its inverse.
+ *             May be NULL.
+ *   The factorizations run in fp64 on the device; the result is rounded to
+ *   fp32 once.  The call synchronizes `stream` once (to read the pivot flag).
+ *   On GPTQ_ERR_NOT_PD the contents of Hinv are undefined.
+ */
+gptq_status gptq_prepare_hinv(const float* H, int64_t d, double percdamp, float* Hinv,
+                              void* workspace, size_t workspace_bytes, int64_t* info,
+                              void* stream);
+
+/*
+ * gptq_quantize_layer -- the GPTQ column sweep.
+ *
+ * Columns are processed left to right in one order shared by all rows, in
+ * blocks of `blocksize`; inside a block each quantized column's scaled error
+ * e = (w - w_hat) / Hinv[j,j] is applied at once to the block's remaining
+ * columns (rank-1 update along Hinv[j, j:]); when the block is done its errors
+ * Err1 are applied to all later columns at once, W[:, rest] -= Err1 *
+ * Hinv[block, rest] ("GPTQ > The GPTQ Algorithm", lazy batch updates;
+ * "GPTQ, Line by Line", blocks-of-128 question).  The quantizer is the
+ * asymmetric min/max grid per row and group of `groupsize` columns, with the
+ * statistics taken from the current (compensated) weights when the sweep
+ * reaches the group's first column ("GPTQ-style round-to-nearest ..."
+ * listing):
+ *     scale = max((max - min) / (2^bits - 1), 1e-8)
+ *     zero  = clamp(rint(-min / scale), 0, 2^bits - 1)
+ *     code  = clamp(rint(w / scale + zero), 0, 2^bits - 1)   (half to even)
+ *     w_hat = (code - zero) * scale
+ *
+ *   W          rows x cols, fp16 or fp32 (w_dtype), row r at W + r*ldw; not
+ *              modified (the working copy lives in the workspace).
+ *   ldw        row stride of W in elements, >= cols.
+ *   Hinv       cols x cols fp32 from gptq_prepare_hinv; only the upper
+ *              triangle (including the diagonal) is read.
+ *   bits       2..8.
+ *   groupsize  16, 32, 64 or a multiple of 128 (the last group may be
+ *              short when cols is not a multiple of groupsize).
+ *   blocksize  128.  Other values return GPTQ_ERR_UNSUPPORTED.  The result
+ *              does not depend on it in exact arithmetic.
+ *   codes      rows x cols uint8 out, values in [0, 2^bits - 1].
+ *   scales     rows x ceil(cols / groupsize) fp32 out.
+ *   zeros      rows x ceil(cols / groupsize) fp32 out (integer-valued).
+ *   losses     cols fp32 out: losses[j] = sum over rows of
+ *              (w - w_hat)^2 / (2 Hinv[j,j]^2), the increase of
+ *              1/2 dw H_d dw^T caused by quantizing column j.
+ *   Asynchronous; the sweep state is fp32.
+ */
+gptq_status gptq_quantize_layer(const void* W, int w_dtype, int64_t rows, int64_t cols,
+                                int64_t ldw, const float* Hinv, int bits, int groupsize,
+                                int blocksize, uint8_t* codes, float* scales, float* zeros,
+                                float* losses, void* workspace, size_t workspace_bytes,
+                                void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GPTQ_MI355X_H */

@@ -1,0 +1,192 @@
+"""ctypes binding of libgptq_mi355x.so (the C ABI in include/gptq.h).
+
+Argument marshalling only: every step of the path runs in the library's HIP
+kernels. PyTorch provides device memory and streams. If the library is not
+built, importing this module raises ImportError: there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libgptq_mi355x.so")
+
+GPTQ_OK = 0
+GPTQ_ERR_INVALID_ARG = 1
+GPTQ_ERR_WORKSPACE = 2
+GPTQ_ERR_NOT_PD = 3
+GPTQ_ERR_HIP = 4
+GPTQ_ERR_UNSUPPORTED = 5
+
+GPTQ_DTYPE_F16 = 0
+GPTQ_DTYPE_F32 = 1
+
+OP_ACCUMULATE = 0
+OP_PREPARE = 1
+OP_QUANTIZE = 2
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is not built; run __graft_entry__.build() (hipcc, gfx950) first")
+
+# PyTorch-ROCm ships its own libamdhip64.so.7. Importing torch first makes the
+# dynamic loader bind the library's libamdhip64.so.7 dependency to that
+# already-loaded runtime, so torch's streams and allocations and the
+# library's launches live in one HIP runtime.
+import torch  # noqa: E402,F401
+
+lib = ctypes.CDLL(LIB_PATH)
+
+_p = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_int = ctypes.c_int
+_sz = ctypes.c_size_t
+
+lib.gptq_version.restype = _int
+lib.gptq_version.argtypes = []
+lib.gptq_status_string.restype = ctypes.c_char_p
+lib.gptq_status_string.argtypes = [_int]
+lib.gptq_workspace_bytes.restype = _sz
+lib.gptq_workspace_bytes.argtypes = [_int, _i64, _i64, _i64]
+lib.gptq_hessian_accumulate.restype = _int
+lib.gptq_hessian_accumulate.argtypes = [_p, _i64, _p, _i64, _i64, ctypes.c_float, _p, _sz, _p]
+lib.gptq_prepare_hinv.restype = _int
+lib.gptq_prepare_hinv.argtypes = [_p, _i64, ctypes.c_double, _p, _p, _sz,
+                                  ctypes.POINTER(ctypes.c_int64), _p]
+lib.gptq_quantize_layer.restype = _int
+lib.gptq_quantize_layer.argtypes = [_p, _int, _i64, _i64, _i64, _p, _int, _int, _int,
+                                    _p, _p, _p, _p, _p, _sz, _p]
+
+
+class GPTQError(RuntimeError):
+    def __init__(self, status: int, where: str, info: int = 0):
+        name = lib.gptq_status_string(status).decode()
+        msg = f"{where}: {name}"
+        if info:
+            msg += f" (info={info})"
+        super().__init__(msg)
+        self.status = status
+        self.info = info
+
+
+def status_string(status: int) -> str:
+    return lib.gptq_status_string(status).decode()
+
+
+def version() -> int:
+    return lib.gptq_version()
+
+
+def workspace_bytes(op: int, rows: int, cols: int, n: int) -> int:
+    return int(lib.gptq_workspace_bytes(op, rows, cols, n))
+
+
+# ---------------------------------------------------------------- torch layer
+def _torch():
+    import torch
+    return torch
+
+
+def _stream_ptr(stream, device) -> Optional[int]:
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return stream.cuda_stream
+
+
+def _workspace(nbytes: int, device, workspace=None):
+    torch = _torch()
+    if nbytes == 0:
+        return None, 0
+    if workspace is not None:
+        if workspace.device != device or workspace.numel() * workspace.element_size() < nbytes:
+            raise ValueError("workspace too small or on another device")
+        if workspace.data_ptr() % 256:
+            raise ValueError("workspace must be 256-byte aligned")
+        return workspace, workspace.numel() * workspace.element_size()
+    ws = torch.empty(nbytes + 256, dtype=torch.uint8, device=device)
+    off = (-ws.data_ptr()) % 256
+    ws = ws[off:off + nbytes]
+    return ws, nbytes
+
+
+def _check(status: int, where: str, info: int = 0):
+    if status != GPTQ_OK:
+        raise GPTQError(status, where, info)
+
+
+def hessian_accumulate(H, X, alpha: float = 2.0, workspace=None, stream=None):
+    """H += alpha * X^T X on the GPU. H: d x d fp32 (contiguous), X: n x d fp16
+    with unit column stride. Returns H."""
+    torch = _torch()
+    if H.dtype != torch.float32 or not H.is_cuda or not H.is_contiguous():
+        raise ValueError("H must be a contiguous fp32 CUDA tensor")
+    if X.dtype != torch.float16 or X.device != H.device or X.dim() != 2 or X.stride(1) != 1:
+        raise ValueError("X must be a 2-D fp16 CUDA tensor with unit column stride")
+    d = H.shape[0]
+    if H.shape != (d, d) or X.shape[1] != d:
+        raise ValueError("shape mismatch")
+    n = X.shape[0]
+    ldx = X.stride(0) if n > 1 else d
+    ws, wsb = _workspace(workspace_bytes(OP_ACCUMULATE, 0, d, n), H.device, workspace)
+    st = lib.gptq_hessian_accumulate(H.data_ptr(), d, X.data_ptr(), n, ldx, alpha,
+                                     ws.data_ptr() if ws is not None else None, wsb,
+                                     _stream_ptr(stream, H.device))
+    _check(st, "gptq_hessian_accumulate")
+    return H
+
+
+def prepare_hinv(H, percdamp: float = 0.01, out=None, workspace=None, stream=None):
+    """Hinv (d x d fp32, upper triangular) from H. Raises GPTQError with
+    status GPTQ_ERR_NOT_PD and the failing pivot in .info."""
+    torch = _torch()
+    if H.dtype != torch.float32 or not H.is_cuda or not H.is_contiguous() or H.dim() != 2:
+        raise ValueError("H must be a contiguous fp32 CUDA tensor")
+    d = H.shape[0]
+    if out is None:
+        out = torch.empty((d, d), dtype=torch.float32, device=H.device)
+    ws, wsb = _workspace(workspace_bytes(OP_PREPARE, 0, d, 0), H.device, workspace)
+    info = ctypes.c_int64(0)
+    st = lib.gptq_prepare_hinv(H.data_ptr(), d, float(percdamp), out.data_ptr(),
+                               ws.data_ptr(), wsb, ctypes.byref(info),
+                               _stream_ptr(stream, H.device))
+    _check(st, "gptq_prepare_hinv", info.value)
+    return out
+
+
+def quantize_layer(W, Hinv, bits: int = 4, groupsize: int = 128, blocksize: int = 128,
+                   out=None, workspace=None, stream=None):
+    """GPTQ sweep. W: rows x cols fp16/fp32 (unit column stride); Hinv from
+    prepare_hinv. Returns (codes uint8, scales fp32, zeros fp32, losses fp32)."""
+    torch = _torch()
+    if W.dim() != 2 or W.stride(1) != 1 or not W.is_cuda:
+        raise ValueError("W must be a 2-D CUDA tensor with unit column stride")
+    if W.dtype == torch.float16:
+        wdt = GPTQ_DTYPE_F16
+    elif W.dtype == torch.float32:
+        wdt = GPTQ_DTYPE_F32
+    else:
+        raise ValueError("W must be fp16 or fp32")
+    rows, cols = W.shape
+    if Hinv.shape != (cols, cols) or Hinv.dtype != torch.float32 or not Hinv.is_contiguous():
+        raise ValueError("Hinv must be a contiguous cols x cols fp32 tensor")
+    g = groupsize
+    ng = (cols + g - 1) // g
+    dev = W.device
+    if out is None:
+        codes = torch.empty((rows, cols), dtype=torch.uint8, device=dev)
+        scales = torch.empty((rows, ng), dtype=torch.float32, device=dev)
+        zeros = torch.empty((rows, ng), dtype=torch.float32, device=dev)
+        losses = torch.empty((cols,), dtype=torch.float32, device=dev)
+    else:
+        codes, scales, zeros, losses = out
+    ws, wsb = _workspace(workspace_bytes(OP_QUANTIZE, rows, cols, 0), dev, workspace)
+    ldw = W.stride(0) if rows > 1 else cols
+    st = lib.gptq_quantize_layer(W.data_ptr(), wdt, rows, cols, ldw, Hinv.data_ptr(), bits,
+                                 groupsize, blocksize, codes.data_ptr(), scales.data_ptr(),
+                                 zeros.data_ptr(), losses.data_ptr(), ws.data_ptr(), wsb,
+                                 _stream_ptr(stream, dev))
+    _check(st, "gptq_quantize_layer")
+    return codes, scales, zeros, losses

@@ -1,0 +1,68 @@
+// Internal helpers shared by the gfx950 kernels and the host entry points.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/gptq.h"
+
+namespace gptq {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+__host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+__host__ __device__ inline int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
+
+// Index of a lower-triangle tile (bi >= bj) in row-major order of the lower
+// triangle: t = bi*(bi+1)/2 + bj.
+__host__ __device__ inline void lower_tile(int64_t t, int& bi, int& bj) {
+  int64_t i = (int64_t)((__builtin_sqrt(8.0 * (double)t + 1.0) - 1.0) * 0.5);
+  while (i * (i + 1) / 2 > t) --i;
+  while ((i + 1) * (i + 2) / 2 <= t) ++i;
+  bi = (int)i;
+  bj = (int)(t - i * (i + 1) / 2);
+}
+
+// ---------------------------------------------------------------- launches
+// Each launcher returns hipSuccess or the launch error.
+hipError_t launch_syrk_partial(const _Float16* X, int64_t ldx, int d, int64_t n, int splits,
+                               int64_t kper, float* partials, hipStream_t s);
+hipError_t launch_syrk_reduce(const float* partials, int d, int splits, float alpha, float* H,
+                              hipStream_t s);
+
+int syrk_splits(int64_t d, int64_t n);
+int64_t syrk_kper(int64_t n, int splits);
+constexpr int kSyrkTile = 128;
+
+// fp64 Cholesky route
+hipError_t launch_damp_to_f64(const float* H, int d, double percdamp, double* A, int* flag,
+                              hipStream_t s);
+hipError_t launch_potrf_panel(double* A, int lda, int d, int k, int* flag, int info_offset,
+                              hipStream_t s);
+hipError_t launch_potrf_update(double* A, int lda, int d, int k, hipStream_t s);
+hipError_t launch_trtri_diag(const double* L, int ldl, double* X, int ldx, int d, hipStream_t s);
+hipError_t launch_trtri_level(const double* L, int ldl, double* X, int ldx, int d, int half,
+                              hipStream_t s);
+hipError_t launch_lauum(const double* X, int ldx, double* S, int lds, int d, hipStream_t s);
+hipError_t launch_store_upper_f32(const double* L2, int ld2, float* Hinv, int d, hipStream_t s);
+constexpr int kPanel = 64;
+
+// sweep
+hipError_t launch_convert_w(const void* W, int w_dtype, int64_t rows, int64_t cols, int64_t ldw,
+                            float* Wk, int64_t ldk, hipStream_t s);
+hipError_t launch_sweep_block(float* Wk, int64_t ldk, int64_t rows, int64_t cols, int i1,
+                              const float* Hinv, int bits, int groupsize, uint8_t* codes,
+                              float* scales, float* zeros, float* Err, float* loss_part,
+                              hipStream_t s);
+hipError_t launch_lazy_update(float* Wk, int64_t ldk, int64_t rows, int64_t cols, int i1, int i2,
+                              const float* Err, const float* Hinv, hipStream_t s);
+hipError_t launch_loss_reduce(const float* loss_part, int64_t nparts, int64_t cols,
+                              float* losses, hipStream_t s);
+constexpr int kSweepRows = 16;  // rows per sweep workgroup
+constexpr int kBlock = 128;     // columns per block
+
+}  // namespace gptq

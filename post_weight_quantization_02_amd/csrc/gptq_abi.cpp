@@ -1,0 +1,209 @@
+// Host side of the C ABI declared in include/gptq.h: argument validation,
+// workspace carving and the launch order of the gfx950 kernels.
+#include <stddef.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "common.h"
+
+using namespace gptq;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+inline bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Upper bound on dimensions: indices are int inside the kernels.
+constexpr int64_t kMaxDim = 1 << 20;
+constexpr int64_t kMaxElems = (int64_t)1 << 40;
+
+size_t acc_bytes(int64_t d, int64_t n) {
+  if (d < 1 || d > kMaxDim || n < 0) return 0;
+  if (n == 0) return 0;
+  const int64_t nb = ceil_div(d, kSyrkTile);
+  const int64_t tiles = nb * (nb + 1) / 2;
+  const int splits = syrk_splits(d, n);
+  return align_up((size_t)splits * tiles * kSyrkTile * kSyrkTile * sizeof(float));
+}
+
+size_t prep_bytes(int64_t d) {
+  if (d < 1 || d > kMaxDim) return 0;
+  return 2 * align_up((size_t)d * d * sizeof(double)) + kAlign;
+}
+
+struct QuantLayout {
+  int64_t ldk;        // row stride of the fp32 working copy and of Err
+  size_t wk_off, err_off, loss_off, total;
+  int64_t nparts;     // loss partial rows
+};
+
+QuantLayout quant_layout(int64_t rows, int64_t cols) {
+  QuantLayout L{};
+  L.ldk = round_up(cols, kBlock);
+  L.nparts = ceil_div(rows, kSweepRows);
+  L.wk_off = 0;
+  L.err_off = L.wk_off + align_up((size_t)rows * L.ldk * sizeof(float));
+  L.loss_off = L.err_off + align_up((size_t)rows * L.ldk * sizeof(float));
+  L.total = L.loss_off + align_up((size_t)L.nparts * L.ldk * sizeof(float));
+  return L;
+}
+
+size_t quant_bytes(int64_t rows, int64_t cols) {
+  if (rows < 1 || cols < 1 || rows > kMaxDim || cols > kMaxDim) return 0;
+  return quant_layout(rows, cols).total;
+}
+
+bool group_ok(int g) {
+  if (g == 16 || g == 32 || g == 64) return true;
+  return g >= kBlock && g % kBlock == 0;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gptq_version(void) { return 100; }
+
+const char* gptq_status_string(int status) {
+  switch (status) {
+    case GPTQ_OK: return "GPTQ_OK";
+    case GPTQ_ERR_INVALID_ARG: return "GPTQ_ERR_INVALID_ARG";
+    case GPTQ_ERR_WORKSPACE: return "GPTQ_ERR_WORKSPACE";
+    case GPTQ_ERR_NOT_PD: return "GPTQ_ERR_NOT_PD";
+    case GPTQ_ERR_HIP: return "GPTQ_ERR_HIP";
+    case GPTQ_ERR_UNSUPPORTED: return "GPTQ_ERR_UNSUPPORTED";
+    default: return "GPTQ_ERR_UNKNOWN";
+  }
+}
+
+size_t gptq_workspace_bytes(int op, int64_t rows, int64_t cols, int64_t n) {
+  switch (op) {
+    case GPTQ_OP_ACCUMULATE: return acc_bytes(cols, n);
+    case GPTQ_OP_PREPARE: return prep_bytes(cols);
+    case GPTQ_OP_QUANTIZE: return quant_bytes(rows, cols);
+    default: return 0;
+  }
+}
+
+gptq_status gptq_hessian_accumulate(float* H, int64_t d, const void* X, int64_t n, int64_t ldx,
+                                    float alpha, void* workspace, size_t workspace_bytes,
+                                    void* stream) {
+  if (d < 1 || d > kMaxDim || n < 0 || ldx < d) return GPTQ_ERR_INVALID_ARG;
+  if (H == nullptr || (n > 0 && X == nullptr)) return GPTQ_ERR_INVALID_ARG;
+  if (n > 0 && (n > kMaxElems / ldx)) return GPTQ_ERR_INVALID_ARG;
+  if (!aligned(H, 4) || !aligned(X, 2)) return GPTQ_ERR_INVALID_ARG;
+  if (n == 0) return GPTQ_OK;
+  const size_t need = acc_bytes(d, n);
+  if (workspace_bytes < need || (need > 0 && workspace == nullptr)) return GPTQ_ERR_WORKSPACE;
+  if (!aligned(workspace, kAlign)) return GPTQ_ERR_INVALID_ARG;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int splits = syrk_splits(d, n);
+  const int64_t kper = syrk_kper(n, splits);
+  float* P = reinterpret_cast<float*>(workspace);
+  if (launch_syrk_partial(reinterpret_cast<const _Float16*>(X), ldx, (int)d, n, splits, kper, P,
+                          s) != hipSuccess)
+    return GPTQ_ERR_HIP;
+  if (launch_syrk_reduce(P, (int)d, splits, alpha, H, s) != hipSuccess) return GPTQ_ERR_HIP;
+  return GPTQ_OK;
+}
+
+gptq_status gptq_prepare_hinv(const float* H, int64_t d, double percdamp, float* Hinv,
+                              void* workspace, size_t workspace_bytes, int64_t* info,
+                              void* stream) {
+  if (info) *info = 0;
+  if (d < 1 || d > 65536 || H == nullptr || Hinv == nullptr) return GPTQ_ERR_INVALID_ARG;
+  if (!(percdamp >= 0.0) || percdamp > 1e6) return GPTQ_ERR_INVALID_ARG;
+  if (!aligned(H, 4) || !aligned(Hinv, 4)) return GPTQ_ERR_INVALID_ARG;
+  const size_t need = prep_bytes(d);
+  if (workspace == nullptr || workspace_bytes < need) return GPTQ_ERR_WORKSPACE;
+  if (!aligned(workspace, kAlign)) return GPTQ_ERR_INVALID_ARG;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int di = (int)d;
+  const size_t mat = align_up((size_t)d * d * sizeof(double));
+  double* A = reinterpret_cast<double*>(workspace);
+  double* Xi = reinterpret_cast<double*>(reinterpret_cast<char*>(workspace) + mat);
+  int* flag = reinterpret_cast<int*>(reinterpret_cast<char*>(workspace) + 2 * mat);
+
+#define GPTQ_TRY(call) \
+  do {                 \
+    if ((call) != hipSuccess) return GPTQ_ERR_HIP; \
+  } while (0)
+
+  // A = H + lambda I (fp64, lower triangle); resets the pivot flag.
+  GPTQ_TRY(launch_damp_to_f64(H, di, percdamp, A, flag, s));
+  // L = chol(A), in place
+  for (int k = 0; k < di; k += kPanel) {
+    GPTQ_TRY(launch_potrf_panel(A, di, di, k, flag, 0, s));
+    if (k + kPanel < di) GPTQ_TRY(launch_potrf_update(A, di, di, k, s));
+  }
+  // Xi = L^{-1}
+  GPTQ_TRY(launch_trtri_diag(A, di, Xi, di, di, s));
+  for (int half = kPanel; half < di; half *= 2) GPTQ_TRY(launch_trtri_level(A, di, Xi, di, di, half, s));
+  // A = Xi^T Xi = H_d^{-1} (lower triangle)
+  GPTQ_TRY(launch_lauum(Xi, di, A, di, di, s));
+  // L2 = chol(H_d^{-1}), in place
+  for (int k = 0; k < di; k += kPanel) {
+    GPTQ_TRY(launch_potrf_panel(A, di, di, k, flag, di, s));
+    if (k + kPanel < di) GPTQ_TRY(launch_potrf_update(A, di, di, k, s));
+  }
+  // Hinv = L2^T (upper), fp32
+  GPTQ_TRY(launch_store_upper_f32(A, di, Hinv, di, s));
+  int hflag = 0;
+  GPTQ_TRY(hipMemcpyAsync(&hflag, flag, sizeof(int), hipMemcpyDeviceToHost, s));
+  GPTQ_TRY(hipStreamSynchronize(s));
+#undef GPTQ_TRY
+  if (hflag != 0x7fffffff) {
+    if (info) *info = hflag;
+    return GPTQ_ERR_NOT_PD;
+  }
+  return GPTQ_OK;
+}
+
+gptq_status gptq_quantize_layer(const void* W, int w_dtype, int64_t rows, int64_t cols,
+                                int64_t ldw, const float* Hinv, int bits, int groupsize,
+                                int blocksize, uint8_t* codes, float* scales, float* zeros,
+                                float* losses, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+  if (rows < 1 || cols < 1 || rows > kMaxDim || cols > kMaxDim || ldw < cols)
+    return GPTQ_ERR_INVALID_ARG;
+  if (W == nullptr || Hinv == nullptr || codes == nullptr || scales == nullptr ||
+      zeros == nullptr || losses == nullptr)
+    return GPTQ_ERR_INVALID_ARG;
+  if (w_dtype != GPTQ_DTYPE_F16 && w_dtype != GPTQ_DTYPE_F32) return GPTQ_ERR_INVALID_ARG;
+  if (bits < 2 || bits > 8) return GPTQ_ERR_INVALID_ARG;
+  if (groupsize < 1 || blocksize < 1) return GPTQ_ERR_INVALID_ARG;
+  // group statistics taken at a group start must see every pending update:
+  // either groups lie inside blocks or blocks inside groups
+  if (groupsize % blocksize != 0 && blocksize % groupsize != 0) return GPTQ_ERR_INVALID_ARG;
+  if (rows > kMaxElems / ldw) return GPTQ_ERR_INVALID_ARG;
+  if (!aligned(W, w_dtype == GPTQ_DTYPE_F16 ? 2 : 4) || !aligned(Hinv, 4) ||
+      !aligned(scales, 4) || !aligned(zeros, 4) || !aligned(losses, 4))
+    return GPTQ_ERR_INVALID_ARG;
+  if (blocksize != kBlock || !group_ok(groupsize)) return GPTQ_ERR_UNSUPPORTED;
+  const QuantLayout L = quant_layout(rows, cols);
+  if (workspace == nullptr || workspace_bytes < L.total) return GPTQ_ERR_WORKSPACE;
+  if (!aligned(workspace, kAlign)) return GPTQ_ERR_INVALID_ARG;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  char* ws = reinterpret_cast<char*>(workspace);
+  float* Wk = reinterpret_cast<float*>(ws + L.wk_off);
+  float* Err = reinterpret_cast<float*>(ws + L.err_off);
+  float* lpart = reinterpret_cast<float*>(ws + L.loss_off);
+
+  if (launch_convert_w(W, w_dtype, rows, cols, ldw, Wk, L.ldk, s) != hipSuccess) return GPTQ_ERR_HIP;
+  for (int64_t i1 = 0; i1 < cols; i1 += kBlock) {
+    const int64_t i2 = (i1 + kBlock < cols) ? i1 + kBlock : cols;
+    if (launch_sweep_block(Wk, L.ldk, rows, cols, (int)i1, Hinv, bits, groupsize, codes, scales,
+                           zeros, Err, lpart, s) != hipSuccess)
+      return GPTQ_ERR_HIP;
+    if (i2 < cols && launch_lazy_update(Wk, L.ldk, rows, cols, (int)i1, (int)i2, Err, Hinv, s) !=
+                         hipSuccess)
+      return GPTQ_ERR_HIP;
+  }
+  if (launch_loss_reduce(lpart, L.nparts, cols, losses, s) != hipSuccess) return GPTQ_ERR_HIP;
+  return GPTQ_OK;
+}
+
+}  // extern "C"
