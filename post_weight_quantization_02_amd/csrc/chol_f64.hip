@@ -33,6 +33,26 @@ namespace gptq {
 namespace {
 
 constexpr int NB = kPanel;  // 64
+constexpr int PP = NB + 2;  // LDS pitch (doubles) of the 64x64 panel tiles: conflict-free
+                            // MFMA operand reads (rows m = lane%16, columns k = lane/16)
+
+// 1/p to full fp64 accuracy: hardware reciprocal estimate + two Newton steps.
+__device__ inline double recip_f64(double p) {
+  double r = __builtin_amdgcn_rcp(p);
+  double e = __builtin_fma(-p, r, 1.0);
+  r = __builtin_fma(r, e, r);
+  e = __builtin_fma(-p, r, 1.0);
+  return __builtin_fma(r, e, r);
+}
+
+// 1/sqrt(p) to fp64 accuracy: hardware estimate + two Newton steps.
+__device__ inline double rsqrt_f64(double p) {
+  double r = __builtin_amdgcn_rsq(p);
+  double h = 0.5 * p;
+  r = r * __builtin_fma(-h * r, r, 1.5);
+  r = r * __builtin_fma(-h * r, r, 1.5);
+  return r;
+}
 constexpr int GT = 64;      // GEMM tile edge
 constexpr int GK = 16;      // GEMM K chunk
 
@@ -68,74 +88,234 @@ __global__ __launch_bounds__(256) void damp_copy_kernel(const float* __restrict_
 }
 
 // -------------------------------------------------------------- panel
-// Factor the 64x64 diagonal block of the panel at column k in LDS and write
-// L_kk over it (one workgroup).  Right-looking and unscaled: step j subtracts
-// D[i][j] D[l][j] / D[j][j] from the trailing lower triangle; the column is
-// scaled by 1/sqrt(D[j][j]) at the end.  One barrier per step.
+// One workgroup factors the 64x64 diagonal block of the panel at column k and
+// inverts the factor: A_kk = L L^T, X = L^-1.  L overwrites the lower triangle
+// of A_kk, X (with zeros above its diagonal) goes to Xd (leading dim ldxd).
+//
+// Thread (tx, ty) = (t % 16, t / 16) keeps the 16 elements of rows
+// ty + 16a, columns tx + 16b (a, b < 4) of two matrices in registers: the
+// Schur complement `a` (right-looking, unscaled: a[i][l] -= a[i][j] a[l][j] /
+// a[j][j]) and Y, the forward substitution L Y = I run row by row.  Step j of
+// both recurrences needs only column j of L and row j of Y, which are final
+// when step j starts, so one loop of 64 steps does both: the owners publish
+// that column and that row through LDS, one barrier, then every thread
+// applies the two rank-1 updates to its registers.
 __global__ __launch_bounds__(256) void potrf_diag_kernel(double* __restrict__ A, int lda, int d,
-                                                         int k, int* flag, int info_offset) {
-  __shared__ double D[NB][NB + 1];
-  __shared__ double rinv[NB];
+                                                         int k, int* flag, int info_offset,
+                                                         double* __restrict__ Xd, int ldxd) {
+  __shared__ double colb[2][NB];
+  __shared__ double rowb[2][NB];
+  __shared__ double rsq[NB];
   const int tid = threadIdx.x;
   const int tx = tid & 15, ty = tid >> 4;
   const int kb = min(NB, d - k);
-  for (int e = tid; e < NB * NB; e += 256) {
-    const int i = e / NB, j = e % NB;
-    double v = (i == j) ? 1.0 : 0.0;
-    if (i < kb && j < kb && j <= i) v = A[(int64_t)(k + i) * lda + k + j];
-    D[i][j] = v;
-  }
-  __syncthreads();
-  for (int j = 0; j < kb; ++j) {
-    const double djj = D[j][j];
-    if (tid == 0 && !(djj > 0.0)) atomicMin(flag, info_offset + k + j + 1);
-    const double inv = 1.0 / djj;
-    for (int i = j + 1 + ty; i < kb; i += 16) {
-      const double dij = D[i][j] * inv;
-      for (int l = j + 1 + tx; l <= i; l += 16) D[i][l] -= dij * D[l][j];
+  double a[4][4], y[4][4];
+#pragma unroll
+  for (int ai = 0; ai < 4; ++ai)
+#pragma unroll
+    for (int bj = 0; bj < 4; ++bj) {
+      const int i = ty + 16 * ai, l = tx + 16 * bj;
+      const int r = i >= l ? i : l, c = i >= l ? l : i;
+      double v = (i == l) ? 1.0 : 0.0;
+      if (r < kb) v = A[(int64_t)(k + r) * lda + k + c];
+      a[ai][bj] = v;
+      y[ai][bj] = (i == l) ? 1.0 : 0.0;
     }
-    __syncthreads();
+
+#pragma unroll
+  for (int bb = 0; bb < 4; ++bb) {
+#pragma unroll 1
+    for (int jj = 0; jj < 16; ++jj) {
+      const int j = 16 * bb + jj;
+      double* cb = colb[j & 1];
+      double* rb = rowb[j & 1];
+      if (tx == jj) {
+#pragma unroll
+        for (int ai = 0; ai < 4; ++ai) cb[ty + 16 * ai] = a[ai][bb];
+      }
+      if (ty == jj) {
+#pragma unroll
+        for (int bj = 0; bj < 4; ++bj) rb[tx + 16 * bj] = y[bb][bj];
+      }
+      __syncthreads();
+      const double p = cb[j];
+      const double inv = recip_f64(p);
+      const double rs = rsqrt_f64(p);  // 1 / L[j][j]
+      if (tid == 0) rsq[j] = rs;
+      double ci[4], cl[4], li[4], xr[4];
+#pragma unroll
+      for (int ai = 0; ai < 4; ++ai) {
+        const int i = ty + 16 * ai;
+        const double c = cb[i];
+        ci[ai] = (i > j) ? c * inv : 0.0;
+        li[ai] = (i > j) ? c * rs : 0.0;  // L[i][j]
+      }
+#pragma unroll
+      for (int bj = 0; bj < 4; ++bj) {
+        const int l = tx + 16 * bj;
+        cl[bj] = (l > j) ? cb[l] : 0.0;
+        xr[bj] = rb[l] * rs;              // X[j][l]
+      }
+#pragma unroll
+      for (int ai = 0; ai < 4; ++ai)
+#pragma unroll
+        for (int bj = 0; bj < 4; ++bj) {
+          a[ai][bj] -= ci[ai] * cl[bj];
+          y[ai][bj] -= li[ai] * xr[bj];
+        }
+      if (ty == jj) {
+#pragma unroll
+        for (int bj = 0; bj < 4; ++bj) y[bb][bj] = xr[bj];
+      }
+    }
   }
-  if (tid < NB) rinv[tid] = (tid < kb) ? 1.0 / sqrt(D[tid][tid]) : 1.0;
+  // pivots are the final diagonal entries of the Schur complement
+#pragma unroll
+  for (int ai = 0; ai < 4; ++ai)
+#pragma unroll
+    for (int bj = 0; bj < 4; ++bj)
+      if (ty + 16 * ai == tx + 16 * bj) {
+        const int j = ty + 16 * ai;
+        if (j < kb && !(a[ai][bj] > 0.0)) atomicMin(flag, info_offset + k + j + 1);
+      }
   __syncthreads();
-  for (int e = tid; e < NB * NB; e += 256) {
-    const int i = e / NB, j = e % NB;
-    if (i < kb && j <= i) A[(int64_t)(k + i) * lda + k + j] = D[i][j] * rinv[j];
+#pragma unroll
+  for (int ai = 0; ai < 4; ++ai)
+#pragma unroll
+    for (int bj = 0; bj < 4; ++bj) {
+      const int i = ty + 16 * ai, l = tx + 16 * bj;
+      if (i < kb && l < kb) {
+        if (l <= i) A[(int64_t)(k + i) * lda + k + l] = a[ai][bj] * rsq[l];
+        Xd[(int64_t)i * ldxd + l] = (l <= i) ? y[ai][bj] : 0.0;
+      }
+    }
+}
+
+// 64x64x64 fp64 MFMA product on LDS tiles: acc += P (64 x K) * Q^T, with
+// P[m][kk] and Q[n][kk] stored row-major at pitch PP.  Wave w owns the
+// 32x32 quadrant (w/2, w%2) as 2x2 tiles of 16x16.
+__device__ inline void mma64_f64(const double (*P)[PP], const double (*Q)[PP], int K,
+                                 f64x4 (&acc)[2][2], int lane, int wm, int wn) {
+  for (int ks = 0; ks < K; ks += 4) {
+    const int kr = ks + (lane >> 4);
+    double af[2], bf[2];
+#pragma unroll
+    for (int a = 0; a < 2; ++a) af[a] = P[32 * wm + 16 * a + (lane & 15)][kr];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) bf[b] = Q[32 * wn + 16 * b + (lane & 15)][kr];
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+        acc[a][b] = __builtin_amdgcn_mfma_f64_16x16x4f64(af[a], bf[b], acc[a][b], 0, 0, 0);
   }
 }
 
-// Solve X L_kk^T = A[k+64(r+1).., k..k+63] for the row blocks below the
-// diagonal block (one workgroup per 64-row block), right-looking over
-// columns: B[:, m] -= (B[:, j] / L[j][j]) L[m][j].
+// Row of the 16x16 fp64 MFMA result held in element i of lane `lane`
+// (the fp64 variant interleaves rows: lane/16, lane/16 + 4, ...).
+__device__ inline int mfma64_row(int lane, int i) { return (lane >> 4) + 4 * i; }
+
+// L_ik = A_ik X_kk^T for the 64-row blocks below the diagonal block
+// (one workgroup per block; X_kk = L_kk^-1 from the diagonal kernel).
 __global__ __launch_bounds__(256) void potrf_trsm_kernel(double* __restrict__ A, int lda, int d,
-                                                         int k) {
-  __shared__ double Lk[NB][NB + 1];
-  __shared__ double Bk[NB][NB + 1];
+                                                         int k, const double* __restrict__ Xd,
+                                                         int ldxd) {
+  __shared__ double Bs[NB][PP];
+  __shared__ double Xs[NB][PP];
   const int tid = threadIdx.x;
-  const int tx = tid & 15, ty = tid >> 4;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
   const int kb = min(NB, d - k);
   const int row0 = k + NB * (blockIdx.x + 1);
   const int rb = min(NB, d - row0);
-  for (int e = tid; e < NB * NB; e += 256) {
-    const int i = e / NB, j = e % NB;
-    double v = (i == j) ? 1.0 : 0.0;
-    if (i < kb && j <= i) v = A[(int64_t)(k + i) * lda + k + j];
-    Lk[i][j] = v;
-    Bk[i][j] = (i < rb && j < kb) ? A[(int64_t)(row0 + i) * lda + k + j] : 0.0;
+  const int j = tid & 63, i0 = tid >> 6;
+  double bv[16], xv[16];
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    const int i = i0 + 4 * q;
+    bv[q] = (i < rb && j < kb) ? A[(int64_t)(row0 + i) * lda + k + j] : 0.0;
+    xv[q] = (i < kb && j < kb) ? Xd[(int64_t)i * ldxd + j] : 0.0;
+  }
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    Bs[i0 + 4 * q][j] = bv[q];
+    Xs[i0 + 4 * q][j] = xv[q];
   }
   __syncthreads();
-  for (int j = 0; j < kb; ++j) {
-    const double ljj = 1.0 / Lk[j][j];
-    for (int i = ty; i < rb; i += 16) {
-      const double xij = Bk[i][j] * ljj;
-      for (int m = j + 1 + tx; m < kb; m += 16) Bk[i][m] -= xij * Lk[m][j];
-    }
-    __syncthreads();
+  f64x4 acc[2][2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b) acc[a][b] = f64x4{0.0, 0.0, 0.0, 0.0};
+  mma64_f64(Bs, Xs, NB, acc, lane, wm, wn);
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 32 * wm + 16 * a + mfma64_row(lane, i);
+        const int c = 32 * wn + 16 * b + (lane & 15);
+        if (r < rb && c < kb) A[(int64_t)(row0 + r) * lda + k + c] = acc[a][b][i];
+      }
+}
+
+// Trailing update of the lower triangle: A_ij -= L_ik L_jk^T for all 64x64
+// tiles i >= j of A[t0:, t0:], t0 = k + 64; both panel blocks sit in LDS.
+__global__ __launch_bounds__(256) void potrf_update_kernel(double* __restrict__ A, int lda, int d,
+                                                           int k) {
+  __shared__ double Ps[NB][PP];
+  __shared__ double Qs[NB][PP];
+  int ti, tj;
+  lower_tile(blockIdx.x, ti, tj);
+  const int t0 = k + NB;
+  const int r0 = t0 + NB * ti, c0 = t0 + NB * tj;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const bool diag = (ti == tj);
+  const int j = tid & 63, i0 = tid >> 6;
+  double pv[16], qv[16];
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    const int i = i0 + 4 * q;
+    pv[q] = (r0 + i < d) ? A[(int64_t)(r0 + i) * lda + k + j] : 0.0;
+    qv[q] = (!diag && c0 + i < d) ? A[(int64_t)(c0 + i) * lda + k + j] : 0.0;
   }
-  for (int e = tid; e < NB * NB; e += 256) {
-    const int i = e / NB, j = e % NB;
-    if (i < rb && j < kb) A[(int64_t)(row0 + i) * lda + k + j] = Bk[i][j] / Lk[j][j];
+  // C tile (read early so its latency overlaps the MFMA work)
+  f64x4 cv[2][2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = r0 + 32 * wm + 16 * a + mfma64_row(lane, i);
+        const int c = c0 + 32 * wn + 16 * b + (lane & 15);
+        cv[a][b][i] = (r < d && c < d) ? A[(int64_t)r * lda + c] : 0.0;
+      }
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    Ps[i0 + 4 * q][j] = pv[q];
+    Qs[i0 + 4 * q][j] = qv[q];
   }
+  __syncthreads();
+  f64x4 acc[2][2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b) acc[a][b] = f64x4{0.0, 0.0, 0.0, 0.0};
+  mma64_f64(Ps, diag ? Ps : Qs, NB, acc, lane, wm, wn);
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = r0 + 32 * wm + 16 * a + mfma64_row(lane, i);
+        const int c = c0 + 32 * wn + 16 * b + (lane & 15);
+        if (r < d && c < d) A[(int64_t)r * lda + c] = cv[a][b][i] - acc[a][b][i];
+      }
 }
 
 // -------------------------------------------------------------- MFMA GEMM
@@ -155,10 +335,15 @@ struct GemmDesc {
 // AK: A element (m,k) at A[m*lda+k] (else A[k*lda+m]).
 // BN: B element (k,n) at B[k*ldb+n] (else B[n*ldb+k]).
 // CN: C element (m,n) at C[m*ldc+n] (else C[n*ldc+m]).
+// K is streamed in chunks of GK through double-buffered LDS tiles stored
+// k-major ([k][m], pitch GT + 16 so the four k rows an MFMA operand read
+// touches fall in alternating bank halves); the next chunk's global loads are
+// issued before the current chunk's MFMAs.
 template <bool AK, bool BN, bool CN>
 __global__ __launch_bounds__(256) void gemm64_f64_kernel(GemmDesc g) {
-  __shared__ double As[GK][GT + 1];
-  __shared__ double Bs[GK][GT + 1];
+  constexpr int PK = GT + 16;
+  __shared__ double As[2][GK][PK];
+  __shared__ double Bs[2][GK][PK];
   int tm, tn;
   const int ntn = (int)ceil_div(g.N, GT);
   if (g.tri) {
@@ -185,40 +370,55 @@ __global__ __launch_bounds__(256) void gemm64_f64_kernel(GemmDesc g) {
 #pragma unroll
     for (int b = 0; b < 2; ++b) acc[a][b] = f64x4{0.0, 0.0, 0.0, 0.0};
 
-  for (int kc = k0; kc < k1; kc += GK) {
+  double av[4], bv[4];
+  auto gload = [&](int kc) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int e = tid + 256 * q;
-      int kk, mm;
-      if (AK) { kk = e % GK; mm = e / GK; } else { mm = e % GT; kk = e / GT; }
+      const int kk = AK ? (e % GK) : (e / GT);
+      const int mm = AK ? (e / GK) : (e % GT);
       const int gm = m0 + mm, gk = kc + kk;
-      double v = 0.0;
-      if (gm < g.M && gk < k1) v = AK ? Ap[(int64_t)gm * g.lda + gk] : Ap[(int64_t)gk * g.lda + gm];
-      As[kk][mm] = v;
-      int nn;
-      if (BN) { nn = e % GT; kk = e / GT; } else { kk = e % GK; nn = e / GK; }
-      const int gn = n0 + nn;
-      const int gk2 = kc + kk;
-      double u = 0.0;
-      if (gn < g.N && gk2 < k1) u = BN ? Bp[(int64_t)gk2 * g.ldb + gn] : Bp[(int64_t)gn * g.ldb + gk2];
-      Bs[kk][nn] = u;
+      av[q] = (gm < g.M && gk < k1) ? (AK ? Ap[(int64_t)gm * g.lda + gk] : Ap[(int64_t)gk * g.lda + gm]) : 0.0;
+      const int kb = BN ? (e / GT) : (e % GK);
+      const int nn = BN ? (e % GT) : (e / GK);
+      const int gn = n0 + nn, gk2 = kc + kb;
+      bv[q] = (gn < g.N && gk2 < k1) ? (BN ? Bp[(int64_t)gk2 * g.ldb + gn] : Bp[(int64_t)gn * g.ldb + gk2]) : 0.0;
     }
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = tid + 256 * q;
+      As[buf][AK ? (e % GK) : (e / GT)][AK ? (e / GK) : (e % GT)] = av[q];
+      Bs[buf][BN ? (e / GT) : (e % GK)][BN ? (e % GT) : (e / GK)] = bv[q];
+    }
+  };
+  if (k0 < k1) {
+    gload(k0);
+    lstore(0);
     __syncthreads();
+  }
+  int buf = 0;
+  for (int kc = k0; kc < k1; kc += GK) {
+    const bool more = kc + GK < k1;
+    if (more) gload(kc + GK);
 #pragma unroll
     for (int ks = 0; ks < GK; ks += 4) {
       const int kr = ks + (lane >> 4);
       double af[2], bf[2];
 #pragma unroll
-      for (int a = 0; a < 2; ++a) af[a] = As[kr][32 * wm + 16 * a + (lane & 15)];
+      for (int a = 0; a < 2; ++a) af[a] = As[buf][kr][32 * wm + 16 * a + (lane & 15)];
 #pragma unroll
-      for (int b = 0; b < 2; ++b) bf[b] = Bs[kr][32 * wn + 16 * b + (lane & 15)];
+      for (int b = 0; b < 2; ++b) bf[b] = Bs[buf][kr][32 * wn + 16 * b + (lane & 15)];
 #pragma unroll
       for (int a = 0; a < 2; ++a)
 #pragma unroll
         for (int b = 0; b < 2; ++b)
           acc[a][b] = __builtin_amdgcn_mfma_f64_16x16x4f64(af[a], bf[b], acc[a][b], 0, 0, 0);
     }
+    if (more) lstore(buf ^ 1);
     __syncthreads();
+    buf ^= 1;
   }
 #pragma unroll
   for (int a = 0; a < 2; ++a)
@@ -226,9 +426,7 @@ __global__ __launch_bounds__(256) void gemm64_f64_kernel(GemmDesc g) {
     for (int b = 0; b < 2; ++b)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        // v_mfma_f64_16x16x4_f64 returns rows lane/16, lane/16 + 4, ... in
-        // its four doubles (row-interleaved, unlike the fp32 variant)
-        const int m = m0 + 32 * wm + 16 * a + (lane >> 4) + 4 * i;
+        const int m = m0 + 32 * wm + 16 * a + mfma64_row(lane, i);
         const int n = n0 + 32 * wn + 16 * b + (lane & 15);
         if (m < g.M && n < g.N) {
           double* c = CN ? Cp + (int64_t)m * g.ldc + n : Cp + (int64_t)n * g.ldc + m;
@@ -320,32 +518,27 @@ hipError_t launch_damp_to_f64(const float* H, int d, double percdamp, double* A,
 }
 
 hipError_t launch_potrf_panel(double* A, int lda, int d, int k, int* flag, int info_offset,
-                              hipStream_t s) {
-  hipLaunchKernelGGL(potrf_diag_kernel, dim3(1), dim3(256), 0, s, A, lda, d, k, flag, info_offset);
+                              double* Xi, int ldxi, hipStream_t s) {
+  double* Xd = Xi + (int64_t)k * ldxi + k;
+  hipLaunchKernelGGL(potrf_diag_kernel, dim3(1), dim3(256), 0, s, A, lda, d, k, flag, info_offset,
+                     Xd, ldxi);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int nbelow = (int)ceil_div(d - k, NB) - 1;
   if (nbelow > 0) {
-    hipLaunchKernelGGL(potrf_trsm_kernel, dim3(nbelow), dim3(256), 0, s, A, lda, d, k);
+    hipLaunchKernelGGL(potrf_trsm_kernel, dim3(nbelow), dim3(256), 0, s, A, lda, d, k,
+                       (const double*)Xd, ldxi);
     e = hipGetLastError();
   }
   return e;
 }
 
 hipError_t launch_potrf_update(double* A, int lda, int d, int k, hipStream_t s) {
-  const int t0 = k + NB;
-  GemmDesc g{};
-  g.A = A + (int64_t)t0 * lda + k;
-  g.B = A + (int64_t)t0 * lda + k;
-  g.C = A + (int64_t)t0 * lda + t0;
-  g.lda = g.ldb = g.ldc = lda;
-  g.M = g.N = d - t0;
-  g.K = NB;
-  g.alpha = -1.0;
-  g.beta = 1.0;
-  g.tri = 1;
-  g.kmode = 0;
-  return gemm64<true, false, true>(g, 1, s);
+  const int64_t nt = ceil_div(d - k - NB, NB);
+  if (nt <= 0) return hipSuccess;
+  hipLaunchKernelGGL(potrf_update_kernel, dim3((unsigned)(nt * (nt + 1) / 2)), dim3(256), 0, s, A,
+                     lda, d, k);
+  return hipGetLastError();
 }
 
 hipError_t launch_trtri_diag(const double* L, int ldl, double* X, int ldx, int d, hipStream_t s) {

@@ -36,13 +36,13 @@ hipError_t launch_syrk_reduce(const float* partials, int d, int splits, float al
 
 int syrk_splits(int64_t d, int64_t n);
 int64_t syrk_kper(int64_t n, int splits);
-constexpr int kSyrkTile = 128;
+constexpr int kSyrkTile = 256;
 
 // fp64 Cholesky route
 hipError_t launch_damp_to_f64(const float* H, int d, double percdamp, double* A, int* flag,
                               hipStream_t s);
 hipError_t launch_potrf_panel(double* A, int lda, int d, int k, int* flag, int info_offset,
-                              hipStream_t s);
+                              double* Xi, int ldxi, hipStream_t s);
 hipError_t launch_potrf_update(double* A, int lda, int d, int k, hipStream_t s);
 hipError_t launch_trtri_diag(const double* L, int ldl, double* X, int ldx, int d, hipStream_t s);
 hipError_t launch_trtri_level(const double* L, int ldl, double* X, int ldx, int d, int half,

@@ -6,79 +6,98 @@
 // weighting", collect_hessian listing).
 //
 // gfx950 design:
-//   * Output tiles of 128x128 over the lower triangle only; the upper
-//     triangle is written by mirroring in the reduction kernel.
-//   * The token (K) range is split so the grid holds several waves of
-//     workgroups per CU; every split writes its own fp32 partial tile and a
-//     second kernel sums the partials in a fixed order (bitwise reproducible,
-//     no float atomics).
-//   * X arrives token-major (channels contiguous) but MFMA wants each lane to
-//     hold a run of consecutive K (token) values.  Each thread loads a
-//     4-token x 8-channel block with 16-byte loads, transposes it in
-//     registers and stores four-token runs into a channel-major LDS tile.
-//   * v_mfma_f32_16x16x32_f16: each of the 4 waves owns a 64x64 quadrant
-//     (4x4 MFMA tiles); fp16 products are exact in fp32 and accumulate in
-//     fp32.
+//   * 256x256 output tiles over the lower triangle only (the upper triangle
+//     is written by mirroring in the reduction kernel).  Four waves, each
+//     owning a 128x128 quadrant as 8x8 tiles of v_mfma_f32_16x16x32_f16
+//     (256 fp32 accumulators per lane): 0.5 LDS fragment reads per MFMA keeps
+//     LDS traffic well under its bandwidth at full MFMA rate.
+//   * X chunks of 32 tokens are copied into LDS exactly as they sit in HBM
+//     (token-major, 16-byte loads, rows padded by 32 bytes).  MFMA wants each
+//     lane to hold a run of K (token) values for one channel; gfx950's
+//     transposing LDS read ds_read_b64_tr_b16 delivers exactly that from the
+//     token-major tile: in every 16-lane group, lane s addresses row s/4,
+//     columns 4*(s%4).., and lane i receives channel i at four consecutive
+//     rows.  Two such reads give the 8-token run of a 16x16x32 operand.
+//   * Double-buffered LDS; the next chunk's global loads are issued before
+//     the current chunk's MFMAs.
+//   * The token range is split so the grid fills every CU for several rounds;
+//     each split writes its own fp32 partial tile and a second kernel sums the
+//     partials in a fixed order (bitwise reproducible, no float atomics).
+//   * fp16 products are exact in fp32; accumulation is fp32.
 #include "common.h"
 
 namespace gptq {
 
 namespace {
 
-constexpr int T = kSyrkTile;   // 128
-constexpr int KC = 32;         // tokens per K chunk
-constexpr int PITCH = KC + 8;  // halves per LDS row (80 bytes: conflict-free 16B reads)
+constexpr int T = kSyrkTile;     // 256
+constexpr int KC = 32;           // tokens per K chunk
+constexpr int PITCH = T + 16;    // halves per LDS row (544 bytes = 136 dwords: rows 8 banks apart)
+constexpr int NLOAD = (KC * T * 2) / (16 * 256);  // 16-byte loads per thread per operand block
 
-struct Chunk {
-  uint32_t r[4][4];  // [token][channel pair]
-};
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
+// 8 consecutive tokens (rows kb..kb+7 of the LDS tile) of channel c0 + (lane % 16),
+// as the K run of a 16x16x32 MFMA operand.
+__device__ inline half8 tr_frag(const _Float16* tile, int kb, int c0, int lane) {
+  const int s = lane & 15;
+  const _Float16* p0 = tile + (kb + (s >> 2)) * PITCH + c0 + 4 * (s & 3);
+  const _Float16* p1 = p0 + 4 * PITCH;
+  // whole-vector bit casts (casting single elements of the result mis-lowers)
+  const f16x4 lo = __builtin_bit_cast(f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p0));
+  const f16x4 hi = __builtin_bit_cast(f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p1));
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Chunk layout: 32 rows (tokens) x 256 channels = 1024 16-byte pieces per
+// operand block; thread t takes pieces t, t+256, ... (row = piece / 32).
 template <bool VEC>
-__device__ inline void load_chunk(const _Float16* __restrict__ X, int64_t ldx, int d, int64_t t0,
-                                  int64_t tend, int c0, Chunk& ch) {
+__device__ inline void load_block(const _Float16* __restrict__ X, int64_t ldx, int d,
+                                  int64_t t0, int64_t tend, int c0, uint4 (&v)[NLOAD], int tid) {
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const int64_t tok = t0 + t;
-    if (VEC) {
-      if (tok < tend && c0 + 8 <= d) {
-        const uint4 v = *reinterpret_cast<const uint4*>(X + tok * ldx + c0);
-        ch.r[t][0] = v.x;
-        ch.r[t][1] = v.y;
-        ch.r[t][2] = v.z;
-        ch.r[t][3] = v.w;
-        continue;
+  for (int q = 0; q < NLOAD; ++q) {
+    const int piece = tid + 256 * q;
+    const int r = piece >> 5, cp = (piece & 31) * 8;
+    const int64_t tok = t0 + r;
+    const int c = c0 + cp;
+    uint4 u = make_uint4(0, 0, 0, 0);
+    if (tok < tend) {
+      if (VEC && c + 8 <= d) {
+        u = *reinterpret_cast<const uint4*>(X + tok * ldx + c);
+      } else {
+        const uint16_t* xs = reinterpret_cast<const uint16_t*>(X) + tok * ldx;
+        uint32_t w[4];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const uint32_t lo = (c + 2 * p < d) ? xs[c + 2 * p] : 0u;
+          const uint32_t hi = (c + 2 * p + 1 < d) ? xs[c + 2 * p + 1] : 0u;
+          w[p] = lo | (hi << 16);
+        }
+        u = make_uint4(w[0], w[1], w[2], w[3]);
       }
     }
-    const uint16_t* xs = reinterpret_cast<const uint16_t*>(X);
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      uint32_t lo = 0, hi = 0;
-      if (tok < tend && c0 + 2 * p < d) lo = xs[tok * ldx + c0 + 2 * p];
-      if (tok < tend && c0 + 2 * p + 1 < d) hi = xs[tok * ldx + c0 + 2 * p + 1];
-      ch.r[t][p] = lo | (hi << 16);
-    }
+    v[q] = u;
   }
 }
 
-// Write the 4x8 block channel-major: channel c gets tokens t..t+3 as 8 bytes.
-__device__ inline void store_chunk(_Float16* __restrict__ s, int cl, int tq, const Chunk& ch) {
+__device__ inline void store_block(_Float16* __restrict__ s, const uint4 (&v)[NLOAD], int tid) {
 #pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const uint32_t l0 = (ch.r[0][p] & 0xffffu) | (ch.r[1][p] << 16);
-    const uint32_t l1 = (ch.r[2][p] & 0xffffu) | (ch.r[3][p] << 16);
-    const uint32_t h0 = (ch.r[0][p] >> 16) | (ch.r[1][p] & 0xffff0000u);
-    const uint32_t h1 = (ch.r[2][p] >> 16) | (ch.r[3][p] & 0xffff0000u);
-    *reinterpret_cast<uint2*>(s + (cl + 2 * p) * PITCH + tq) = make_uint2(l0, l1);
-    *reinterpret_cast<uint2*>(s + (cl + 2 * p + 1) * PITCH + tq) = make_uint2(h0, h1);
+  for (int q = 0; q < NLOAD; ++q) {
+    const int piece = tid + 256 * q;
+    const int r = piece >> 5, cp = (piece & 31) * 8;
+    *reinterpret_cast<uint4*>(s + r * PITCH + cp) = v[q];
   }
 }
 
 template <bool VEC>
-__global__ __launch_bounds__(256) void syrk_partial_kernel(const _Float16* __restrict__ X,
-                                                           int64_t ldx, int d, int64_t n,
-                                                           int64_t kper, float* __restrict__ P) {
-  __shared__ __attribute__((aligned(16))) _Float16 sA[2][T * PITCH];
-  __shared__ __attribute__((aligned(16))) _Float16 sB[2][T * PITCH];
+__global__ __launch_bounds__(256, 1) void syrk_partial_kernel(const _Float16* __restrict__ X,
+                                                              int64_t ldx, int d, int64_t n,
+                                                              int64_t kper,
+                                                              float* __restrict__ P) {
+  __shared__ __attribute__((aligned(16))) _Float16 sA[2][KC * PITCH];
+  __shared__ __attribute__((aligned(16))) _Float16 sB[2][KC * PITCH];
 
   const int ntiles = gridDim.x;
   const int tile = blockIdx.x;
@@ -94,99 +113,96 @@ __global__ __launch_bounds__(256) void syrk_partial_kernel(const _Float16* __res
 
   const int64_t kbeg = (int64_t)split * kper;
   const int64_t kend = (kbeg + kper < n) ? kbeg + kper : n;
-
-  // loader role: 128 tasks per operand block (8 token quads x 16 channel octets)
-  const bool loadB = tid >= 128;
-  const int task = tid & 127;
-  const int tq = (task & 7) * 4;   // token offset within the chunk
-  const int cl = (task >> 3) * 8;  // channel offset within the tile
-  const int cbase = (loadB ? bj : bi) * T;
-  const bool active_loader = !(loadB && diag);
-
-  f32x4 acc[4][4];
-#pragma unroll
-  for (int a = 0; a < 4; ++a)
-#pragma unroll
-    for (int b = 0; b < 4; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  Chunk ch;
   const int64_t nk = (kend > kbeg) ? ceil_div(kend - kbeg, KC) : 0;
+
+  f32x4 acc[8][8];
+#pragma unroll
+  for (int a = 0; a < 8; ++a)
+#pragma unroll
+    for (int b = 0; b < 8; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  uint4 va[NLOAD], vb[NLOAD];
   if (nk > 0) {
-    if (active_loader) {
-      load_chunk<VEC>(X, ldx, d, kbeg + tq, kend, cbase + cl, ch);
-      store_chunk(loadB ? sB[0] : sA[0], cl, tq, ch);
-    }
+    load_block<VEC>(X, ldx, d, kbeg, kend, bi * T, va, tid);
+    if (!diag) load_block<VEC>(X, ldx, d, kbeg, kend, bj * T, vb, tid);
+    store_block(sA[0], va, tid);
+    if (!diag) store_block(sB[0], vb, tid);
     __syncthreads();
   }
   int buf = 0;
+  const int kg = 8 * (lane >> 4);  // token run of this lane's 16-lane group
   for (int64_t kc = 0; kc < nk; ++kc) {
-    const bool more = (kc + 1 < nk);
-    if (more && active_loader) load_chunk<VEC>(X, ldx, d, kbeg + (kc + 1) * KC + tq, kend, cbase + cl, ch);
-
+    const bool more = kc + 1 < nk;
+    if (more) {
+      const int64_t t0 = kbeg + (kc + 1) * KC;
+      load_block<VEC>(X, ldx, d, t0, kend, bi * T, va, tid);
+      if (!diag) load_block<VEC>(X, ldx, d, t0, kend, bj * T, vb, tid);
+    }
     const _Float16* a_s = sA[buf];
     const _Float16* b_s = diag ? sA[buf] : sB[buf];
-    const int koff = 8 * (lane >> 4);
-    half8 af[4], bf[4];
+    half8 bf[8];
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
-      af[m] = *reinterpret_cast<const half8*>(a_s + (64 * wm + 16 * m + (lane & 15)) * PITCH + koff);
+    for (int b = 0; b < 8; ++b) bf[b] = tr_frag(b_s, kg, 128 * wn + 16 * b, lane);
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
-      bf[m] = *reinterpret_cast<const half8*>(b_s + (64 * wn + 16 * m + (lane & 15)) * PITCH + koff);
+    for (int a = 0; a < 8; ++a) {
+      const half8 af = tr_frag(a_s, kg, 128 * wm + 16 * a, lane);
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
-#pragma unroll
-      for (int b = 0; b < 4; ++b)
-        acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[a], bf[b], acc[a][b], 0, 0, 0);
-
-    if (more && active_loader) store_chunk(loadB ? sB[buf ^ 1] : sA[buf ^ 1], cl, tq, ch);
+      for (int b = 0; b < 8; ++b)
+        acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bf[b], acc[a][b], 0, 0, 0);
+    }
+    if (more) {
+      store_block(sA[buf ^ 1], va, tid);
+      if (!diag) store_block(sB[buf ^ 1], vb, tid);
+    }
     __syncthreads();
     buf ^= 1;
   }
 
-  // partial tile, row-major 128x128
-  float* out = P + ((int64_t)split * ntiles + tile) * (T * T);
+  // partial tile, row-major 256x256
+  float* out = P + ((int64_t)split * ntiles + tile) * ((int64_t)T * T);
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+  for (int a = 0; a < 8; ++a)
 #pragma unroll
-    for (int b = 0; b < 4; ++b)
+    for (int b = 0; b < 8; ++b)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int r = 64 * wm + 16 * a + 4 * (lane >> 4) + i;
-        const int c = 64 * wn + 16 * b + (lane & 15);
+        const int r = 128 * wm + 16 * a + 4 * (lane >> 4) + i;
+        const int c = 128 * wn + 16 * b + (lane & 15);
         out[r * T + c] = acc[a][b][i];
       }
 }
 
-// Sum the split partials of one 64x64 quarter of a lower tile in split
+// Sum the split partials of one 64x64 sub-block of a lower tile in split
 // order, add alpha * sum into H, and mirror into the upper triangle.
 __global__ __launch_bounds__(256) void syrk_reduce_kernel(const float* __restrict__ P, int d,
                                                           int splits, int ntiles, float alpha,
                                                           float* __restrict__ H) {
+  constexpr int SB = T / 64;  // sub-blocks per tile edge
   __shared__ float st[64][65];
   const int tile = blockIdx.x;
-  const int q = blockIdx.y;  // quarter: (qr, qc)
-  const int qr = q >> 1, qc = q & 1;
+  const int q = blockIdx.y;
+  const int qr = q / SB, qc = q % SB;
   int bi, bj;
   lower_tile(tile, bi, bj);
-  if (bi == bj && qr < qc) return;  // strictly upper quarter of a diagonal tile
+  if (bi == bj && qr < qc) return;  // strictly upper sub-block of a diagonal tile
   const int tid = threadIdx.x;
   const int cx = tid & 63;
   const int ry = tid >> 6;
   const int gr0 = bi * T + 64 * qr;
   const int gc0 = bj * T + 64 * qc;
+  if (gr0 >= d || gc0 >= d) return;
   const bool on_diag = (bi == bj && qr == qc);
   for (int rr = ry; rr < 64; rr += 4) {
     const int lr = 64 * qr + rr, lc = 64 * qc + cx;
     float v = 0.f;
-    for (int s = 0; s < splits; ++s) v += P[((int64_t)s * ntiles + tile) * (T * T) + lr * T + lc];
+    for (int s = 0; s < splits; ++s)
+      v += P[((int64_t)s * ntiles + tile) * ((int64_t)T * T) + (int64_t)lr * T + lc];
     v *= alpha;
     st[rr][cx] = v;
     const int gr = gr0 + rr, gc = gc0 + cx;
     if (gr < d && gc < d && (!on_diag || gc <= gr)) H[(int64_t)gr * d + gc] += v;
   }
   __syncthreads();
-  // mirror: element (gr, gc) with gr > gc goes to H[gc][gr]
   for (int rr = ry; rr < 64; rr += 4) {
     const int gr = gr0 + cx;  // source row (lower)
     const int gc = gc0 + rr;  // source column
@@ -198,13 +214,25 @@ __global__ __launch_bounds__(256) void syrk_reduce_kernel(const float* __restric
 }  // namespace
 
 int syrk_splits(int64_t d, int64_t n) {
+  // One 256x256 workgroup runs per CU at a time.  Pick the split count that
+  // minimises (rounds of 256 workgroups) x (time of one split) plus the time
+  // to write and re-read the fp32 partial tiles.
   const int64_t nb = ceil_div(d, T);
   const int64_t tiles = nb * (nb + 1) / 2;
   const int64_t chunks = ceil_div(n, KC);
-  int64_t s = ceil_div(2048, tiles);
-  if (s > chunks) s = chunks;
-  if (s < 1) s = 1;
-  return (int)s;
+  const double t_tile = 2.0 * T * T * (double)(chunks * KC) / (4.0 * 1024.0 * 2.4e9);
+  const double t_part = (double)T * T * 4.0 * 2.0 / 6.0e12;
+  int64_t best = 1;
+  double best_cost = 1e30;
+  for (int64_t s = 1; s <= 64 && s <= chunks; ++s) {
+    const double rounds = (double)ceil_div(tiles * s, 256);
+    const double cost = rounds * t_tile / (double)s + (double)(s * tiles) * t_part;
+    if (cost < best_cost) {
+      best_cost = cost;
+      best = s;
+    }
+  }
+  return (int)best;
 }
 
 int64_t syrk_kper(int64_t n, int splits) {
@@ -229,8 +257,8 @@ hipError_t launch_syrk_reduce(const float* P, int d, int splits, float alpha, fl
                               hipStream_t s) {
   const int nb = (int)ceil_div(d, T);
   const int tiles = nb * (nb + 1) / 2;
-  hipLaunchKernelGGL(syrk_reduce_kernel, dim3(tiles, 4), dim3(256), 0, s, P, d, splits, tiles,
-                     alpha, H);
+  hipLaunchKernelGGL(syrk_reduce_kernel, dim3(tiles, (T / 64) * (T / 64)), dim3(256), 0, s, P, d,
+                     splits, tiles, alpha, H);
   return hipGetLastError();
 }
 
