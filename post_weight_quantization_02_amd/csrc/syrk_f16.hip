@@ -172,6 +172,188 @@ __global__ __launch_bounds__(256, 1) void syrk_partial_kernel(const _Float16* __
       }
 }
 
+// XCD-aware tile order.  Workgroups are handed to the 8 XCDs round-robin by
+// linear id, and each XCD has its own L2.  Tiles are listed group-pair by
+// group-pair (groups of 4 block rows/columns), and XCD x takes the x-th
+// contiguous segment of that list, so the ~17 tiles an XCD works on at once
+// share few 256-channel blocks of X and re-read them from its L2.
+constexpr int kXcds = 8;
+constexpr int kGroup = 4;
+
+__device__ inline void grouped_tile(int idx, int nb, int& bi, int& bj) {
+  const int ng = (nb + kGroup - 1) / kGroup;
+  for (int gi = 0; gi < ng; ++gi) {
+    const int rows = min(kGroup, nb - gi * kGroup);
+    for (int gj = 0; gj <= gi; ++gj) {
+      const int cols = min(kGroup, nb - gj * kGroup);
+      const int cnt = (gi == gj) ? rows * (rows + 1) / 2 : rows * cols;
+      if (idx < cnt) {
+        int r, c;
+        if (gi == gj) {
+          lower_tile(idx, r, c);
+        } else {
+          r = idx / cols;
+          c = idx % cols;
+        }
+        bi = gi * kGroup + r;
+        bj = gj * kGroup + c;
+        return;
+      }
+      idx -= cnt;
+    }
+  }
+  bi = bj = -1;
+}
+
+// Slot t of a split (grid padded to a multiple of 8 slots) -> tile, or false
+// for a padding slot.
+__device__ inline bool xcd_tile(int t, int slots, int ntiles, int nb, int& bi, int& bj) {
+  const int per = slots / kXcds;
+  const int idx = (t % kXcds) * per + t / kXcds;
+  if (idx >= ntiles) return false;
+  grouped_tile(idx, nb, bi, bj);
+  return true;
+}
+
+// ------------------------------------------------------------------ fast path
+// Interior 256x256 tiles with whole 32-token chunks: every chunk goes from HBM
+// straight into LDS with global_load_lds_dwordx4 (no register staging) into a
+// ring of NS stages, so several chunks are in flight while one is consumed.
+// Rows are 512 bytes, unpadded; the 16-byte pieces of row R are XOR-permuted
+// by sw(R) so the 16 rows one transposing read touches (R = 8g + r, g,r < 4)
+// use 16 distinct bank groups.
+constexpr int NS = 4;                 // LDS ring stages
+constexpr int RB = T * 2;             // bytes per LDS row (unpadded)
+constexpr int BLK = KC * T;           // halves per operand block per stage
+
+__device__ inline int swz(int row) { return 2 * ((row & 3) | (((row >> 3) & 3) << 2)); }
+
+// Swizzled transposing read: 8 tokens of channel c0 + lane%16 from rows kb..kb+7.
+__device__ inline half8 tr_frag_sw(const _Float16* tile, int kb, int c0, int lane) {
+  const int s = lane & 15;
+  const int r0 = kb + (s >> 2);
+  const int q = (c0 >> 3) + ((s & 3) >> 1);
+  const int off = 4 * (s & 1);
+  const _Float16* p0 = tile + r0 * T + 8 * (q ^ swz(r0)) + off;
+  const _Float16* p1 = p0 + 4 * T;  // rows r0 + 4 share r0's swizzle
+  const f16x4 lo = __builtin_bit_cast(f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p0));
+  const f16x4 hi = __builtin_bit_cast(f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p1));
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Issue the direct loads of one 32 x 256 operand block: 16 wave instructions
+// of two rows each; wave w issues row pairs w, w+4, w+8, w+12.
+__device__ inline void issue_block(const _Float16* __restrict__ X, int64_t ldx, int64_t t0,
+                                   int c0, _Float16* dst, int wave, int lane) {
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int rp = wave + 4 * u;
+    const int row = 2 * rp + (lane >> 5);
+    const int ql = (lane & 31) ^ swz(row);
+    const _Float16* g = X + (t0 + row) * ldx + c0 + 8 * ql;
+    __builtin_amdgcn_global_load_lds((const void*)g,
+                                     (__attribute__((address_space(3))) void*)(dst + rp * 2 * T),
+                                     16, 0, 0);
+  }
+}
+
+// s_waitcnt immediate: vmcnt <= n, expcnt and lgkmcnt unconstrained (gfx9 encoding)
+template <int N>
+__device__ inline void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+__device__ inline void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Chunks k = 0..nk-1 of 32 tokens flow through an LDS ring of NS stages:
+// direct loads for chunk k+NS-1 are issued right after the barrier that
+// publishes chunk k, so up to NS-1 chunks are in flight while one is
+// consumed.  Before that barrier each wave waits only for its own loads of
+// stage k (vmcnt) -- the LDS reads of stage k-1 have already been consumed by
+// its MFMAs -- so a bare s_barrier suffices; __syncthreads() would also
+// drain the loads still in flight.
+template <bool DIAG>
+__device__ inline void fast_body(const _Float16* __restrict__ X, int64_t ldx, int64_t kbeg,
+                                 int64_t nk, int ca, int cb, _Float16* ring, f32x4 (&acc)[8][8],
+                                 int wave, int lane, int wm, int wn) {
+  constexpr int LPS = DIAG ? 4 : 8;  // direct loads per stage per wave
+  for (int64_t k = 0; k < NS - 1 && k < nk; ++k) {
+    _Float16* st = ring + (int)(k % NS) * 2 * BLK;
+    issue_block(X, ldx, kbeg + k * KC, ca, st, wave, lane);
+    if (!DIAG) issue_block(X, ldx, kbeg + k * KC, cb, st + BLK, wave, lane);
+  }
+  const int kg = 8 * (lane >> 4);
+  for (int64_t k = 0; k < nk; ++k) {
+    // stage k must have landed; stages k+1, k+2 may still be in flight
+    if (k + 2 < nk) wait_vm<2 * LPS>();
+    else if (k + 1 < nk) wait_vm<LPS>();
+    else wait_vm<0>();
+    lds_barrier();
+    if (k + NS - 1 < nk) {
+      const int64_t kn = k + NS - 1;
+      _Float16* st = ring + (int)(kn % NS) * 2 * BLK;
+      issue_block(X, ldx, kbeg + kn * KC, ca, st, wave, lane);
+      if (!DIAG) issue_block(X, ldx, kbeg + kn * KC, cb, st + BLK, wave, lane);
+    }
+    const _Float16* a_s = ring + (int)(k % NS) * 2 * BLK;
+    const _Float16* b_s = DIAG ? a_s : a_s + BLK;
+    half8 bf[8];
+#pragma unroll
+    for (int b = 0; b < 8; ++b) bf[b] = tr_frag_sw(b_s, kg, 128 * wn + 16 * b, lane);
+#pragma unroll
+    for (int a = 0; a < 8; ++a) {
+      const half8 af = tr_frag_sw(a_s, kg, 128 * wm + 16 * a, lane);
+#pragma unroll
+      for (int b = 0; b < 8; ++b)
+        acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bf[b], acc[a][b], 0, 0, 0);
+    }
+  }
+}
+
+__global__ __launch_bounds__(256, 1) void syrk_fast_kernel(const _Float16* __restrict__ X,
+                                                           int64_t ldx, int64_t n, int64_t kper,
+                                                           int nb, float* __restrict__ P) {
+  __shared__ __attribute__((aligned(16))) _Float16 ring[NS * 2 * BLK];
+  const int ntiles = nb * (nb + 1) / 2;
+  const int split = blockIdx.y;
+  int bi, bj;
+  if (!xcd_tile(blockIdx.x, gridDim.x, ntiles, nb, bi, bj)) return;
+  const int tile = bi * (bi + 1) / 2 + bj;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int64_t kbeg = (int64_t)split * kper;
+  const int64_t kend = (kbeg + kper < n) ? kbeg + kper : n;
+  const int64_t nk = (kend > kbeg) ? (kend - kbeg) / KC : 0;  // whole chunks only
+
+  f32x4 acc[8][8];
+#pragma unroll
+  for (int a = 0; a < 8; ++a)
+#pragma unroll
+    for (int b = 0; b < 8; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (bi == bj)
+    fast_body<true>(X, ldx, kbeg, nk, bi * T, bj * T, ring, acc, wave, lane, wm, wn);
+  else
+    fast_body<false>(X, ldx, kbeg, nk, bi * T, bj * T, ring, acc, wave, lane, wm, wn);
+
+  float* out = P + ((int64_t)split * ntiles + tile) * ((int64_t)T * T);
+#pragma unroll
+  for (int a = 0; a < 8; ++a)
+#pragma unroll
+    for (int b = 0; b < 8; ++b)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 128 * wm + 16 * a + 4 * (lane >> 4) + i;
+        const int c = 128 * wn + 16 * b + (lane & 15);
+        out[r * T + c] = acc[a][b][i];
+      }
+}
+
 // Sum the split partials of one 64x64 sub-block of a lower tile in split
 // order, add alpha * sum into H, and mirror into the upper triangle.
 __global__ __launch_bounds__(256) void syrk_reduce_kernel(const float* __restrict__ P, int d,
@@ -246,7 +428,10 @@ hipError_t launch_syrk_partial(const _Float16* X, int64_t ldx, int d, int64_t n,
   const int tiles = nb * (nb + 1) / 2;
   dim3 grid(tiles, splits);
   const bool vec = (ldx % 8 == 0) && ((reinterpret_cast<uintptr_t>(X) & 15) == 0);
-  if (vec)
+  if (vec && d % T == 0 && n % KC == 0)
+    hipLaunchKernelGGL(syrk_fast_kernel, dim3((unsigned)round_up(tiles, kXcds), splits), dim3(256),
+                       0, s, X, ldx, n, kper, nb, P);
+  else if (vec)
     hipLaunchKernelGGL(syrk_partial_kernel<true>, grid, dim3(256), 0, s, X, ldx, d, n, kper, P);
   else
     hipLaunchKernelGGL(syrk_partial_kernel<false>, grid, dim3(256), 0, s, X, ldx, d, n, kper, P);
