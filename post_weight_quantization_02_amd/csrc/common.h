@@ -58,11 +58,12 @@ hipError_t launch_sweep_block(float* Wk, int64_t ldk, int64_t rows, int64_t cols
                               const float* Hinv, int bits, int groupsize, uint8_t* codes,
                               float* scales, float* zeros, float* Err, float* loss_part,
                               hipStream_t s);
-hipError_t launch_lazy_update(float* Wk, int64_t ldk, int64_t rows, int64_t cols, int i1, int i2,
-                              const float* Err, const float* Hinv, hipStream_t s);
+hipError_t launch_lazy_update(float* Wk, int64_t ldk, int64_t rows, int64_t cols, int k0, int k1,
+                              int c0, int c1, const float* Err, const float* Hinv, hipStream_t s);
 hipError_t launch_loss_reduce(const float* loss_part, int64_t nparts, int64_t cols,
                               float* losses, hipStream_t s);
 constexpr int kSweepRows = 16;  // rows per sweep workgroup
 constexpr int kBlock = 128;     // columns per block
+constexpr int kSuperBlock = 512;  // columns per superblock of the two-level lazy update
 
 }  // namespace gptq

@@ -192,13 +192,28 @@ gptq_status gptq_quantize_layer(const void* W, int w_dtype, int64_t rows, int64_
   float* lpart = reinterpret_cast<float*>(ws + L.loss_off);
 
   if (launch_convert_w(W, w_dtype, rows, cols, ldw, Wk, L.ldk, s) != hipSuccess) return GPTQ_ERR_HIP;
-  for (int64_t i1 = 0; i1 < cols; i1 += kBlock) {
-    const int64_t i2 = (i1 + kBlock < cols) ? i1 + kBlock : cols;
-    if (launch_sweep_block(Wk, L.ldk, rows, cols, (int)i1, Hinv, bits, groupsize, codes, scales,
-                           zeros, Err, lpart, s) != hipSuccess)
-      return GPTQ_ERR_HIP;
-    if (i2 < cols && launch_lazy_update(Wk, L.ldk, rows, cols, (int)i1, (int)i2, Err, Hinv, s) !=
-                         hipSuccess)
+  // Two-level lazy batching.  Inside a superblock of SB columns each block's
+  // errors are applied at once to the rest of the superblock; the columns
+  // after the superblock receive all of its errors in one GEMM with K = SB.
+  // Every column still gets every update before its block is swept (and
+  // before its group's statistics are taken, since SB is a multiple of the
+  // group size when groups span blocks), so the result equals per-block lazy
+  // updates in exact arithmetic.
+  const int64_t SB = (groupsize > kBlock) ? (groupsize > kSuperBlock ? groupsize : kSuperBlock)
+                                          : kSuperBlock;
+  for (int64_t s0 = 0; s0 < cols; s0 += SB) {
+    const int64_t s1 = (s0 + SB < cols) ? s0 + SB : cols;
+    for (int64_t i1 = s0; i1 < s1; i1 += kBlock) {
+      const int64_t i2 = (i1 + kBlock < s1) ? i1 + kBlock : s1;
+      if (launch_sweep_block(Wk, L.ldk, rows, cols, (int)i1, Hinv, bits, groupsize, codes, scales,
+                             zeros, Err, lpart, s) != hipSuccess)
+        return GPTQ_ERR_HIP;
+      if (launch_lazy_update(Wk, L.ldk, rows, cols, (int)i1, (int)i2, (int)i2, (int)s1, Err, Hinv,
+                             s) != hipSuccess)
+        return GPTQ_ERR_HIP;
+    }
+    if (launch_lazy_update(Wk, L.ldk, rows, cols, (int)s0, (int)s1, (int)s1, (int)cols, Err, Hinv,
+                           s) != hipSuccess)
       return GPTQ_ERR_HIP;
   }
   if (launch_loss_reduce(lpart, L.nparts, cols, losses, s) != hipSuccess) return GPTQ_ERR_HIP;

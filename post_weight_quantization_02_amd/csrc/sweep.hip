@@ -55,8 +55,36 @@ __device__ inline void grid_params(float mn, float mx, float qm, float& s, float
   z = fminf(fmaxf(rintf(-mn / s), 0.f), qm);
 }
 
+// Row min/max of the current group across the 16 lanes of a row and the
+// resulting grid; lane 0 of the row records it.
+__device__ inline void group_stats(float mn, float mx, float qm, float& s, float& z, bool rv,
+                                   int l, int64_t row, int64_t ngroups, int64_t gi,
+                                   float* __restrict__ scales, float* __restrict__ zeros) {
+  row_minmax(mn, mx);
+  grid_params(mn, mx, qm, s, z);
+  if (rv && l == 0) {
+    scales[row * ngroups + gi] = s;
+    zeros[row * ngroups + gi] = z;
+  }
+}
+
+// Value of `v` held by lane `src + 16*rg` of the wave, for each lane's row
+// group rg (src is wave-uniform): four readlanes and a select.
+__device__ inline float bcast16(float v, int src, int rg) {
+  const float e0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), src));
+  const float e1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), src + 16));
+  const float e2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), src + 32));
+  const float e3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), src + 48));
+  return rg == 0 ? e0 : rg == 1 ? e1 : rg == 2 ? e2 : e3;
+}
+
 // G: group size when it divides the block (16, 32, 64, 128); G == 0 means the
 // group spans several blocks (groupsize a multiple of 128).
+//
+// Column j = 16*kj + lj lives in register kj of lane lj.  The register group
+// kj is an unrolled outer loop (so every register index is a compile-time
+// constant) and the 16 steps inside it are a runtime loop whose owner lane lj
+// is wave-uniform.
 template <int G>
 __global__ __launch_bounds__(256) void sweep_kernel(float* __restrict__ Wk, int64_t ldk,
                                                     int64_t rows, int64_t cols, int i1,
@@ -117,12 +145,7 @@ __global__ __launch_bounds__(256) void sweep_kernel(float* __restrict__ Wk, int6
           mn = fminf(mn, v);
           mx = fmaxf(mx, v);
         }
-      row_minmax(mn, mx);
-      grid_params(mn, mx, qm, s, z);
-      if (rv && l == 0) {
-        scales[row * ngroups + gi] = s;
-        zeros[row * ngroups + gi] = z;
-      }
+      group_stats(mn, mx, qm, s, z, rv, l, row, ngroups, gi, scales, zeros);
     } else if (rv) {
       s = scales[row * ngroups + gi];
       z = zeros[row * ngroups + gi];
@@ -137,33 +160,32 @@ __global__ __launch_bounds__(256) void sweep_kernel(float* __restrict__ Wk, int6
   }
 
 #pragma unroll
-  for (int j = 0; j < BC; ++j) {
-    if (j < nbc) {
-      const int kj = j >> 4, lj = j & 15;
-      if (G != 0 && j % (G > 0 ? G : 1) == 0) {
-        float mn = INFINITY, mx = -INFINITY;
+  for (int kj = 0; kj < CPL; ++kj) {
+    if (RL * kj >= nbc) break;
+    if (G != 0 && (RL * kj) % (G > 0 ? G : 1) == 0) {
+      // a group starts at column 16*kj: statistics over its current values
+      float mn = INFINITY, mx = -INFINITY;
 #pragma unroll
-        for (int k = 0; k < CPL; ++k) {
-          const int c = l + RL * k;
-          if (c >= j && c < j + G && c < nbc) {
-            mn = fminf(mn, w[k]);
-            mx = fmaxf(mx, w[k]);
-          }
-        }
-        row_minmax(mn, mx);
-        grid_params(mn, mx, qm, s, z);
-        if (rv && l == 0) {
-          const int64_t gi = (i1 + j) / groupsize;
-          scales[row * ngroups + gi] = s;
-          zeros[row * ngroups + gi] = z;
+      for (int k = 0; k < CPL; ++k) {
+        const int c = l + RL * k;
+        if (k >= kj && k < kj + (G > 0 ? G : RL) / RL && c < nbc) {
+          mn = fminf(mn, w[k]);
+          mx = fmaxf(mx, w[k]);
         }
       }
+      group_stats(mn, mx, qm, s, z, rv, l, row, ngroups, (i1 + RL * kj) / groupsize, scales,
+                  zeros);
+    }
+    const int jend = min(RL, nbc - RL * kj);
+#pragma unroll 1
+    for (int lj = 0; lj < jend; ++lj) {
+      const int j = RL * kj + lj;
       const float x = w[kj];
       const float t = x / s + z;
       const float q = fminf(fmaxf(rintf(t), 0.f), qm);
       const float err = x - (q - z) * s;
       const float e = err * rdiag[j];
-      const float eb = __shfl(e, lj, RL);
+      const float eb = bcast16(e, lj, rg);
       if (l == lj) {
         qc[kj] = q;
         ev[kj] = eb;
@@ -199,22 +221,28 @@ __global__ __launch_bounds__(256) void sweep_kernel(float* __restrict__ Wk, int6
 }
 
 // ---------------------------------------------------------------- lazy GEMM
+// W[:, c0:c1] -= Err[:, k0:k1] * Hinv[k0:k1, c0:c1]  (fp32, MFMA 16x16x4).
+// 128x128 output tiles, 4 waves of 64x64; K streamed in chunks of 32 through
+// double-buffered LDS stored k-major (pitch 144 floats: the four k rows an
+// operand read touches fall in four different 16-bank groups); the next
+// chunk's global loads are issued before the current chunk's MFMAs, and the
+// C tile is fetched before the last chunk so its latency overlaps the math.
 constexpr int LT = 128;  // output tile edge
-constexpr int LK = 16;   // K chunk
-constexpr int LP = LT + 4;
+constexpr int LK = 32;   // K chunk
+constexpr int LP = LT + 16;
 
 __global__ __launch_bounds__(256) void lazy_kernel(float* __restrict__ Wk, int64_t ldk,
-                                                   int64_t rows, int64_t cols, int i1, int i2,
-                                                   const float* __restrict__ Err,
+                                                   int64_t rows, int64_t cols, int k0, int k1,
+                                                   int c0, int c1, const float* __restrict__ Err,
                                                    const float* __restrict__ Hinv) {
-  __shared__ float As[LK][LP];  // [k][m]
-  __shared__ float Bs[LK][LP];  // [k][n]
+  __shared__ float As[2][LK][LP];  // [k][m]
+  __shared__ float Bs[2][LK][LP];  // [k][n]
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int64_t r0 = (int64_t)blockIdx.y * LT;
-  const int64_t n0 = (int64_t)i2 + (int64_t)blockIdx.x * LT;
-  const int K = i2 - i1;
+  const int64_t n0 = (int64_t)c0 + (int64_t)blockIdx.x * LT;
+  const int K = k1 - k0;
 
   f32x4 acc[4][4];
 #pragma unroll
@@ -222,35 +250,96 @@ __global__ __launch_bounds__(256) void lazy_kernel(float* __restrict__ Wk, int64
 #pragma unroll
     for (int b = 0; b < 4; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int kc = 0; kc < K; kc += LK) {
+  // loader mapping: A chunk = 128 rows x 32 k = 1024 float4 (4 per thread);
+  // B chunk = 32 k-rows x 128 n = 1024 float4 (4 per thread)
+  float4 av[4], bv[4];
+  auto gload = [&](int kc) {
 #pragma unroll
-    for (int q = 0; q < (LT * LK) / 256; ++q) {
+    for (int q = 0; q < 4; ++q) {
       const int e = tid + 256 * q;
-      // A: Err rows, 16 consecutive k per row
-      const int kk = e & (LK - 1), mm = e >> 4;
-      const int64_t gr = r0 + mm;
-      As[kk][mm] = (gr < rows && kc + kk < K) ? Err[gr * ldk + i1 + kc + kk] : 0.f;
-      // B: Hinv rows i1+kc+kk, 128 consecutive columns
-      const int nn = e & (LT - 1), kb = e >> 7;
+      const int m = e >> 3, kk = (e & 7) * 4;  // A: 8 float4 per row
+      const int64_t gr = r0 + m;
+      const int gk = kc + kk;
+      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (gr < rows) {
+        const float* p = Err + gr * ldk + k0 + gk;
+        if (gk + 4 <= K) {
+          v = *reinterpret_cast<const float4*>(p);
+        } else {
+          if (gk + 0 < K) v.x = p[0];
+          if (gk + 1 < K) v.y = p[1];
+          if (gk + 2 < K) v.z = p[2];
+        }
+      }
+      av[q] = v;
+      const int kb = e >> 5, nn = (e & 31) * 4;  // B: 32 float4 per k-row
       const int64_t gc = n0 + nn;
-      Bs[kb][nn] = (gc < cols && kc + kb < K) ? Hinv[(int64_t)(i1 + kc + kb) * cols + gc] : 0.f;
+      float4 u = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (kc + kb < K) {
+        const float* p = Hinv + (int64_t)(k0 + kc + kb) * cols + gc;
+        if (gc + 4 <= c1) {
+          u = make_float4(p[0], p[1], p[2], p[3]);
+        } else {
+          if (gc + 0 < c1) u.x = p[0];
+          if (gc + 1 < c1) u.y = p[1];
+          if (gc + 2 < c1) u.z = p[2];
+        }
+      }
+      bv[q] = u;
     }
-    __syncthreads();
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = tid + 256 * q;
+      const int m = e >> 3, kk = (e & 7) * 4;
+      As[buf][kk + 0][m] = av[q].x;
+      As[buf][kk + 1][m] = av[q].y;
+      As[buf][kk + 2][m] = av[q].z;
+      As[buf][kk + 3][m] = av[q].w;
+      const int kb = e >> 5, nn = (e & 31) * 4;
+      *reinterpret_cast<float4*>(&Bs[buf][kb][nn]) = bv[q];
+    }
+  };
+
+  f32x4 cv[4][4];
+  const int nchunks = (K + LK - 1) / LK;
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  int buf = 0;
+  for (int ch = 0; ch < nchunks; ++ch) {
+    const bool more = ch + 1 < nchunks;
+    if (more) gload((ch + 1) * LK);
+    if (ch + 1 == nchunks) {
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int64_t r = r0 + 64 * wm + 16 * a + 4 * (lane >> 4) + i;
+            const int64_t c = n0 + 64 * wn + 16 * b + (lane & 15);
+            cv[a][b][i] = (r < rows && c < c1) ? Wk[r * ldk + c] : 0.f;
+          }
+    }
 #pragma unroll
     for (int ks = 0; ks < LK; ks += 4) {
       const int kr = ks + (lane >> 4);
       float af[4], bf[4];
 #pragma unroll
-      for (int a = 0; a < 4; ++a) af[a] = As[kr][64 * wm + 16 * a + (lane & 15)];
+      for (int a = 0; a < 4; ++a) af[a] = As[buf][kr][64 * wm + 16 * a + (lane & 15)];
 #pragma unroll
-      for (int b = 0; b < 4; ++b) bf[b] = Bs[kr][64 * wn + 16 * b + (lane & 15)];
+      for (int b = 0; b < 4; ++b) bf[b] = Bs[buf][kr][64 * wn + 16 * b + (lane & 15)];
 #pragma unroll
       for (int a = 0; a < 4; ++a)
 #pragma unroll
         for (int b = 0; b < 4; ++b)
           acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[a], bf[b], acc[a][b], 0, 0, 0);
     }
+    if (more) lstore(buf ^ 1);
     __syncthreads();
+    buf ^= 1;
   }
 #pragma unroll
   for (int a = 0; a < 4; ++a)
@@ -260,7 +349,7 @@ __global__ __launch_bounds__(256) void lazy_kernel(float* __restrict__ Wk, int64
       for (int i = 0; i < 4; ++i) {
         const int64_t r = r0 + 64 * wm + 16 * a + 4 * (lane >> 4) + i;
         const int64_t c = n0 + 64 * wn + 16 * b + (lane & 15);
-        if (r < rows && c < cols) Wk[r * ldk + c] -= acc[a][b][i];
+        if (r < rows && c < c1) Wk[r * ldk + c] = cv[a][b][i] - acc[a][b][i];
       }
 }
 
@@ -317,10 +406,12 @@ hipError_t launch_sweep_block(float* Wk, int64_t ldk, int64_t rows, int64_t cols
   return hipGetLastError();
 }
 
-hipError_t launch_lazy_update(float* Wk, int64_t ldk, int64_t rows, int64_t cols, int i1, int i2,
-                              const float* Err, const float* Hinv, hipStream_t s) {
-  dim3 grid((unsigned)ceil_div(cols - i2, LT), (unsigned)ceil_div(rows, LT));
-  hipLaunchKernelGGL(lazy_kernel, grid, dim3(256), 0, s, Wk, ldk, rows, cols, i1, i2, Err, Hinv);
+hipError_t launch_lazy_update(float* Wk, int64_t ldk, int64_t rows, int64_t cols, int k0, int k1,
+                              int c0, int c1, const float* Err, const float* Hinv, hipStream_t s) {
+  if (c1 <= c0 || k1 <= k0) return hipSuccess;
+  dim3 grid((unsigned)ceil_div(c1 - c0, LT), (unsigned)ceil_div(rows, LT));
+  hipLaunchKernelGGL(lazy_kernel, grid, dim3(256), 0, s, Wk, ldk, rows, cols, k0, k1, c0, c1, Err,
+                     Hinv);
   return hipGetLastError();
 }
 
