@@ -19,9 +19,10 @@
 //   * Step j: every lane evaluates the quantizer on its register j/16 (only
 //     lane j%16 holds column j), the owner's scaled error is broadcast inside
 //     the 16-lane group, and each lane applies the rank-1 update to the
-//     columns it holds.  Hinv's 128x128 diagonal block is in LDS, permuted so
-//     a lane's 8 coefficients for step j are contiguous; entries left of the
-//     diagonal are zero, which makes the update of finished columns a no-op.
+//     columns it holds.  Hinv's 128x128 diagonal block is in LDS row by row
+//     (lanes of a row read 16 consecutive floats, the four rows of a wave
+//     the same ones); entries left of the diagonal are zero, which makes the
+//     update of finished columns a no-op.
 //   * Group min/max is a per-lane reduction followed by a 4-step xor shuffle
 //     across the 16 lanes of the row.
 //   * Per-column loss partials are reduced inside the workgroup and written
@@ -55,13 +56,24 @@ __device__ inline void grid_params(float mn, float mx, float qm, float& s, float
   z = fminf(fmaxf(rintf(-mn / s), 0.f), qm);
 }
 
+// x / s correctly rounded (IEEE binary32), given rs = RN(1/s): the residual
+// x - q0*s is exact under FMA, and one correction step yields RN(x/s)
+// (Markstein's division theorem).  For |x| < 2^-100 the correction may be
+// off by an ulp, but then x/s + z rounds to the same integer either way.
+__device__ inline float div_rn(float x, float s, float rs) {
+  const float q0 = x * rs;
+  const float r = __builtin_fmaf(-q0, s, x);
+  return __builtin_fmaf(r, rs, q0);
+}
+
 // Row min/max of the current group across the 16 lanes of a row and the
 // resulting grid; lane 0 of the row records it.
-__device__ inline void group_stats(float mn, float mx, float qm, float& s, float& z, bool rv,
-                                   int l, int64_t row, int64_t ngroups, int64_t gi,
+__device__ inline void group_stats(float mn, float mx, float qm, float& s, float& z, float& rs,
+                                   bool rv, int l, int64_t row, int64_t ngroups, int64_t gi,
                                    float* __restrict__ scales, float* __restrict__ zeros) {
   row_minmax(mn, mx);
   grid_params(mn, mx, qm, s, z);
+  rs = 1.0f / s;
   if (rv && l == 0) {
     scales[row * ngroups + gi] = s;
     zeros[row * ngroups + gi] = z;
@@ -69,13 +81,15 @@ __device__ inline void group_stats(float mn, float mx, float qm, float& s, float
 }
 
 // Value of `v` held by lane `src + 16*rg` of the wave, for each lane's row
-// group rg (src is wave-uniform): four readlanes and a select.
-__device__ inline float bcast16(float v, int src, int rg) {
-  const float e0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), src));
-  const float e1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), src + 16));
-  const float e2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), src + 32));
-  const float e3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), src + 48));
-  return rg == 0 ? e0 : rg == 1 ? e1 : rg == 2 ? e2 : e3;
+// group rg (src is wave-uniform): four readlanes combined with the lane's 0/1
+// row-group masks (branch-free; exact because each product is v or 0).
+__device__ inline float bcast16(float v, int src, const float (&m)[4]) {
+  const int iv = __builtin_bit_cast(int, v);
+  const float e0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(iv, src));
+  const float e1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(iv, src + 16));
+  const float e2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(iv, src + 32));
+  const float e3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(iv, src + 48));
+  return (e0 * m[0] + e1 * m[1]) + (e2 * m[2] + e3 * m[3]);
 }
 
 // G: group size when it divides the block (16, 32, 64, 128); G == 0 means the
@@ -94,7 +108,7 @@ __global__ __launch_bounds__(256) void sweep_kernel(float* __restrict__ Wk, int6
                                                     float* __restrict__ zeros,
                                                     float* __restrict__ Err,
                                                     float* __restrict__ lpart) {
-  __shared__ __attribute__((aligned(16))) float Up[BC * RL * CPL];  // [j][l][k]
+  __shared__ __attribute__((aligned(16))) float Ub[BC * BC];  // Hinv block, row j at Ub + 128 j
   __shared__ float rdiag[BC];
   __shared__ float lsum[4][BC];
 
@@ -108,11 +122,40 @@ __global__ __launch_bounds__(256) void sweep_kernel(float* __restrict__ Wk, int6
   const int nbc = (int)((cols - i1) < BC ? (cols - i1) : BC);
   const int64_t ngroups = ceil_div(cols, groupsize);
 
-  for (int e = tid; e < BC * BC; e += 256) {
-    const int j = e >> 7, c = e & (BC - 1);
-    float v = 0.f;
-    if (c >= j && c < nbc) v = Hinv[(int64_t)(i1 + j) * cols + i1 + c];
-    Up[(j * RL + (c & 15)) * CPL + (c >> 4)] = v;
+  // Hinv[i1:i1+128, i1:i1+128] with the part left of the diagonal (and past
+  // the last column) zeroed: 16 float4 per thread, all loads issued first
+  {
+    float4 v[16];
+    const bool vec = (cols % 4 == 0) && (reinterpret_cast<uintptr_t>(Hinv) % 16 == 0);
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int e = tid + 256 * q;  // float4 index: row e/32, columns 4*(e%32)..
+      const int j = e >> 5, c = (e & 31) * 4;
+      const float* p = Hinv + (int64_t)(i1 + j) * cols + i1 + c;
+      float4 u = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (j < nbc) {
+        if (vec && c + 4 <= nbc) {
+          u = *reinterpret_cast<const float4*>(p);
+        } else {
+          if (c + 0 < nbc) u.x = p[0];
+          if (c + 1 < nbc) u.y = p[1];
+          if (c + 2 < nbc) u.z = p[2];
+          if (c + 3 < nbc) u.w = p[3];
+        }
+      }
+      v[q] = u;
+    }
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int e = tid + 256 * q;
+      const int j = e >> 5, c = (e & 31) * 4;
+      float4 u = v[q];
+      if (c + 0 < j) u.x = 0.f;
+      if (c + 1 < j) u.y = 0.f;
+      if (c + 2 < j) u.z = 0.f;
+      if (c + 3 < j) u.w = 0.f;
+      *reinterpret_cast<float4*>(Ub + j * BC + c) = u;
+    }
   }
   for (int j = tid; j < BC; j += 256)
     rdiag[j] = (j < nbc) ? 1.f / Hinv[(int64_t)(i1 + j) * cols + i1 + j] : 0.f;
@@ -126,7 +169,10 @@ __global__ __launch_bounds__(256) void sweep_kernel(float* __restrict__ Wk, int6
   __syncthreads();
 
   const float qm = (float)((1 << bits) - 1);
-  float s = 1.f, z = 0.f;
+  float s = 1.f, z = 0.f, rs = 1.f;
+  float rmask[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) rmask[r] = (rg == r) ? 1.f : 0.f;
   if (G == 0) {
     // group of groupsize columns spanning blocks
     const int64_t gi = i1 / groupsize;
@@ -145,10 +191,11 @@ __global__ __launch_bounds__(256) void sweep_kernel(float* __restrict__ Wk, int6
           mn = fminf(mn, v);
           mx = fmaxf(mx, v);
         }
-      group_stats(mn, mx, qm, s, z, rv, l, row, ngroups, gi, scales, zeros);
+      group_stats(mn, mx, qm, s, z, rs, rv, l, row, ngroups, gi, scales, zeros);
     } else if (rv) {
       s = scales[row * ngroups + gi];
       z = zeros[row * ngroups + gi];
+      rs = 1.0f / s;
     }
   }
 
@@ -173,26 +220,38 @@ __global__ __launch_bounds__(256) void sweep_kernel(float* __restrict__ Wk, int6
           mx = fmaxf(mx, w[k]);
         }
       }
-      group_stats(mn, mx, qm, s, z, rv, l, row, ngroups, (i1 + RL * kj) / groupsize, scales,
+      group_stats(mn, mx, qm, s, z, rs, rv, l, row, ngroups, (i1 + RL * kj) / groupsize, scales,
                   zeros);
     }
     const int jend = min(RL, nbc - RL * kj);
+    // this lane's column 16*kj + l: its 1/Hinv[j][j] (only the owner's is used)
+    const float rd = rdiag[RL * kj + l];
+    float u[CPL], un[CPL];
+#pragma unroll
+    for (int k = kj; k < CPL; ++k) u[k] = Ub[(RL * kj) * BC + l + RL * k];
 #pragma unroll 1
     for (int lj = 0; lj < jend; ++lj) {
       const int j = RL * kj + lj;
+      // next step's Hinv row segment, off the dependency chain
+      if (lj + 1 < jend) {
+#pragma unroll
+        for (int k = kj; k < CPL; ++k) un[k] = Ub[(j + 1) * BC + l + RL * k];
+      }
       const float x = w[kj];
-      const float t = x / s + z;
+      const float t = div_rn(x, s, rs) + z;
       const float q = fminf(fmaxf(rintf(t), 0.f), qm);
-      const float err = x - (q - z) * s;
-      const float e = err * rdiag[j];
-      const float eb = bcast16(e, lj, rg);
+      const float err = __builtin_fmaf(-(q - z), s, x);
+      const float e = err * rd;
+      const float eb = bcast16(e, lj, rmask);
       if (l == lj) {
         qc[kj] = q;
         ev[kj] = eb;
       }
-      const float* u = Up + (j * RL + l) * CPL;
 #pragma unroll
-      for (int k = kj; k < CPL; ++k) w[k] -= eb * u[k];
+      for (int k = kj; k < CPL; ++k) {
+        w[k] = __builtin_fmaf(-eb, u[k], w[k]);
+        u[k] = un[k];
+      }
     }
   }
 
@@ -231,31 +290,35 @@ constexpr int LT = 128;  // output tile edge
 constexpr int LK = 32;   // K chunk
 constexpr int LP = LT + 16;
 
+template <int MT>  // 16x16 MFMA tiles per wave along rows: workgroup tile (32*MT) x 128
 __global__ __launch_bounds__(256) void lazy_kernel(float* __restrict__ Wk, int64_t ldk,
                                                    int64_t rows, int64_t cols, int k0, int k1,
                                                    int c0, int c1, const float* __restrict__ Err,
                                                    const float* __restrict__ Hinv) {
-  __shared__ float As[2][LK][LP];  // [k][m]
+  constexpr int TM = 32 * MT;      // rows per workgroup tile
+  constexpr int PM = TM + 16;
+  constexpr int AV = TM * LK / 4 / 256;  // float4 A loads per thread
+  __shared__ float As[2][LK][PM];  // [k][m]
   __shared__ float Bs[2][LK][LP];  // [k][n]
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int64_t r0 = (int64_t)blockIdx.y * LT;
+  const int64_t r0 = (int64_t)blockIdx.y * TM;
   const int64_t n0 = (int64_t)c0 + (int64_t)blockIdx.x * LT;
   const int K = k1 - k0;
 
-  f32x4 acc[4][4];
+  f32x4 acc[MT][4];
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+  for (int a = 0; a < MT; ++a)
 #pragma unroll
     for (int b = 0; b < 4; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // loader mapping: A chunk = 128 rows x 32 k = 1024 float4 (4 per thread);
   // B chunk = 32 k-rows x 128 n = 1024 float4 (4 per thread)
-  float4 av[4], bv[4];
+  float4 av[AV], bv[4];
   auto gload = [&](int kc) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < AV; ++q) {
       const int e = tid + 256 * q;
       const int m = e >> 3, kk = (e & 7) * 4;  // A: 8 float4 per row
       const int64_t gr = r0 + m;
@@ -272,6 +335,10 @@ __global__ __launch_bounds__(256) void lazy_kernel(float* __restrict__ Wk, int64
         }
       }
       av[q] = v;
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = tid + 256 * q;
       const int kb = e >> 5, nn = (e & 31) * 4;  // B: 32 float4 per k-row
       const int64_t gc = n0 + nn;
       float4 u = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -290,19 +357,23 @@ __global__ __launch_bounds__(256) void lazy_kernel(float* __restrict__ Wk, int64
   };
   auto lstore = [&](int buf) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < AV; ++q) {
       const int e = tid + 256 * q;
       const int m = e >> 3, kk = (e & 7) * 4;
       As[buf][kk + 0][m] = av[q].x;
       As[buf][kk + 1][m] = av[q].y;
       As[buf][kk + 2][m] = av[q].z;
       As[buf][kk + 3][m] = av[q].w;
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = tid + 256 * q;
       const int kb = e >> 5, nn = (e & 31) * 4;
       *reinterpret_cast<float4*>(&Bs[buf][kb][nn]) = bv[q];
     }
   };
 
-  f32x4 cv[4][4];
+  f32x4 cv[MT][4];
   const int nchunks = (K + LK - 1) / LK;
   gload(0);
   lstore(0);
@@ -313,12 +384,12 @@ __global__ __launch_bounds__(256) void lazy_kernel(float* __restrict__ Wk, int64
     if (more) gload((ch + 1) * LK);
     if (ch + 1 == nchunks) {
 #pragma unroll
-      for (int a = 0; a < 4; ++a)
+      for (int a = 0; a < MT; ++a)
 #pragma unroll
         for (int b = 0; b < 4; ++b)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const int64_t r = r0 + 64 * wm + 16 * a + 4 * (lane >> 4) + i;
+            const int64_t r = r0 + 16 * MT * wm + 16 * a + 4 * (lane >> 4) + i;
             const int64_t c = n0 + 64 * wn + 16 * b + (lane & 15);
             cv[a][b][i] = (r < rows && c < c1) ? Wk[r * ldk + c] : 0.f;
           }
@@ -326,13 +397,13 @@ __global__ __launch_bounds__(256) void lazy_kernel(float* __restrict__ Wk, int64
 #pragma unroll
     for (int ks = 0; ks < LK; ks += 4) {
       const int kr = ks + (lane >> 4);
-      float af[4], bf[4];
+      float af[MT], bf[4];
 #pragma unroll
-      for (int a = 0; a < 4; ++a) af[a] = As[buf][kr][64 * wm + 16 * a + (lane & 15)];
+      for (int a = 0; a < MT; ++a) af[a] = As[buf][kr][16 * MT * wm + 16 * a + (lane & 15)];
 #pragma unroll
       for (int b = 0; b < 4; ++b) bf[b] = Bs[buf][kr][64 * wn + 16 * b + (lane & 15)];
 #pragma unroll
-      for (int a = 0; a < 4; ++a)
+      for (int a = 0; a < MT; ++a)
 #pragma unroll
         for (int b = 0; b < 4; ++b)
           acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[a], bf[b], acc[a][b], 0, 0, 0);
@@ -342,12 +413,12 @@ __global__ __launch_bounds__(256) void lazy_kernel(float* __restrict__ Wk, int64
     buf ^= 1;
   }
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+  for (int a = 0; a < MT; ++a)
 #pragma unroll
     for (int b = 0; b < 4; ++b)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int64_t r = r0 + 64 * wm + 16 * a + 4 * (lane >> 4) + i;
+        const int64_t r = r0 + 16 * MT * wm + 16 * a + 4 * (lane >> 4) + i;
         const int64_t c = n0 + 64 * wn + 16 * b + (lane & 15);
         if (r < rows && c < c1) Wk[r * ldk + c] = cv[a][b][i] - acc[a][b][i];
       }
@@ -409,9 +480,17 @@ hipError_t launch_sweep_block(float* Wk, int64_t ldk, int64_t rows, int64_t cols
 hipError_t launch_lazy_update(float* Wk, int64_t ldk, int64_t rows, int64_t cols, int k0, int k1,
                               int c0, int c1, const float* Err, const float* Hinv, hipStream_t s) {
   if (c1 <= c0 || k1 <= k0) return hipSuccess;
-  dim3 grid((unsigned)ceil_div(c1 - c0, LT), (unsigned)ceil_div(rows, LT));
-  hipLaunchKernelGGL(lazy_kernel, grid, dim3(256), 0, s, Wk, ldk, rows, cols, k0, k1, c0, c1, Err,
-                     Hinv);
+  const int64_t ncol = ceil_div(c1 - c0, LT);
+  // big updates: 128x128 tiles; small ones: 32x128 tiles so more CUs take part
+  if (ncol * ceil_div(rows, 128) >= 512) {
+    dim3 grid((unsigned)ncol, (unsigned)ceil_div(rows, 128));
+    hipLaunchKernelGGL(lazy_kernel<4>, grid, dim3(256), 0, s, Wk, ldk, rows, cols, k0, k1, c0, c1,
+                       Err, Hinv);
+  } else {
+    dim3 grid((unsigned)ncol, (unsigned)ceil_div(rows, 32));
+    hipLaunchKernelGGL(lazy_kernel<1>, grid, dim3(256), 0, s, Wk, ldk, rows, cols, k0, k1, c0, c1,
+                       Err, Hinv);
+  }
   return hipGetLastError();
 }
 
