@@ -7,16 +7,24 @@ A step is the whole path on inputs already resident in HBM:
     Hinv = upper Cholesky factor of (H + lambda I)^-1
     codes, scales, zeros, losses = column sweep with lazy block updates
 The printed JSON line reports ms per layer, the roofline of the dominant
-kernel (the fp16 MFMA SYRK) and the fp64 CPU oracle timed on a bounded
-sample on this host.
+kernel (the fp16 MFMA SYRK of the H accumulation) and the fp64 CPU oracle
+timed on a bounded sample on this host.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
+Other workloads: --layer mlp_up | mlp_down | tiny (one layer each), and
+--layer block, the seven layers of a Llama-7B-shaped block (four H's, four
+Hinv preparations, seven quantizations in the order q, k, v, o, gate, up,
+down); a block step is reported as ms per block.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--layer NAME]
+                       [--no-cpu] [--copy-probe-mib M]
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -24,10 +32,14 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
+# MI355X published peaks (dense)
 HBM_PEAK_GBS = 8000.0
 FP16_MFMA_TFLOPS = 2500.0
 FP32_MFMA_TFLOPS = 157.3
 FP64_MFMA_TFLOPS = 78.6
+
+SYRK_SOURCE = os.path.join(ROOT, "post_weight_quantization_02_amd", "csrc", "syrk_f16.hip")
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "hessian_accumulate_attn_traffic.md")
 
 
 def log(*a):
@@ -35,40 +47,179 @@ def log(*a):
 
 
 def algorithmic_work(rows, d, n, B=128):
-    """Flops of the method's own work (one triangle of H; the upper-triangular
-    part of the lazy update), matching the design notes."""
-    syrk = d * (d + 1) * n                       # lower triangle incl. diagonal, 2 flop/FMA
-    prep = 4.0 * d ** 3 / 3.0                    # potrf + trtri + lauum + potrf (d^3/3 each)
+    """Flops of the method's own work: one triangle of H (with diagonal),
+    4d^3/3 for the three factorizations plus the product of the inverse, the
+    upper-triangular part of the lazy update and the in-block rank-1 updates."""
+    syrk = float(d) * (d + 1) * n
+    prep = 4.0 * d ** 3 / 3.0
     nb = (d + B - 1) // B
     lazy = 2.0 * rows * B * sum(d - min((b + 1) * B, d) for b in range(nb))
     sweep = 2.0 * rows * (B * (B + 1) / 2.0) * nb
     return dict(syrk=syrk, prep=prep, lazy=lazy, sweep=sweep)
 
 
-def cpu_baseline(layer, X, W, tok_sample=16384, row_sample=256):
-    """The fp64 oracle on a bounded sample, scaled to one full layer."""
+def source_digest(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def recorded_traffic():
+    """HBM bytes per accumulate call from the committed counter summary, or
+    None when there is none or the SYRK source has changed since it was
+    taken."""
+    try:
+        text = open(TRAFFIC_SUMMARY).read()
+    except OSError:
+        return None
+    m_b = re.search(r"^traffic_bytes_per_call:\s*([0-9.eE+]+)\s*$", text, re.M)
+    m_h = re.search(r"^syrk_source_sha256_16:\s*([0-9a-f]+)\s*$", text, re.M)
+    if not (m_b and m_h) or m_h.group(1) != source_digest(SYRK_SOURCE):
+        return None
+    return float(m_b.group(1))
+
+
+def measured_peaks(torch, dev):
+    """Attainable rates on this GPU from library kernels: hipBLASLt/rocBLAS
+    GEMMs per dtype and a device-to-device copy.  Context for the roofline
+    fractions, which use the published peaks."""
+    out = {}
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / reps
+
+    for name, dt, m in (("f16_gemm_tflops", torch.float16, 8192),
+                        ("f32_gemm_tflops", torch.float32, 8192),
+                        ("f64_gemm_tflops", torch.float64, 4096)):
+        a = torch.randn(m, m, device=dev, dtype=dt)
+        b = torch.randn(m, m, device=dev, dtype=dt)
+        c = torch.empty(m, m, device=dev, dtype=dt)
+        t = timed(lambda: torch.mm(a, b, out=c), 10)
+        out[name] = round(2.0 * m ** 3 / t / 1e12, 1)
+        del a, b, c
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    t = timed(lambda: dst.copy_(src), 10)
+    out["copy_gbs"] = round(2.0 * src.numel() / t / 1e9, 1)
+    del src, dst
+    torch.cuda.empty_cache()
+    return out
+
+
+def cpu_baseline(layer, X, W, budget_s=8.0):
+    """The fp64 oracle, as it is, on a bounded sample of the same layer,
+    scaled to one full layer: H on as many 8192-token chunks as fit in about
+    budget_s seconds, the full Hinv preparation, and the sweep on a doubling
+    number of rows until a call takes about budget_s seconds."""
     import numpy as np
 
     import oracle
     d, rows, n = layer.x.d, layer.w.rows, layer.x.n
     cores = len(os.sched_getaffinity(0))
+    # H
     t0 = time.perf_counter()
-    Hs = oracle.hessian((X[t:t + 8192] for t in range(0, tok_sample, 8192)), d)
+    Hs = np.zeros((d, d))
+    toks = 0
+    while toks < n:
+        t1 = min(toks + 8192, n)
+        Hs += oracle.hessian([X[toks:t1]], d)
+        toks = t1
+        if time.perf_counter() - t0 >= budget_s:
+            break
     t_h = time.perf_counter() - t0
-    Hfull = Hs * (n / tok_sample)  # a stand-in H of the right scale for the timing of prep/sweep
+    Hfull = Hs * (n / toks)  # an H of the full layer's scale for timing prep and sweep
+    # prep
     t0 = time.perf_counter()
     U, _ = oracle.hinv_upper(Hfull, layer.percdamp)
     t_p = time.perf_counter() - t0
-    t0 = time.perf_counter()
-    oracle.gptq(W[:row_sample], U, layer.bits, layer.groupsize, layer.blocksize, precision="f32")
-    t_s = time.perf_counter() - t0
-    est = t_h * (n / tok_sample) + t_p + t_s * (rows / row_sample)
+    # sweep
+    r = min(16, rows)
+    while True:
+        t0 = time.perf_counter()
+        oracle.gptq(W[:r], U, layer.bits, layer.groupsize, layer.blocksize, precision="f32")
+        t_s = time.perf_counter() - t0
+        if t_s >= budget_s or r >= rows:
+            break
+        r = min(rows, 2 * r)
+    est = t_h * (n / toks) + t_p + t_s * (rows / r)
     return {
         "value": round(est * 1e3, 1), "unit": "ms", "cores": cores, "kind": "oracle",
-        "sample": (f"H on {tok_sample} of {n} tokens (x{n // tok_sample}), full Hinv prep at "
-                   f"d={d}, sweep on {row_sample} of {rows} rows (x{rows // row_sample}); "
-                   f"phases s: H {t_h:.2f}, prep {t_p:.2f}, sweep {t_s:.2f}"),
+        "sample": (f"H on {toks} of {n} tokens (x{n / toks:.1f}), full Hinv prep at d={d}, "
+                   f"sweep on {r} of {rows} rows (x{rows / r:.1f}); measured s: H {t_h:.2f}, "
+                   f"prep {t_p:.2f}, sweep {t_s:.2f}"),
     }
+
+
+class Job:
+    """Device buffers and the per-step call sequence of one workload.
+
+    ``hs``: list of (XSpec, layers sharing its H); every layer of a group
+    shares one Hinv.  One workspace of the largest size serves every call.
+    """
+
+    def __init__(self, torch, gq, synth, groups, dev):
+        self.torch, self.gq = torch, gq
+        self.groups = []
+        ws_bytes = 0
+        threads = min(16, len(os.sched_getaffinity(0)))
+        for xs, layers in groups:
+            log(f"generating X {xs.n}x{xs.d} fp16")
+            X = synth.activations(xs, threads=threads)
+            Xd = torch.from_numpy(X).to(dev)
+            H = torch.empty((xs.d, xs.d), dtype=torch.float32, device=dev)
+            U = torch.empty((xs.d, xs.d), dtype=torch.float32, device=dev)
+            ls = []
+            for L in layers:
+                W = synth.weights(L.w)
+                ng = (L.w.cols + L.groupsize - 1) // L.groupsize
+                outs = (torch.empty((L.w.rows, L.w.cols), dtype=torch.uint8, device=dev),
+                        torch.empty((L.w.rows, ng), dtype=torch.float32, device=dev),
+                        torch.empty((L.w.rows, ng), dtype=torch.float32, device=dev),
+                        torch.empty((L.w.cols,), dtype=torch.float32, device=dev))
+                ls.append((L, W, torch.from_numpy(W).to(dev), outs))
+                ws_bytes = max(ws_bytes, gq.workspace_bytes(gq.OP_QUANTIZE, L.w.rows, xs.d, 0))
+            ws_bytes = max(ws_bytes, gq.workspace_bytes(gq.OP_ACCUMULATE, 0, xs.d, xs.n),
+                           gq.workspace_bytes(gq.OP_PREPARE, 0, xs.d, 0))
+            self.groups.append((xs, X, Xd, H, U, ls))
+        raw = torch.empty(ws_bytes + 256, dtype=torch.uint8, device=dev)
+        off = (-raw.data_ptr()) % 256
+        self.ws = raw[off:off + ws_bytes]
+        self.stream = torch.cuda.current_stream(dev)
+        self.ev = {k: [] for k in ("acc", "prep", "quant")}
+
+    def step(self, record):
+        torch, gq = self.torch, self.gq
+        for xs, X, Xd, H, U, ls in self.groups:
+            H.zero_()
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(3)] if record else None
+            if record:
+                e[0].record(self.stream)
+            gq.hessian_accumulate(H, Xd, 2.0, workspace=self.ws)
+            if record:
+                e[1].record(self.stream)
+            gq.prepare_hinv(H, ls[0][0].percdamp, out=U, workspace=self.ws)
+            if record:
+                e[2].record(self.stream)
+                self.ev["acc"].append((e[0], e[1]))
+                self.ev["prep"].append((e[1], e[2]))
+            for L, W, Wd, outs in ls:
+                if record:
+                    q0 = torch.cuda.Event(enable_timing=True)
+                    q1 = torch.cuda.Event(enable_timing=True)
+                    q0.record(self.stream)
+                gq.quantize_layer(Wd, U, L.bits, L.groupsize, L.blocksize, out=outs,
+                                  workspace=self.ws)
+                if record:
+                    q1.record(self.stream)
+                    self.ev["quant"].append((q0, q1))
 
 
 def main():
@@ -76,12 +227,16 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=1)
-    ap.add_argument("--layer", default="attn")
-    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--layer", default="attn",
+                    choices=["attn", "mlp_up", "mlp_down", "tiny", "block"])
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
+    ap.add_argument("--no-peaks", action="store_true", help="skip the library peak probes")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="run one device copy of this size first (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the multi-GPU "
-              "sharding of this path is a design note, not a measured run.", file=sys.stderr)
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); how this path "
+              "shards over several GPUs is a design note, not a measured run.", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
@@ -90,84 +245,95 @@ def main():
     import post_weight_quantization_02_amd as gq
     import synth
 
-    layer = synth.LAYERS[args.layer]
-    d, rows, n = layer.x.d, layer.w.rows, layer.x.n
     dev = torch.device("cuda:0")
-    log(f"generating inputs: W {rows}x{d}, X {n}x{d} fp16")
-    t0 = time.time()
-    X = synth.activations(layer.x, threads=min(16, len(os.sched_getaffinity(0))))
-    W = synth.weights(layer.w)
-    log(f"  done in {time.time() - t0:.1f}s; uploading")
-    Xd = torch.from_numpy(X).to(dev)
-    Wd = torch.from_numpy(W).to(dev)
-    H = torch.empty((d, d), dtype=torch.float32, device=dev)
-    U = torch.empty((d, d), dtype=torch.float32, device=dev)
-    ng = (d + layer.groupsize - 1) // layer.groupsize
-    outs = (torch.empty((rows, d), dtype=torch.uint8, device=dev),
-            torch.empty((rows, ng), dtype=torch.float32, device=dev),
-            torch.empty((rows, ng), dtype=torch.float32, device=dev),
-            torch.empty((d,), dtype=torch.float32, device=dev))
-    ws_bytes = max(gq.workspace_bytes(gq.OP_ACCUMULATE, 0, d, n),
-                   gq.workspace_bytes(gq.OP_PREPARE, 0, d, 0),
-                   gq.workspace_bytes(gq.OP_QUANTIZE, rows, d, 0))
-    ws_raw = torch.empty(ws_bytes + 256, dtype=torch.uint8, device=dev)
-    off = (-ws_raw.data_ptr()) % 256
-    ws = ws_raw[off:off + ws_bytes]
-    stream = torch.cuda.current_stream(dev)
+    if args.copy_probe_mib:
+        nb = args.copy_probe_mib << 20
+        src = torch.ones(nb // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy probe: {nb} bytes read, {nb} bytes written")
+        del src, dst
 
-    ev = {k: [] for k in ("acc", "prep", "quant")}
+    if args.layer == "block":
+        groups = []
+        for L in synth.BLOCK:
+            if groups and groups[-1][0] == L.x:
+                groups[-1][1].append(L)
+            else:
+                groups.append((L.x, [L]))
+        layers = synth.BLOCK
+        workload = ("Llama-7B-shaped block: q,k,v,o 4096x4096, gate,up 11008x4096, down "
+                    "4096x11008 fp16; 4 H's (attn-in, o-in, mlp-in 262144x4096, down-in "
+                    "262144x11008 fp16, 128x2048 tokens each); int4 g128 B128 percdamp 0.01; "
+                    "layers in order q,k,v,o,gate,up,down")
+        metric = "ms per Llama-7B-shaped block (7 layers, 4 H's incl. accumulate)"
+    else:
+        L = synth.LAYERS[args.layer]
+        groups = [(L.x, [L])]
+        layers = [L]
+        rows, d, n = L.w.rows, L.x.d, L.x.n
+        extra = ""
+        if L.x.zero_frac:
+            extra = f", {int(L.x.zero_frac * 100)}% zeros, {L.x.dead} dead channels"
+        workload = (f"{L.name}: W {rows}x{d} {L.w.dtype}, X {n}x{d} fp16{extra}, "
+                    f"int{L.bits} g{L.groupsize} B{L.blocksize} percdamp {L.percdamp}")
+        metric = "ms per 4096x4096 int4 g128 GPTQ layer (incl. H accumulate); % MFMA roofline"
+        if args.layer != "attn":
+            metric = f"ms per {rows}x{d} int{L.bits} g{L.groupsize} GPTQ layer (incl. H accumulate)"
 
-    def step(record):
-        H.zero_()
-        if record:
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e2 = torch.cuda.Event(enable_timing=True)
-            e3 = torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-        gq.hessian_accumulate(H, Xd, 2.0, workspace=ws)
-        if record:
-            e1.record(stream)
-        gq.prepare_hinv(H, layer.percdamp, out=U, workspace=ws)
-        if record:
-            e2.record(stream)
-        gq.quantize_layer(Wd, U, layer.bits, layer.groupsize, layer.blocksize, out=outs,
-                          workspace=ws)
-        if record:
-            e3.record(stream)
-            ev["acc"].append((e0, e1))
-            ev["prep"].append((e1, e2))
-            ev["quant"].append((e2, e3))
+    peaks = None if args.no_peaks else measured_peaks(torch, dev)
+    if peaks:
+        log("measured peaks:", peaks)
 
+    job = Job(torch, gq, synth, groups, dev)
     log(f"warmup {args.warmup}")
     for _ in range(args.warmup):
-        step(False)
+        job.step(False)
     torch.cuda.synchronize()
     log(f"timing {args.steps} steps")
-    torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        step(True)
+        job.step(True)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = wall * 1e3 / args.steps
-    ph = {k: float(np.mean([a.elapsed_time(b) for a, b in v])) for k, v in ev.items()}
-    log("phase ms:", {k: round(v, 3) for k, v in ph.items()})
+    per = {k: [a.elapsed_time(b) for a, b in v] for k, v in job.ev.items()}
+    ph = {k: float(np.sum(v)) / args.steps for k, v in per.items()}  # ms per step per phase
+    log("phase ms per step:", {k: round(v, 3) for k, v in ph.items()})
 
-    work = algorithmic_work(rows, d, n, layer.blocksize)
-    syrk_tflops = work["syrk"] / (ph["acc"] * 1e-3) / 1e12
-    floor_ms = (work["syrk"] / FP16_MFMA_TFLOPS + (work["prep"]) / FP64_MFMA_TFLOPS
-                + work["lazy"] / FP32_MFMA_TFLOPS) / 1e9
-    eff_tflops = (work["syrk"] + work["prep"] + work["lazy"] + work["sweep"]) / (ms_step * 1e-3) / 1e12
+    # algorithmic work per step
+    work = dict(syrk=0.0, prep=0.0, lazy=0.0, sweep=0.0)
+    for xs, X, Xd, H, U, ls in job.groups:
+        w0 = algorithmic_work(0, xs.d, xs.n)
+        work["syrk"] += w0["syrk"]
+        work["prep"] += w0["prep"]
+        for Lq, *_ in ls:
+            w1 = algorithmic_work(Lq.w.rows, xs.d, 0, Lq.blocksize)
+            work["lazy"] += w1["lazy"]
+            work["sweep"] += w1["sweep"]
+    floor = {"acc": work["syrk"] / FP16_MFMA_TFLOPS / 1e9,
+             "prep": work["prep"] / FP64_MFMA_TFLOPS / 1e9,
+             "quant": work["lazy"] / FP32_MFMA_TFLOPS / 1e9}
+    floor_ms = sum(floor.values())
+    eff_tflops = sum(work.values()) / (ms_step * 1e-3) / 1e12
+
+    # dominant kernel: the SYRK of the H accumulation (one call per H)
+    acc_calls = per["acc"]
+    acc_ms = float(np.mean(acc_calls))
+    syrk_flops_call = work["syrk"] / len(job.groups)
+    syrk_tflops = syrk_flops_call / (acc_ms * 1e-3) / 1e12
+    traffic = recorded_traffic() if args.layer == "attn" else None
 
     cpu = None
-    if not args.no_cpu:
+    if not args.no_cpu and args.layer != "block":
         log("cpu baseline (oracle on a bounded sample)")
-        cpu = cpu_baseline(layer, X, W)
+        xs, X, *_ = job.groups[0]
+        cpu = cpu_baseline(layers[0], X, job.groups[0][5][0][1])
         log("  ", cpu)
 
     line = {
-        "metric": "ms per 4096x4096 int4 g128 GPTQ layer (incl. H accumulate); % MFMA roofline",
+        "metric": metric,
         "value": round(ms_step, 4),
         "unit": "ms",
         "n_gpus": 1,
@@ -179,17 +345,21 @@ def main():
         "vs_baseline": None,
         "dtype": "f16-in/f32-acc SYRK, f64 Hinv, f32 sweep",
         "data": "synthetic (seeded low-rank-plus-noise activations, Gaussian weights)",
-        "config": {"workload": f"{layer.name}: W {rows}x{d} fp16, X {n}x{d} fp16 (128x2048 "
-                               f"tokens), int{layer.bits} g{layer.groupsize} B{layer.blocksize} "
-                               f"percdamp {layer.percdamp}",
+        "config": {"workload": workload,
                    "phase_ms": {k: round(v, 4) for k, v in ph.items()},
+                   "phase_floor_ms": {k: round(v, 4) for k, v in floor.items()},
+                   "phase_frac_of_floor": {k: round(floor[k] / ph[k], 4) for k in floor},
                    "effective_tflops": round(eff_tflops, 2),
                    "roofline_floor_ms": round(floor_ms, 3),
-                   "frac_of_floor": round(floor_ms / ms_step, 4)},
-        "roofline": {"bound": "mfma", "kernel": "hessian accumulate (fp16 MFMA SYRK + split reduce)",
+                   "frac_of_floor": round(floor_ms / ms_step, 4),
+                   "peaks_measured": peaks},
+        "roofline": {"bound": "mfma",
+                     "kernel": "hessian accumulate call: syrk_fast_kernel + syrk_reduce_kernel",
                      "achieved": round(syrk_tflops, 2), "peak": FP16_MFMA_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(syrk_tflops / FP16_MFMA_TFLOPS, 4),
-                     "traffic": None},
+                     "traffic": traffic,
+                     "per_launch_ms": round(acc_ms, 4),
+                     "flops_per_launch": syrk_flops_call},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
