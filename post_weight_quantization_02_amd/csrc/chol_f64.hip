@@ -26,6 +26,8 @@
 //     1-based index; the host reads it once at the end.
 #include <limits.h>
 
+#include <utility>
+
 #include "common.h"
 
 namespace gptq {
@@ -87,108 +89,218 @@ __global__ __launch_bounds__(256) void damp_copy_kernel(const float* __restrict_
   A[e] = v;
 }
 
+// Row of the 16x16 fp64 MFMA result held in element i of lane `lane`
+// (the fp64 variant interleaves rows: lane/16, lane/16 + 4, ...).
+__device__ inline int mfma64_row(int lane, int i) { return (lane >> 4) + 4 * i; }
+
 // -------------------------------------------------------------- panel
-// One workgroup factors the 64x64 diagonal block of the panel at column k and
-// inverts the factor: A_kk = L L^T, X = L^-1.  L overwrites the lower triangle
-// of A_kk, X (with zeros above its diagonal) goes to Xd (leading dim ldxd).
+// Value of v held by lane J of this lane's row of 16 (DPP row_newbcast; one
+// v_mov_b64_dpp; with every row and bank enabled the old value is unused).
+template <int J>
+__device__ inline double row_bcast(double v) {
+  return __builtin_amdgcn_update_dpp(0.0, v, 0x150 + J, 0xF, 0xF, true);
+}
+
+// Step J of the in-wave 16x16 Cholesky and inverse (see factor16).
+template <int J>
+__device__ inline void factor16_step(double (&a)[16], double (&y)[16], double& ysc, int i,
+                                     int* flag, int info_base, bool report) {
+  const double p = row_bcast<J>(a[J]);
+  if (report && (threadIdx.x & 63) == 0 && !(p > 0.0)) atomicMin(flag, info_base + J + 1);
+  const double rs = rsqrt_f64(p);
+  const double cij = a[J];
+  const double t = (i > J) ? cij * (rs * rs) : 0.0;
+#pragma unroll
+  for (int l = J + 1; l < 16; ++l) a[l] = __builtin_fma(-t, row_bcast<J>(a[l]), a[l]);
+  const double lij = cij * rs;
+  const double coef = (i > J) ? -lij * rs : 0.0;
+#pragma unroll
+  for (int l = 0; l <= J; ++l) y[l] = __builtin_fma(coef, row_bcast<J>(y[l]), y[l]);
+  if (i == J) ysc = rs;
+  a[J] = (i > J) ? lij : ((i == J) ? p * rs : 0.0);
+  __builtin_amdgcn_sched_barrier(0);  // keep steps apart: bounded register pressure
+}
+
+template <int... J>
+__device__ inline void factor16_steps(double (&a)[16], double (&y)[16], double& ysc, int i,
+                                      int* flag, int info_base, bool report,
+                                      std::integer_sequence<int, J...>) {
+  (factor16_step<J>(a, y, ysc, i, flag, info_base, report), ...);
+}
+
+// Cholesky factor and inverse of one symmetric 16x16 block held by a single
+// wave, with no barrier: lane i (and its copies i+16, i+32, i+48, one per row
+// of 16 lanes) keeps row i of the block in a[] and row i of Y in y[] (Y
+// starts as I).  Step j takes the pivot and row j from lane j of the row
+// (DPP broadcast), applies the unscaled right-looking update
+// a[i][l] -= (a[i][j] / p) a[j][l], and the forward substitution of L Y = I:
+// Y[i][:] -= L[i][j] X[j][:] below row j, with X[j][:] = Y[j][:] / L[j][j]
+// (row j itself is scaled once at the end).  On return a[] holds row i of L
+// and y[] row i of L^-1 (zeros above the diagonal in both).  Pivots that are
+// not > 0 (or NaN) are reported through atomicMin(flag, info_base + j + 1)
+// by lane 0 when `report` is set.
+__device__ __attribute__((always_inline)) inline void factor16(double (&a)[16], double (&y)[16], int i, int* flag, int info_base,
+                                bool report) {
+#pragma unroll
+  for (int l = 0; l < 16; ++l) y[l] = (l == i) ? 1.0 : 0.0;
+  double ysc = 1.0;
+  factor16_steps(a, y, ysc, i, flag, info_base, report, std::make_integer_sequence<int, 16>{});
+#pragma unroll
+  for (int l = 0; l < 16; ++l) y[l] *= ysc;
+}
+
+// LDS of the diagonal-block factorization; the trailing update reuses S and
+// Xs as its two panel tiles.
+struct DiagLds {
+  double S[NB][PP];      // A, then L (lower triangle)
+  double Xs[NB][PP];     // L^-1 (lower triangle)
+  double Wx[4][16][17];  // per-wave copy of X_JJ for the MFMA operand
+};
+
+// Factor the 64x64 block in sh.S (lower triangle; rows past the matrix are
+// identity) and invert the factor: L goes to the lower triangle of the block
+// at A[k.., k..], L^-1 (zeros above its diagonal) to Xd.  sh.Xs must be zero
+// and a barrier must separate its clearing and the filling of sh.S from the
+// call.
 //
-// Thread (tx, ty) = (t % 16, t / 16) keeps the 16 elements of rows
-// ty + 16a, columns tx + 16b (a, b < 4) of two matrices in registers: the
-// Schur complement `a` (right-looking, unscaled: a[i][l] -= a[i][j] a[l][j] /
-// a[j][j]) and Y, the forward substitution L Y = I run row by row.  Step j of
-// both recurrences needs only column j of L and row j of Y, which are final
-// when step j starts, so one loop of 64 steps does both: the owners publish
-// that column and that row through LDS, one barrier, then every thread
-// applies the two rank-1 updates to its registers.
+// The block is split into 4x4 sub-blocks of 16.  For each block column J:
+// every wave factors and inverts the 16x16 diagonal sub-block on its own
+// (factor16, no barrier), wave I > J forms L_IJ = A_IJ X_JJ^T, and after one
+// barrier applies A_IK -= L_IJ L_KJ^T for J < K <= I; all 16x16 products are
+// v_mfma_f64_16x16x4f64.  Finally wave J forms the inverse blocks of column
+// J, X_IJ = -X_II sum_{K=J..I-1} L_IK X_KJ.
+__device__ __attribute__((always_inline)) inline void diag_factor(DiagLds& sh, double* __restrict__ A, int lda, int k, int kb,
+                                   int* flag, int info_offset, double* __restrict__ Xd,
+                                   int ldxd) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int m = lane & 15, kq = lane >> 4;
+  double (*S)[PP] = sh.S;
+  double (*Xs)[PP] = sh.Xs;
+
+#pragma unroll 1
+  for (int J = 0; J < 4; ++J) {
+    const int r0 = 16 * J;
+    double a[16], y[16];
+#pragma unroll
+    for (int l = 0; l < 16; ++l) a[l] = (l <= m) ? S[r0 + m][r0 + l] : S[r0 + l][r0 + m];
+    factor16(a, y, m, flag, info_offset + k + r0, wave == 0);
+    if (lane < 16) {
+#pragma unroll
+      for (int l = 0; l < 16; ++l) sh.Wx[wave][m][l] = y[l];
+      if (wave == J) {
+#pragma unroll
+        for (int l = 0; l < 16; ++l) {
+          S[r0 + m][r0 + l] = a[l];
+          Xs[r0 + m][r0 + l] = y[l];
+        }
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (wave > J) {
+      // L_IJ = A_IJ X_JJ^T, I = wave
+      f64x4 acc = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) {
+        const int kk = 4 * s4 + kq;
+        acc = __builtin_amdgcn_mfma_f64_16x16x4f64(S[16 * wave + m][r0 + kk], sh.Wx[wave][m][kk],
+                                                   acc, 0, 0, 0);
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) S[16 * wave + mfma64_row(lane, q)][r0 + m] = acc[q];
+    }
+    __syncthreads();
+    if (wave > J) {
+      // A_IK -= L_IJ L_KJ^T for J < K <= I
+#pragma unroll 1
+      for (int K = J + 1; K <= wave; ++K) {
+        f64x4 acc;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[q] = S[16 * wave + mfma64_row(lane, q)][16 * K + m];
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4) {
+          const int kk = 4 * s4 + kq;
+          acc = __builtin_amdgcn_mfma_f64_16x16x4f64(-S[16 * wave + m][r0 + kk],
+                                                     S[16 * K + m][r0 + kk], acc, 0, 0, 0);
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) S[16 * wave + mfma64_row(lane, q)][16 * K + m] = acc[q];
+      }
+    }
+    __syncthreads();
+  }
+
+  // off-diagonal blocks of L^-1: wave J owns block column J
+  if (wave < 3) {
+    const int J = wave;
+#pragma unroll 1
+    for (int I = J + 1; I < 4; ++I) {
+      f64x4 t = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll 1
+      for (int K = J; K < I; ++K) {
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4) {
+          const int kk = 4 * s4 + kq;
+          t = __builtin_amdgcn_mfma_f64_16x16x4f64(S[16 * I + m][16 * K + kk],
+                                                   Xs[16 * K + kk][16 * J + m], t, 0, 0, 0);
+        }
+      }
+      // X_IJ = -X_II T; the D layout of T (rows kq + 4q) is the B layout of step q
+      f64x4 x = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) {
+        const int kk = 4 * s4 + kq;
+        x = __builtin_amdgcn_mfma_f64_16x16x4f64(-Xs[16 * I + m][16 * I + kk], t[s4], x, 0, 0, 0);
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) Xs[16 * I + mfma64_row(lane, q)][16 * J + m] = x[q];
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+  }
+  __syncthreads();
+
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    const int e = tid + 256 * q;
+    const int i = e >> 6, l = e & 63;
+    if (i < kb && l < kb) {
+      if (l <= i) A[(int64_t)(k + i) * lda + k + l] = S[i][l];
+      Xd[(int64_t)i * ldxd + l] = (l <= i) ? Xs[i][l] : 0.0;
+    }
+  }
+}
+
+// One workgroup factors the 64x64 diagonal block of the panel at column k and
+// inverts the factor (diag_factor); the block is read from the lower
+// triangle of A.  Used for the first panel; later diagonal blocks are
+// factored inside the previous panel's trailing update.
 __global__ __launch_bounds__(256) void potrf_diag_kernel(double* __restrict__ A, int lda, int d,
                                                          int k, int* flag, int info_offset,
                                                          double* __restrict__ Xd, int ldxd) {
-  __shared__ double colb[2][NB];
-  __shared__ double rowb[2][NB];
-  __shared__ double rsq[NB];
+  __shared__ DiagLds sh;
   const int tid = threadIdx.x;
-  const int tx = tid & 15, ty = tid >> 4;
   const int kb = min(NB, d - k);
-  double a[4][4], y[4][4];
+  double v[16];
 #pragma unroll
-  for (int ai = 0; ai < 4; ++ai)
-#pragma unroll
-    for (int bj = 0; bj < 4; ++bj) {
-      const int i = ty + 16 * ai, l = tx + 16 * bj;
-      const int r = i >= l ? i : l, c = i >= l ? l : i;
-      double v = (i == l) ? 1.0 : 0.0;
-      if (r < kb) v = A[(int64_t)(k + r) * lda + k + c];
-      a[ai][bj] = v;
-      y[ai][bj] = (i == l) ? 1.0 : 0.0;
-    }
-
-#pragma unroll
-  for (int bb = 0; bb < 4; ++bb) {
-#pragma unroll 1
-    for (int jj = 0; jj < 16; ++jj) {
-      const int j = 16 * bb + jj;
-      double* cb = colb[j & 1];
-      double* rb = rowb[j & 1];
-      if (tx == jj) {
-#pragma unroll
-        for (int ai = 0; ai < 4; ++ai) cb[ty + 16 * ai] = a[ai][bb];
-      }
-      if (ty == jj) {
-#pragma unroll
-        for (int bj = 0; bj < 4; ++bj) rb[tx + 16 * bj] = y[bb][bj];
-      }
-      __syncthreads();
-      const double p = cb[j];
-      const double inv = recip_f64(p);
-      const double rs = rsqrt_f64(p);  // 1 / L[j][j]
-      if (tid == 0) rsq[j] = rs;
-      double ci[4], cl[4], li[4], xr[4];
-#pragma unroll
-      for (int ai = 0; ai < 4; ++ai) {
-        const int i = ty + 16 * ai;
-        const double c = cb[i];
-        ci[ai] = (i > j) ? c * inv : 0.0;
-        li[ai] = (i > j) ? c * rs : 0.0;  // L[i][j]
-      }
-#pragma unroll
-      for (int bj = 0; bj < 4; ++bj) {
-        const int l = tx + 16 * bj;
-        cl[bj] = (l > j) ? cb[l] : 0.0;
-        xr[bj] = rb[l] * rs;              // X[j][l]
-      }
-#pragma unroll
-      for (int ai = 0; ai < 4; ++ai)
-#pragma unroll
-        for (int bj = 0; bj < 4; ++bj) {
-          a[ai][bj] -= ci[ai] * cl[bj];
-          y[ai][bj] -= li[ai] * xr[bj];
-        }
-      if (ty == jj) {
-#pragma unroll
-        for (int bj = 0; bj < 4; ++bj) y[bb][bj] = xr[bj];
-      }
-    }
+  for (int q = 0; q < 16; ++q) {
+    const int e = tid + 256 * q;
+    const int i = e >> 6, l = e & 63;
+    double x = (i == l) ? 1.0 : 0.0;
+    if (i < kb && l <= i) x = A[(int64_t)(k + i) * lda + k + l];
+    v[q] = x;
   }
-  // pivots are the final diagonal entries of the Schur complement
 #pragma unroll
-  for (int ai = 0; ai < 4; ++ai)
-#pragma unroll
-    for (int bj = 0; bj < 4; ++bj)
-      if (ty + 16 * ai == tx + 16 * bj) {
-        const int j = ty + 16 * ai;
-        if (j < kb && !(a[ai][bj] > 0.0)) atomicMin(flag, info_offset + k + j + 1);
-      }
+  for (int q = 0; q < 16; ++q) {
+    const int e = tid + 256 * q;
+    sh.S[e >> 6][e & 63] = v[q];
+    sh.Xs[e >> 6][e & 63] = 0.0;
+  }
   __syncthreads();
-#pragma unroll
-  for (int ai = 0; ai < 4; ++ai)
-#pragma unroll
-    for (int bj = 0; bj < 4; ++bj) {
-      const int i = ty + 16 * ai, l = tx + 16 * bj;
-      if (i < kb && l < kb) {
-        if (l <= i) A[(int64_t)(k + i) * lda + k + l] = a[ai][bj] * rsq[l];
-        Xd[(int64_t)i * ldxd + l] = (l <= i) ? y[ai][bj] : 0.0;
-      }
-    }
+  diag_factor(sh, A, lda, k, kb, flag, info_offset, Xd, ldxd);
 }
 
 // 64x64x64 fp64 MFMA product on LDS tiles: acc += P (64 x K) * Q^T, with
@@ -211,9 +323,6 @@ __device__ inline void mma64_f64(const double (*P)[PP], const double (*Q)[PP], i
   }
 }
 
-// Row of the 16x16 fp64 MFMA result held in element i of lane `lane`
-// (the fp64 variant interleaves rows: lane/16, lane/16 + 4, ...).
-__device__ inline int mfma64_row(int lane, int i) { return (lane >> 4) + 4 * i; }
 
 // L_ik = A_ik X_kk^T for the 64-row blocks below the diagonal block
 // (one workgroup per block; X_kk = L_kk^-1 from the diagonal kernel).
@@ -260,12 +369,19 @@ __global__ __launch_bounds__(256) void potrf_trsm_kernel(double* __restrict__ A,
       }
 }
 
-// Trailing update of the lower triangle: A_ij -= L_ik L_jk^T for all 64x64
-// tiles i >= j of A[t0:, t0:], t0 = k + 64; both panel blocks sit in LDS.
-__global__ __launch_bounds__(256) void potrf_update_kernel(double* __restrict__ A, int lda, int d,
-                                                           int k) {
-  __shared__ double Ps[NB][PP];
-  __shared__ double Qs[NB][PP];
+// Trailing update of the lower triangle after panel k: A_ij -= L_ik L_jk^T
+// for all 64x64 tiles i >= j of A[t0:, t0:], t0 = k + 64, both panel blocks
+// in LDS.  Workgroup 0 takes tile (0, 0), the next panel's diagonal block,
+// keeps the updated block in LDS and goes on to factor and invert it
+// (diag_factor): the next panel's serial step runs while the other
+// workgroups are still updating, instead of after them (lookahead of one
+// panel).
+__global__ __launch_bounds__(256, 2) void potrf_update_kernel(double* __restrict__ A, int lda, int d,
+                                                           int k, int* flag, int info_offset,
+                                                           double* __restrict__ Xn, int ldxn) {
+  __shared__ DiagLds sh;
+  double (*Ps)[PP] = sh.S;
+  double (*Qs)[PP] = sh.Xs;
   int ti, tj;
   lower_tile(blockIdx.x, ti, tj);
   const int t0 = k + NB;
@@ -274,6 +390,7 @@ __global__ __launch_bounds__(256) void potrf_update_kernel(double* __restrict__ 
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const bool diag = (ti == tj);
+  const bool lookahead = (blockIdx.x == 0);
   const int j = tid & 63, i0 = tid >> 6;
   double pv[16], qv[16];
 #pragma unroll
@@ -306,16 +423,40 @@ __global__ __launch_bounds__(256) void potrf_update_kernel(double* __restrict__ 
 #pragma unroll
     for (int b = 0; b < 2; ++b) acc[a][b] = f64x4{0.0, 0.0, 0.0, 0.0};
   mma64_f64(Ps, diag ? Ps : Qs, NB, acc, lane, wm, wn);
+  if (!lookahead) {
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = r0 + 32 * wm + 16 * a + mfma64_row(lane, i);
+          const int c = c0 + 32 * wn + 16 * b + (lane & 15);
+          if (r < d && c < d) A[(int64_t)r * lda + c] = cv[a][b][i] - acc[a][b][i];
+        }
+    return;
+  }
+  // workgroup 0: the updated diagonal block of the next panel goes to sh.S
+  // (rows past the matrix become identity), then it is factored in place
+  const int kb = min(NB, d - t0);
+  __syncthreads();  // every wave is done reading the panel tiles
 #pragma unroll
   for (int a = 0; a < 2; ++a)
 #pragma unroll
     for (int b = 0; b < 2; ++b)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int r = r0 + 32 * wm + 16 * a + mfma64_row(lane, i);
-        const int c = c0 + 32 * wn + 16 * b + (lane & 15);
-        if (r < d && c < d) A[(int64_t)r * lda + c] = cv[a][b][i] - acc[a][b][i];
+        const int r = 32 * wm + 16 * a + mfma64_row(lane, i);
+        const int c = 32 * wn + 16 * b + (lane & 15);
+        sh.S[r][c] = (r < kb && c < kb) ? cv[a][b][i] - acc[a][b][i] : ((r == c) ? 1.0 : 0.0);
       }
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    const int e = tid + 256 * q;
+    sh.Xs[e >> 6][e & 63] = 0.0;
+  }
+  __syncthreads();
+  diag_factor(sh, A, lda, t0, kb, flag, info_offset, Xn, ldxn);
 }
 
 // -------------------------------------------------------------- MFMA GEMM
@@ -446,38 +587,6 @@ hipError_t gemm64(const GemmDesc& g, int batches, hipStream_t s) {
   return hipGetLastError();
 }
 
-// -------------------------------------------------------------- trtri diag
-// X_bb = inverse of the lower-triangular 64x64 diagonal block L_bb.
-__global__ __launch_bounds__(256) void trtri_diag_kernel(const double* __restrict__ L, int ldl,
-                                                         double* __restrict__ X, int ldx, int d) {
-  __shared__ double Ls[NB][NB + 1];
-  __shared__ double Xs[NB][NB + 1];
-  const int b0 = blockIdx.x * NB;
-  const int nb = min(NB, d - b0);
-  const int tid = threadIdx.x;
-  const int tx = tid & 15, ty = tid >> 4;
-  for (int e = tid; e < NB * NB; e += 256) {
-    const int i = e / NB, j = e % NB;
-    double v = (i == j) ? 1.0 : 0.0;
-    if (i < nb && j <= i) v = L[(int64_t)(b0 + i) * ldl + b0 + j];
-    Ls[i][j] = v;
-    Xs[i][j] = (i == j) ? 1.0 : 0.0;  // right-hand side I, overwritten by X
-  }
-  __syncthreads();
-  // rows top-down: x_m = xs_m / L_mm is final at step m; then xs_i -= L_im x_m for i > m
-  for (int m = 0; m < nb; ++m) {
-    const double inv = 1.0 / Ls[m][m];
-    for (int i = m + 1 + ty; i < nb; i += 16) {
-      const double lim = Ls[i][m] * inv;
-      for (int j = tx; j <= m; j += 16) Xs[i][j] -= lim * Xs[m][j];
-    }
-    __syncthreads();
-  }
-  for (int e = tid; e < NB * NB; e += 256) {
-    const int i = e / NB, j = e % NB;
-    if (i < nb && j < nb) X[(int64_t)(b0 + i) * ldx + b0 + j] = (j <= i) ? Xs[i][j] / Ls[i][i] : 0.0;
-  }
-}
 
 // -------------------------------------------------------------- fp32 output
 // Hinv[i][j] = L2[j][i] for j >= i, 0 below the diagonal.
@@ -517,33 +626,30 @@ hipError_t launch_damp_to_f64(const float* H, int d, double percdamp, double* A,
   return hipGetLastError();
 }
 
-hipError_t launch_potrf_panel(double* A, int lda, int d, int k, int* flag, int info_offset,
-                              double* Xi, int ldxi, hipStream_t s) {
+hipError_t launch_potrf_diag(double* A, int lda, int d, int k, int* flag, int info_offset,
+                             double* Xi, int ldxi, hipStream_t s) {
   double* Xd = Xi + (int64_t)k * ldxi + k;
   hipLaunchKernelGGL(potrf_diag_kernel, dim3(1), dim3(256), 0, s, A, lda, d, k, flag, info_offset,
                      Xd, ldxi);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const int nbelow = (int)ceil_div(d - k, NB) - 1;
-  if (nbelow > 0) {
-    hipLaunchKernelGGL(potrf_trsm_kernel, dim3(nbelow), dim3(256), 0, s, A, lda, d, k,
-                       (const double*)Xd, ldxi);
-    e = hipGetLastError();
-  }
-  return e;
-}
-
-hipError_t launch_potrf_update(double* A, int lda, int d, int k, hipStream_t s) {
-  const int64_t nt = ceil_div(d - k - NB, NB);
-  if (nt <= 0) return hipSuccess;
-  hipLaunchKernelGGL(potrf_update_kernel, dim3((unsigned)(nt * (nt + 1) / 2)), dim3(256), 0, s, A,
-                     lda, d, k);
   return hipGetLastError();
 }
 
-hipError_t launch_trtri_diag(const double* L, int ldl, double* X, int ldx, int d, hipStream_t s) {
-  hipLaunchKernelGGL(trtri_diag_kernel, dim3((unsigned)ceil_div(d, NB)), dim3(256), 0, s, L, ldl,
-                     X, ldx, d);
+hipError_t launch_potrf_trsm(double* A, int lda, int d, int k, const double* Xi, int ldxi,
+                             hipStream_t s) {
+  const int nbelow = (int)ceil_div(d - k, NB) - 1;
+  if (nbelow <= 0) return hipSuccess;
+  hipLaunchKernelGGL(potrf_trsm_kernel, dim3(nbelow), dim3(256), 0, s, A, lda, d, k,
+                     Xi + (int64_t)k * ldxi + k, ldxi);
+  return hipGetLastError();
+}
+
+hipError_t launch_potrf_update(double* A, int lda, int d, int k, int* flag, int info_offset,
+                               double* Xi, int ldxi, hipStream_t s) {
+  const int64_t nt = ceil_div(d - k - NB, NB);
+  if (nt <= 0) return hipSuccess;
+  const int kn = k + NB;
+  hipLaunchKernelGGL(potrf_update_kernel, dim3((unsigned)(nt * (nt + 1) / 2)), dim3(256), 0, s, A,
+                     lda, d, k, flag, info_offset, Xi + (int64_t)kn * ldxi + kn, ldxi);
   return hipGetLastError();
 }
 

@@ -41,10 +41,15 @@ constexpr int kSyrkTile = 256;
 // fp64 Cholesky route
 hipError_t launch_damp_to_f64(const float* H, int d, double percdamp, double* A, int* flag,
                               hipStream_t s);
-hipError_t launch_potrf_panel(double* A, int lda, int d, int k, int* flag, int info_offset,
-                              double* Xi, int ldxi, hipStream_t s);
-hipError_t launch_potrf_update(double* A, int lda, int d, int k, hipStream_t s);
-hipError_t launch_trtri_diag(const double* L, int ldl, double* X, int ldx, int d, hipStream_t s);
+// Cholesky of panel k's 64x64 diagonal block, with its inverse stored in Xi
+hipError_t launch_potrf_diag(double* A, int lda, int d, int k, int* flag, int info_offset,
+                             double* Xi, int ldxi, hipStream_t s);
+// L_ik = A_ik L_kk^-T below panel k's diagonal block
+hipError_t launch_potrf_trsm(double* A, int lda, int d, int k, const double* Xi, int ldxi,
+                             hipStream_t s);
+// trailing update after panel k, fused with the diagonal block of panel k+1
+hipError_t launch_potrf_update(double* A, int lda, int d, int k, int* flag, int info_offset,
+                               double* Xi, int ldxi, hipStream_t s);
 hipError_t launch_trtri_level(const double* L, int ldl, double* X, int ldx, int d, int half,
                               hipStream_t s);
 hipError_t launch_lauum(const double* X, int ldx, double* S, int lds, int d, hipStream_t s);

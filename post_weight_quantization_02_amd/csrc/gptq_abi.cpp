@@ -134,19 +134,22 @@ gptq_status gptq_prepare_hinv(const float* H, int64_t d, double percdamp, float*
 
   // A = H + lambda I (fp64, lower triangle); resets the pivot flag.
   GPTQ_TRY(launch_damp_to_f64(H, di, percdamp, A, flag, s));
-  // L = chol(A), in place; the inverted 64x64 diagonal blocks of L land in Xi
+  // L = chol(A), in place; the inverted 64x64 diagonal blocks of L land in Xi.
+  // Each trailing update also factors the next panel's diagonal block.
+  GPTQ_TRY(launch_potrf_diag(A, di, di, 0, flag, 0, Xi, di, s));
   for (int k = 0; k < di; k += kPanel) {
-    GPTQ_TRY(launch_potrf_panel(A, di, di, k, flag, 0, Xi, di, s));
-    if (k + kPanel < di) GPTQ_TRY(launch_potrf_update(A, di, di, k, s));
+    GPTQ_TRY(launch_potrf_trsm(A, di, di, k, Xi, di, s));
+    GPTQ_TRY(launch_potrf_update(A, di, di, k, flag, 0, Xi, di, s));
   }
   // Xi = L^{-1}: combine the inverted diagonal blocks level by level
   for (int half = kPanel; half < di; half *= 2) GPTQ_TRY(launch_trtri_level(A, di, Xi, di, di, half, s));
   // A = Xi^T Xi = H_d^{-1} (lower triangle)
   GPTQ_TRY(launch_lauum(Xi, di, A, di, di, s));
   // L2 = chol(H_d^{-1}), in place (Xi is free again and takes the block inverses)
+  GPTQ_TRY(launch_potrf_diag(A, di, di, 0, flag, di, Xi, di, s));
   for (int k = 0; k < di; k += kPanel) {
-    GPTQ_TRY(launch_potrf_panel(A, di, di, k, flag, di, Xi, di, s));
-    if (k + kPanel < di) GPTQ_TRY(launch_potrf_update(A, di, di, k, s));
+    GPTQ_TRY(launch_potrf_trsm(A, di, di, k, Xi, di, s));
+    GPTQ_TRY(launch_potrf_update(A, di, di, k, flag, di, Xi, di, s));
   }
   // Hinv = L2^T (upper), fp32
   GPTQ_TRY(launch_store_upper_f32(A, di, Hinv, di, s));
