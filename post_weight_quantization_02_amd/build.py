@@ -14,6 +14,13 @@ BUILD = os.path.join(HERE, "_build")
 
 SOURCES = ["gptq_abi.cpp", "syrk_f16.hip", "chol_f64.hip", "sweep.hip"]
 
+# Per-file code generation options.  The fp64 kernels keep their MFMA
+# accumulators in ordinary VGPRs: with the default AGPR form the compiler
+# copies fp64 accumulators between the two register files around every
+# MFMA, which halves fp64 MFMA throughput.  (The fp16 SYRK needs the AGPRs
+# for its 256 accumulator registers per lane.)
+EXTRA = {"chol_f64.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",
@@ -26,7 +33,7 @@ FLAGS = [
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, src + ".o")
-    cmd = [HIPCC, *FLAGS, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *EXTRA.get(src, []), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")

@@ -369,21 +369,27 @@ __global__ __launch_bounds__(256) void potrf_trsm_kernel(double* __restrict__ A,
       }
 }
 
-// Trailing update of the lower triangle after panel k: A_ij -= L_ik L_jk^T
-// for all 64x64 tiles i >= j of A[t0:, t0:], t0 = k + 64, both panel blocks
+// Update after panel k inside an outer panel: A_ij -= L_ik L_jk^T for the
+// 64x64 tiles i >= j of A[t0:, t0:], t0 = k + 64, whose column block j lies
+// in the first `ncol` blocks (the launch grid counts them), both panel blocks
 // in LDS.  Workgroup 0 takes tile (0, 0), the next panel's diagonal block,
 // keeps the updated block in LDS and goes on to factor and invert it
 // (diag_factor): the next panel's serial step runs while the other
 // workgroups are still updating, instead of after them (lookahead of one
 // panel).
 __global__ __launch_bounds__(256, 2) void potrf_update_kernel(double* __restrict__ A, int lda, int d,
-                                                           int k, int* flag, int info_offset,
+                                                           int k, int nt, int* flag, int info_offset,
                                                            double* __restrict__ Xn, int ldxn) {
   __shared__ DiagLds sh;
   double (*Ps)[PP] = sh.S;
   double (*Qs)[PP] = sh.Xs;
-  int ti, tj;
-  lower_tile(blockIdx.x, ti, tj);
+  // tile (ti, tj), ti >= tj, column by column: column tj holds nt - tj tiles
+  int ti = blockIdx.x, tj = 0;
+  while (ti >= nt - tj) {
+    ti -= nt - tj;
+    ++tj;
+  }
+  ti += tj;
   const int t0 = k + NB;
   const int r0 = t0 + NB * ti, c0 = t0 + NB * tj;
   const int tid = threadIdx.x;
@@ -469,9 +475,20 @@ struct GemmDesc {
   int M, N, K;
   double alpha, beta;
   int tri;    // 1: only tiles with tm >= tn (square C)
-  int kmode;  // 0 all K; 1 k >= tn*GT; 2 k < (tm+1)*GT; 3 k >= tm*GT
+  int kmode;  // K range of a tile: 0 all; 1 k >= n0; 2 k < m0 + tile; 3 k >= m0
+  int trA;    // 1: opA(m,k) = 0 for k > m; 2: opA(m,k) = 0 for k < m
+  int trB;    // 1: opB(k,n) = 0 for k < n; 2: opB(k,n) = 0 for k > n
   int64_t bsa, bsb, bsc;  // per-batch (blockIdx.y) element offsets
 };
+
+// Zero an operand element outside its triangle (the K-range of a tile is
+// only tile-aligned, so a triangular operand's other half may be read):
+// tr 1 keeps row >= col, tr 2 keeps row <= col.
+__device__ inline double tri_mask(double v, int tr, int row, int col) {
+  if (tr == 1 && col > row) return 0.0;
+  if (tr == 2 && col < row) return 0.0;
+  return v;
+}
 
 // AK: A element (m,k) at A[m*lda+k] (else A[k*lda+m]).
 // BN: B element (k,n) at B[k*ldb+n] (else B[n*ldb+k]).
@@ -511,6 +528,9 @@ __global__ __launch_bounds__(256) void gemm64_f64_kernel(GemmDesc g) {
 #pragma unroll
     for (int b = 0; b < 2; ++b) acc[a][b] = f64x4{0.0, 0.0, 0.0, 0.0};
 
+  // Loads read clamped (always valid) addresses and keep the raw values; the
+  // bounds and triangle masks are applied when the values go to LDS, so the
+  // MFMAs of the current chunk never wait for the next chunk's loads.
   double av[4], bv[4];
   auto gload = [&](int kc) {
 #pragma unroll
@@ -518,25 +538,33 @@ __global__ __launch_bounds__(256) void gemm64_f64_kernel(GemmDesc g) {
       const int e = tid + 256 * q;
       const int kk = AK ? (e % GK) : (e / GT);
       const int mm = AK ? (e / GK) : (e % GT);
-      const int gm = m0 + mm, gk = kc + kk;
-      av[q] = (gm < g.M && gk < k1) ? (AK ? Ap[(int64_t)gm * g.lda + gk] : Ap[(int64_t)gk * g.lda + gm]) : 0.0;
+      const int gm = min(m0 + mm, g.M - 1), gk = min(kc + kk, k1 - 1);
+      av[q] = AK ? Ap[(int64_t)gm * g.lda + gk] : Ap[(int64_t)gk * g.lda + gm];
       const int kb = BN ? (e / GT) : (e % GK);
       const int nn = BN ? (e % GT) : (e / GK);
-      const int gn = n0 + nn, gk2 = kc + kb;
-      bv[q] = (gn < g.N && gk2 < k1) ? (BN ? Bp[(int64_t)gk2 * g.ldb + gn] : Bp[(int64_t)gn * g.ldb + gk2]) : 0.0;
+      const int gn = min(n0 + nn, g.N - 1), gk2 = min(kc + kb, k1 - 1);
+      bv[q] = BN ? Bp[(int64_t)gk2 * g.ldb + gn] : Bp[(int64_t)gn * g.ldb + gk2];
     }
   };
-  auto lstore = [&](int buf) {
+  auto lstore = [&](int buf, int kc) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int e = tid + 256 * q;
-      As[buf][AK ? (e % GK) : (e / GT)][AK ? (e / GK) : (e % GT)] = av[q];
-      Bs[buf][BN ? (e / GT) : (e % GK)][BN ? (e % GT) : (e / GK)] = bv[q];
+      const int kk = AK ? (e % GK) : (e / GT);
+      const int mm = AK ? (e / GK) : (e % GT);
+      const int gm = m0 + mm, gk = kc + kk;
+      const bool va = gm < g.M && gk < k1;
+      As[buf][kk][mm] = va ? tri_mask(av[q], g.trA, gm, gk) : 0.0;
+      const int kb = BN ? (e / GT) : (e % GK);
+      const int nn = BN ? (e % GT) : (e / GK);
+      const int gn = n0 + nn, gk2 = kc + kb;
+      const bool vb = gn < g.N && gk2 < k1;
+      Bs[buf][kb][nn] = vb ? tri_mask(bv[q], g.trB, gk2, gn) : 0.0;
     }
   };
   if (k0 < k1) {
     gload(k0);
-    lstore(0);
+    lstore(0, k0);
     __syncthreads();
   }
   int buf = 0;
@@ -557,7 +585,7 @@ __global__ __launch_bounds__(256) void gemm64_f64_kernel(GemmDesc g) {
         for (int b = 0; b < 2; ++b)
           acc[a][b] = __builtin_amdgcn_mfma_f64_16x16x4f64(af[a], bf[b], acc[a][b], 0, 0, 0);
     }
-    if (more) lstore(buf ^ 1);
+    if (more) lstore(buf ^ 1, kc + GK);
     __syncthreads();
     buf ^= 1;
   }
@@ -587,6 +615,156 @@ hipError_t gemm64(const GemmDesc& g, int batches, hipStream_t s) {
   return hipGetLastError();
 }
 
+
+// The same product on 128x128 tiles: each wave owns a 64x64 quadrant (4x4
+// MFMA tiles), twice the arithmetic per loaded element of the 64x64 kernel,
+// which keeps large products on fp64 MFMA rather than on L2 bandwidth.
+constexpr int GT2 = 128;
+template <bool AK, bool BN, bool CN>
+__global__ __launch_bounds__(256, 2) void gemm128_f64_kernel(GemmDesc g) {
+  // LDS layout per operand follows its contiguous global dimension, so the
+  // stores are conflict-free: k-contiguous operands are kept row-major
+  // ([m][k], pitch GK + 1), m-contiguous ones k-major ([k][m], pitch 144).
+  constexpr int PK = GT2 + 16;
+  constexpr int PR = GK + 1;
+  constexpr int NL = GT2 * GK / 256;  // elements per thread per operand per chunk
+  constexpr int SA = AK ? GT2 * PR : GK * PK;  // doubles per buffer
+  constexpr int SB = BN ? GK * PK : GT2 * PR;
+  __shared__ double As[2][SA];
+  __shared__ double Bs[2][SB];
+  auto a_at = [&](int buf, int m, int k) -> double& {
+    return AK ? As[buf][m * PR + k] : As[buf][k * PK + m];
+  };
+  auto b_at = [&](int buf, int k, int n) -> double& {
+    return BN ? Bs[buf][k * PK + n] : Bs[buf][n * PR + k];
+  };
+  int tm, tn;
+  const int ntn = (int)ceil_div(g.N, GT2);
+  if (g.tri) {
+    lower_tile(blockIdx.x, tm, tn);
+  } else {
+    tm = blockIdx.x / ntn;
+    tn = blockIdx.x % ntn;
+  }
+  const double* Ap = g.A + (int64_t)blockIdx.y * g.bsa;
+  const double* Bp = g.B + (int64_t)blockIdx.y * g.bsb;
+  double* Cp = g.C + (int64_t)blockIdx.y * g.bsc;
+  const int m0 = tm * GT2, n0 = tn * GT2;
+  int k0 = 0, k1 = g.K;
+  if (g.kmode == 1) k0 = n0;
+  else if (g.kmode == 2) k1 = min(g.K, m0 + GT2);
+  else if (g.kmode == 3) k0 = m0;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  f64x4 acc[4][4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) acc[a][b] = f64x4{0.0, 0.0, 0.0, 0.0};
+
+  // raw loads from clamped addresses; masks are applied at the LDS store
+  double av[NL], bv[NL];
+  auto gload = [&](int kc) {
+#pragma unroll
+    for (int q = 0; q < NL; ++q) {
+      const int e = tid + 256 * q;
+      const int kk = AK ? (e % GK) : (e / GT2);
+      const int mm = AK ? (e / GK) : (e % GT2);
+      const int gm = min(m0 + mm, g.M - 1), gk = min(kc + kk, k1 - 1);
+      av[q] = AK ? Ap[(int64_t)gm * g.lda + gk] : Ap[(int64_t)gk * g.lda + gm];
+      const int kb = BN ? (e / GT2) : (e % GK);
+      const int nn = BN ? (e % GT2) : (e / GK);
+      const int gn = min(n0 + nn, g.N - 1), gk2 = min(kc + kb, k1 - 1);
+      bv[q] = BN ? Bp[(int64_t)gk2 * g.ldb + gn] : Bp[(int64_t)gn * g.ldb + gk2];
+    }
+  };
+  auto lstore = [&](int buf, int kc) {
+#pragma unroll
+    for (int q = 0; q < NL; ++q) {
+      const int e = tid + 256 * q;
+      const int kk = AK ? (e % GK) : (e / GT2);
+      const int mm = AK ? (e / GK) : (e % GT2);
+      const int gm = m0 + mm, gk = kc + kk;
+      const bool va = gm < g.M && gk < k1;
+      a_at(buf, mm, kk) = va ? tri_mask(av[q], g.trA, gm, gk) : 0.0;
+      const int kb = BN ? (e / GT2) : (e % GK);
+      const int nn = BN ? (e % GT2) : (e / GK);
+      const int gn = n0 + nn, gk2 = kc + kb;
+      const bool vb = gn < g.N && gk2 < k1;
+      b_at(buf, kb, nn) = vb ? tri_mask(bv[q], g.trB, gk2, gn) : 0.0;
+    }
+  };
+  if (k0 < k1) {
+    gload(k0);
+    lstore(0, k0);
+    __syncthreads();
+  }
+  int buf = 0;
+  for (int kc = k0; kc < k1; kc += GK) {
+    const bool more = kc + GK < k1;
+    if (more) gload(kc + GK);
+#pragma unroll
+    for (int ks = 0; ks < GK; ks += 4) {
+      const int kr = ks + (lane >> 4);
+      double af[4], bf[4];
+#pragma unroll
+      for (int a = 0; a < 4; ++a) af[a] = a_at(buf, 64 * wm + 16 * a + (lane & 15), kr);
+#pragma unroll
+      for (int b = 0; b < 4; ++b) bf[b] = b_at(buf, kr, 64 * wn + 16 * b + (lane & 15));
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+          acc[a][b] = __builtin_amdgcn_mfma_f64_16x16x4f64(af[a], bf[b], acc[a][b], 0, 0, 0);
+    }
+    if (more) lstore(buf ^ 1, kc + GK);
+    __syncthreads();
+    buf ^= 1;
+  }
+  // epilogue: per row block, all C loads go out before any store
+#pragma unroll
+  for (int a = 0; a < 4; ++a) {
+    double cold[4][4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = min(m0 + 64 * wm + 16 * a + mfma64_row(lane, i), g.M - 1);
+        const int n = min(n0 + 64 * wn + 16 * b + (lane & 15), g.N - 1);
+        cold[b][i] = (g.beta == 0.0) ? 0.0
+                     : (CN ? Cp[(int64_t)m * g.ldc + n] : Cp[(int64_t)n * g.ldc + m]);
+      }
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = m0 + 64 * wm + 16 * a + mfma64_row(lane, i);
+        const int n = n0 + 64 * wn + 16 * b + (lane & 15);
+        if (m < g.M && n < g.N) {
+          double* c = CN ? Cp + (int64_t)m * g.ldc + n : Cp + (int64_t)n * g.ldc + m;
+          const double v = g.alpha * acc[a][b][i];
+          *c = (g.beta == 0.0) ? v : __builtin_fma(g.beta, cold[b][i], v);
+        }
+      }
+  }
+}
+
+// Large products take the 128x128 kernel; small ones, and triangular
+// products of moderate size (whose long-K tiles would leave the GPU
+// unbalanced on 128x128 tiles), the 64x64 one.
+template <bool AK, bool BN, bool CN>
+hipError_t gemm_f64(const GemmDesc& g, int batches, hipStream_t s) {
+  if (g.M <= 0 || g.N <= 0 || batches <= 0) return hipSuccess;
+  const int64_t tm = ceil_div(g.M, GT2), tn = ceil_div(g.N, GT2);
+  const int64_t tiles = (g.tri ? tm * (tm + 1) / 2 : tm * tn) * batches;
+  const bool big = g.M > GT && g.N > GT && tiles >= (g.kmode == 0 ? 256 : 1024);
+  if (!big) return gemm64<AK, BN, CN>(g, batches, s);
+  hipLaunchKernelGGL((gemm128_f64_kernel<AK, BN, CN>), dim3((unsigned)(tiles / batches), batches),
+                     dim3(256), 0, s, g);
+  return hipGetLastError();
+}
 
 // -------------------------------------------------------------- fp32 output
 // Hinv[i][j] = L2[j][i] for j >= i, 0 below the diagonal.
@@ -643,14 +821,31 @@ hipError_t launch_potrf_trsm(double* A, int lda, int d, int k, const double* Xi,
   return hipGetLastError();
 }
 
-hipError_t launch_potrf_update(double* A, int lda, int d, int k, int* flag, int info_offset,
-                               double* Xi, int ldxi, hipStream_t s) {
+hipError_t launch_potrf_update(double* A, int lda, int d, int k, int ncol, int* flag,
+                               int info_offset, double* Xi, int ldxi, hipStream_t s) {
   const int64_t nt = ceil_div(d - k - NB, NB);
-  if (nt <= 0) return hipSuccess;
+  if (nt <= 0 || ncol <= 0) return hipSuccess;
+  const int64_t nc = ncol < nt ? ncol : nt;
+  const int64_t tiles = nc * nt - nc * (nc - 1) / 2;
   const int kn = k + NB;
-  hipLaunchKernelGGL(potrf_update_kernel, dim3((unsigned)(nt * (nt + 1) / 2)), dim3(256), 0, s, A,
-                     lda, d, k, flag, info_offset, Xi + (int64_t)kn * ldxi + kn, ldxi);
+  hipLaunchKernelGGL(potrf_update_kernel, dim3((unsigned)tiles), dim3(256), 0, s, A, lda, d, k,
+                     (int)nt, flag, info_offset, Xi + (int64_t)kn * ldxi + kn, ldxi);
   return hipGetLastError();
+}
+
+// A[k1:, k1:] -= P P^T on the lower 128x128 tiles, P = A[k1:, k0:k1] (the
+// panels of the finished outer block): one rank-(k1 - k0) update.
+hipError_t launch_potrf_outer_update(double* A, int lda, int d, int k0, int k1, hipStream_t s) {
+  if (k1 >= d || k1 <= k0) return hipSuccess;
+  GemmDesc g{};
+  g.A = A + (int64_t)k1 * lda + k0;
+  g.B = A + (int64_t)k1 * lda + k0;  // element (k, n) = P[n][k]
+  g.C = A + (int64_t)k1 * lda + k1;
+  g.lda = lda; g.ldb = lda; g.ldc = lda;
+  g.M = g.N = d - k1;
+  g.K = k1 - k0;
+  g.alpha = -1.0; g.beta = 1.0; g.tri = 1; g.kmode = 0;
+  return gemm_f64<true, false, true>(g, 1, s);
 }
 
 // Combine pairs of inverted blocks of size `half`:
@@ -675,8 +870,9 @@ hipError_t launch_trtri_level(const double* L, int ldl, double* X, int ldx, int 
     g1.lda = ldl; g1.ldb = ldx; g1.ldc = ldx;
     g1.M = sc; g1.N = half; g1.K = half;
     g1.alpha = 1.0; g1.beta = 0.0; g1.tri = 0; g1.kmode = 1;
+    g1.trA = 0; g1.trB = 1;
     g1.bsa = (int64_t)2 * half * (ldl + 1); g1.bsb = bs; g1.bsc = bs;
-    hipError_t e = gemm64<true, true, false>(g1, batches, s);
+    hipError_t e = gemm_f64<true, true, false>(g1, batches, s);
     if (e != hipSuccess) return e;
     GemmDesc g2{};
     g2.A = X + (int64_t)c0 * ldx + c0;  // C^-1, lower
@@ -685,8 +881,9 @@ hipError_t launch_trtri_level(const double* L, int ldl, double* X, int ldx, int 
     g2.lda = ldx; g2.ldb = ldx; g2.ldc = ldx;
     g2.M = sc; g2.N = half; g2.K = sc;
     g2.alpha = -1.0; g2.beta = 0.0; g2.tri = 0; g2.kmode = 2;
+    g2.trA = 1; g2.trB = 0;
     g2.bsa = bs; g2.bsb = bs; g2.bsc = bs;
-    e = gemm64<true, false, true>(g2, batches, s);
+    e = gemm_f64<true, false, true>(g2, batches, s);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
@@ -700,7 +897,8 @@ hipError_t launch_lauum(const double* X, int ldx, double* S, int lds, int d, hip
   g.lda = ldx; g.ldb = ldx; g.ldc = lds;
   g.M = g.N = g.K = d;
   g.alpha = 1.0; g.beta = 0.0; g.tri = 1; g.kmode = 3;
-  return gemm64<false, true, true>(g, 1, s);
+  g.trA = 2; g.trB = 1;
+  return gemm_f64<false, true, true>(g, 1, s);
 }
 
 hipError_t launch_store_upper_f32(const double* L2, int ld2, float* Hinv, int d, hipStream_t s) {

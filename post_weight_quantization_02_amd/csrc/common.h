@@ -47,14 +47,18 @@ hipError_t launch_potrf_diag(double* A, int lda, int d, int k, int* flag, int in
 // L_ik = A_ik L_kk^-T below panel k's diagonal block
 hipError_t launch_potrf_trsm(double* A, int lda, int d, int k, const double* Xi, int ldxi,
                              hipStream_t s);
-// trailing update after panel k, fused with the diagonal block of panel k+1
-hipError_t launch_potrf_update(double* A, int lda, int d, int k, int* flag, int info_offset,
-                               double* Xi, int ldxi, hipStream_t s);
+// update after panel k of the first ncol 64-column blocks to its right, fused
+// with the diagonal block of panel k+1
+hipError_t launch_potrf_update(double* A, int lda, int d, int k, int ncol, int* flag,
+                               int info_offset, double* Xi, int ldxi, hipStream_t s);
+// rank-(k1-k0) update of A[k1:, k1:] by the finished outer block [k0, k1)
+hipError_t launch_potrf_outer_update(double* A, int lda, int d, int k0, int k1, hipStream_t s);
 hipError_t launch_trtri_level(const double* L, int ldl, double* X, int ldx, int d, int half,
                               hipStream_t s);
 hipError_t launch_lauum(const double* X, int ldx, double* S, int lds, int d, hipStream_t s);
 hipError_t launch_store_upper_f32(const double* L2, int ld2, float* Hinv, int d, hipStream_t s);
 constexpr int kPanel = 64;
+constexpr int kOuterPanel = 512;  // columns per outer block of the two-level Cholesky
 
 // sweep
 hipError_t launch_convert_w(const void* W, int w_dtype, int64_t rows, int64_t cols, int64_t ldw,

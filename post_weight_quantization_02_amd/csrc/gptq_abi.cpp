@@ -61,6 +61,42 @@ bool group_ok(int g) {
   return g >= kBlock && g % kBlock == 0;
 }
 
+// Blocked Cholesky of the lower triangle of A (d x d), in place; the
+// inverted 64x64 diagonal blocks of L land at the diagonal of Xi.
+//
+// Up to kTwoLevelDim: right-looking with 64-column panels, each trailing
+// update (rank 64) also factoring the next diagonal block.  Above it the
+// trailing matrix no longer fits the Infinity Cache and rank-64 updates
+// become HBM-bound, so the factorization is two-level: outer blocks of
+// kOuterPanel columns are factored panel by panel (updates confined to the
+// outer block), then the trailing matrix takes one rank-kOuterPanel update.
+constexpr int kTwoLevelDim = 8192;
+hipError_t potrf(double* A, int d, int* flag, int info_offset, double* Xi, hipStream_t s) {
+  hipError_t e = launch_potrf_diag(A, d, d, 0, flag, info_offset, Xi, d, s);
+  if (d <= kTwoLevelDim) {
+    for (int k = 0; k < d && e == hipSuccess; k += kPanel) {
+      e = launch_potrf_trsm(A, d, d, k, Xi, d, s);
+      if (e == hipSuccess && k + kPanel < d)
+        e = launch_potrf_update(A, d, d, k, d, flag, info_offset, Xi, d, s);
+    }
+    return e;
+  }
+  for (int K = 0; K < d && e == hipSuccess; K += kOuterPanel) {
+    const int Kend = (K + kOuterPanel < d) ? K + kOuterPanel : d;
+    for (int k = K; k < Kend && e == hipSuccess; k += kPanel) {
+      e = launch_potrf_trsm(A, d, d, k, Xi, d, s);
+      if (e == hipSuccess && k + kPanel < Kend)
+        e = launch_potrf_update(A, d, d, k, (int)ceil_div(Kend - k - kPanel, kPanel), flag,
+                                info_offset, Xi, d, s);
+    }
+    if (e == hipSuccess && Kend < d) {
+      e = launch_potrf_outer_update(A, d, d, K, Kend, s);
+      if (e == hipSuccess) e = launch_potrf_diag(A, d, d, Kend, flag, info_offset, Xi, d, s);
+    }
+  }
+  return e;
+}
+
 }  // namespace
 
 extern "C" {
@@ -135,22 +171,13 @@ gptq_status gptq_prepare_hinv(const float* H, int64_t d, double percdamp, float*
   // A = H + lambda I (fp64, lower triangle); resets the pivot flag.
   GPTQ_TRY(launch_damp_to_f64(H, di, percdamp, A, flag, s));
   // L = chol(A), in place; the inverted 64x64 diagonal blocks of L land in Xi.
-  // Each trailing update also factors the next panel's diagonal block.
-  GPTQ_TRY(launch_potrf_diag(A, di, di, 0, flag, 0, Xi, di, s));
-  for (int k = 0; k < di; k += kPanel) {
-    GPTQ_TRY(launch_potrf_trsm(A, di, di, k, Xi, di, s));
-    GPTQ_TRY(launch_potrf_update(A, di, di, k, flag, 0, Xi, di, s));
-  }
+  GPTQ_TRY(potrf(A, di, flag, 0, Xi, s));
   // Xi = L^{-1}: combine the inverted diagonal blocks level by level
   for (int half = kPanel; half < di; half *= 2) GPTQ_TRY(launch_trtri_level(A, di, Xi, di, di, half, s));
   // A = Xi^T Xi = H_d^{-1} (lower triangle)
   GPTQ_TRY(launch_lauum(Xi, di, A, di, di, s));
   // L2 = chol(H_d^{-1}), in place (Xi is free again and takes the block inverses)
-  GPTQ_TRY(launch_potrf_diag(A, di, di, 0, flag, di, Xi, di, s));
-  for (int k = 0; k < di; k += kPanel) {
-    GPTQ_TRY(launch_potrf_trsm(A, di, di, k, Xi, di, s));
-    GPTQ_TRY(launch_potrf_update(A, di, di, k, flag, di, Xi, di, s));
-  }
+  GPTQ_TRY(potrf(A, di, flag, di, Xi, s));
   // Hinv = L2^T (upper), fp32
   GPTQ_TRY(launch_store_upper_f32(A, di, Hinv, di, s));
   int hflag = 0;

@@ -81,3 +81,18 @@ def test_upper_triangle_of_H_is_not_read(env):
     Hp = H.copy()
     Hp[np.triu_indices(150, 1)] = np.nan
     np.testing.assert_array_equal(_hinv(env, H), _hinv(env, Hp))
+
+
+def test_two_level_cholesky_matches_oracle(env):
+    """Dimensions above 8192 take the two-level factorization (outer blocks of
+    512 columns); 8250 is ragged against both the 64- and 512-column blocks.
+    H = Z Z^T + 0.05 I from a seeded Gaussian Z keeps the oracle fast."""
+    d, r = 8250, 384
+    rng = np.random.default_rng(8250)
+    Z = rng.standard_normal((d, r)) / np.sqrt(r)
+    H32 = (Z @ Z.T + 0.05 * np.eye(d)).astype(np.float32)
+    Uref, _ = oracle.hinv_upper(H32.astype(np.float64), 0.01)
+    U = _hinv(env, H32)
+    assert np.all(np.tril(U, -1) == 0)
+    err = np.abs(U - Uref).max() / np.abs(Uref).max()
+    assert err <= 2e-6, err
