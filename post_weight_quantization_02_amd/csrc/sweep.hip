@@ -291,7 +291,7 @@ constexpr int LK = 32;   // K chunk
 constexpr int LP = LT + 16;
 
 template <int MT>  // 16x16 MFMA tiles per wave along rows: workgroup tile (32*MT) x 128
-__global__ __launch_bounds__(256) void lazy_kernel(float* __restrict__ Wk, int64_t ldk,
+__global__ __launch_bounds__(256, 2) void lazy_kernel(float* __restrict__ Wk, int64_t ldk,
                                                    int64_t rows, int64_t cols, int k0, int k1,
                                                    int c0, int c1, const float* __restrict__ Err,
                                                    const float* __restrict__ Hinv) {
@@ -313,87 +313,72 @@ __global__ __launch_bounds__(256) void lazy_kernel(float* __restrict__ Wk, int64
 #pragma unroll
     for (int b = 0; b < 4; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // loader mapping: A chunk = 128 rows x 32 k = 1024 float4 (4 per thread);
-  // B chunk = 32 k-rows x 128 n = 1024 float4 (4 per thread)
+  // Loads read in-bounds addresses unconditionally and keep the raw values;
+  // entries past K, past c1 or past the last row are zeroed (or ignored)
+  // when the chunk goes to LDS, so no MFMA waits for the next chunk's loads.
+  // A = Err[r0.., k0..k1]: the row stride ldk is a multiple of 128 and k0 a
+  // multiple of 128, so a whole chunk stays inside each (clamped) row.
+  // B = Hinv[k0..k1, n0..]: row and column indices are clamped.
   float4 av[AV], bv[4];
   auto gload = [&](int kc) {
 #pragma unroll
     for (int q = 0; q < AV; ++q) {
       const int e = tid + 256 * q;
       const int m = e >> 3, kk = (e & 7) * 4;  // A: 8 float4 per row
-      const int64_t gr = r0 + m;
-      const int gk = kc + kk;
-      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (gr < rows) {
-        const float* p = Err + gr * ldk + k0 + gk;
-        if (gk + 4 <= K) {
-          v = *reinterpret_cast<const float4*>(p);
-        } else {
-          if (gk + 0 < K) v.x = p[0];
-          if (gk + 1 < K) v.y = p[1];
-          if (gk + 2 < K) v.z = p[2];
-        }
-      }
-      av[q] = v;
+      const int64_t gr = (r0 + m < rows) ? r0 + m : rows - 1;
+      av[q] = *reinterpret_cast<const float4*>(Err + gr * ldk + k0 + kc + kk);
     }
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int e = tid + 256 * q;
       const int kb = e >> 5, nn = (e & 31) * 4;  // B: 32 float4 per k-row
+      const int krow = min(k0 + kc + kb, k1 - 1);
+      const float* p = Hinv + (int64_t)krow * cols;
       const int64_t gc = n0 + nn;
-      float4 u = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (kc + kb < K) {
-        const float* p = Hinv + (int64_t)(k0 + kc + kb) * cols + gc;
-        if (gc + 4 <= c1) {
-          u = make_float4(p[0], p[1], p[2], p[3]);
-        } else {
-          if (gc + 0 < c1) u.x = p[0];
-          if (gc + 1 < c1) u.y = p[1];
-          if (gc + 2 < c1) u.z = p[2];
-        }
-      }
-      bv[q] = u;
+      const int64_t cl = cols - 1;
+      bv[q] = make_float4(p[gc < cl ? gc : cl], p[gc + 1 < cl ? gc + 1 : cl],
+                          p[gc + 2 < cl ? gc + 2 : cl], p[gc + 3 < cl ? gc + 3 : cl]);
     }
   };
-  auto lstore = [&](int buf) {
+  auto lstore = [&](int buf, int kc) {
 #pragma unroll
     for (int q = 0; q < AV; ++q) {
       const int e = tid + 256 * q;
       const int m = e >> 3, kk = (e & 7) * 4;
-      As[buf][kk + 0][m] = av[q].x;
-      As[buf][kk + 1][m] = av[q].y;
-      As[buf][kk + 2][m] = av[q].z;
-      As[buf][kk + 3][m] = av[q].w;
+      const int gk = kc + kk;
+      As[buf][kk + 0][m] = (gk + 0 < K) ? av[q].x : 0.f;
+      As[buf][kk + 1][m] = (gk + 1 < K) ? av[q].y : 0.f;
+      As[buf][kk + 2][m] = (gk + 2 < K) ? av[q].z : 0.f;
+      As[buf][kk + 3][m] = (gk + 3 < K) ? av[q].w : 0.f;
     }
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int e = tid + 256 * q;
       const int kb = e >> 5, nn = (e & 31) * 4;
-      *reinterpret_cast<float4*>(&Bs[buf][kb][nn]) = bv[q];
+      const bool kv = kc + kb < K;
+      const int64_t gc = n0 + nn;
+      float4 u = bv[q];
+      u.x = (kv && gc + 0 < c1) ? u.x : 0.f;
+      u.y = (kv && gc + 1 < c1) ? u.y : 0.f;
+      u.z = (kv && gc + 2 < c1) ? u.z : 0.f;
+      u.w = (kv && gc + 3 < c1) ? u.w : 0.f;
+      *reinterpret_cast<float4*>(&Bs[buf][kb][nn]) = u;
     }
   };
 
-  f32x4 cv[MT][4];
+  // this lane's output elements: rows rb + 16a + i, columns cb + 16b
+  const int64_t rb = r0 + 16 * MT * wm + 4 * (lane >> 4);
+  const int64_t cb = n0 + 64 * wn + (lane & 15);
+  float* const wbase = Wk + rb * ldk + cb;
+  const int ldi = (int)ldk;
   const int nchunks = (K + LK - 1) / LK;
   gload(0);
-  lstore(0);
+  lstore(0, 0);
   __syncthreads();
   int buf = 0;
   for (int ch = 0; ch < nchunks; ++ch) {
     const bool more = ch + 1 < nchunks;
     if (more) gload((ch + 1) * LK);
-    if (ch + 1 == nchunks) {
-#pragma unroll
-      for (int a = 0; a < MT; ++a)
-#pragma unroll
-        for (int b = 0; b < 4; ++b)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int64_t r = r0 + 16 * MT * wm + 16 * a + 4 * (lane >> 4) + i;
-            const int64_t c = n0 + 64 * wn + 16 * b + (lane & 15);
-            cv[a][b][i] = (r < rows && c < c1) ? Wk[r * ldk + c] : 0.f;
-          }
-    }
 #pragma unroll
     for (int ks = 0; ks < LK; ks += 4) {
       const int kr = ks + (lane >> 4);
@@ -408,20 +393,28 @@ __global__ __launch_bounds__(256) void lazy_kernel(float* __restrict__ Wk, int64
         for (int b = 0; b < 4; ++b)
           acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[a], bf[b], acc[a][b], 0, 0, 0);
     }
-    if (more) lstore(buf ^ 1);
+    if (more) lstore(buf ^ 1, (ch + 1) * LK);
     __syncthreads();
     buf ^= 1;
   }
+  // read-modify-write of the W tile, all loads of a row block before its stores
 #pragma unroll
-  for (int a = 0; a < MT; ++a)
+  for (int a = 0; a < MT; ++a) {
+    float cv[4][4];
 #pragma unroll
-    for (int b = 0; b < 4; ++b)
+    for (int i = 0; i < 4; ++i) {
+      const bool rv = rb + 16 * a + i < rows;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int64_t r = r0 + 16 * MT * wm + 16 * a + 4 * (lane >> 4) + i;
-        const int64_t c = n0 + 64 * wn + 16 * b + (lane & 15);
-        if (r < rows && c < c1) Wk[r * ldk + c] = cv[a][b][i] - acc[a][b][i];
-      }
+      for (int b = 0; b < 4; ++b) cv[i][b] = rv ? wbase[(16 * a + i) * ldi + 16 * b] : 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bool rv = rb + 16 * a + i < rows;
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+        if (rv && cb + 16 * b < c1) wbase[(16 * a + i) * ldi + 16 * b] = cv[i][b] - acc[a][b][i];
+    }
+  }
 }
 
 // ---------------------------------------------------------------- helpers
