@@ -33,6 +33,8 @@
 // through LDS in chunks of 16.
 #include "common.h"
 
+#include <utility>
+
 namespace gptq {
 
 namespace {
@@ -83,22 +85,58 @@ __device__ inline void group_stats(float mn, float mx, float qm, float& s, float
 // Value of `v` held by lane `src + 16*rg` of the wave, for each lane's row
 // group rg (src is wave-uniform): four readlanes combined with the lane's 0/1
 // row-group masks (branch-free; exact because each product is v or 0).
-__device__ inline float bcast16(float v, int src, const float (&m)[4]) {
-  const int iv = __builtin_bit_cast(int, v);
-  const float e0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(iv, src));
-  const float e1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(iv, src + 16));
-  const float e2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(iv, src + 32));
-  const float e3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(iv, src + 48));
-  return (e0 * m[0] + e1 * m[1]) + (e2 * m[2] + e3 * m[3]);
+// Value of v held by lane LJ of this lane's row of 16 (DPP row_newbcast):
+// each row of 16 lanes is one row of W, so this is the owner's value.
+template <int LJ>
+__device__ inline float row_bcast(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x150 + LJ, 0xF, 0xF, true));
+}
+
+// Column step j = 16*kj + LJ of the sweep for this lane's row (see sweep_kernel).
+template <int LJ>
+__device__ inline void sweep_step(int kj, int l, float s, float z, float rs, float qm, float rd,
+                                  const float* __restrict__ urow, float (&w)[CPL],
+                                  float (&u)[CPL], float (&qc)[CPL], float (&ev)[CPL]) {
+  // next step's Hinv row segment, off the dependency chain
+  float un[CPL];
+  if (LJ + 1 < RL) {
+#pragma unroll
+    for (int k = kj; k < CPL; ++k) un[k] = urow[(LJ + 1) * BC + l + RL * k];
+  }
+  const float x = w[kj];
+  const float t = div_rn(x, s, rs) + z;
+  const float q = fminf(fmaxf(rintf(t), 0.f), qm);
+  const float err = __builtin_fmaf(-(q - z), s, x);
+  const float eb = row_bcast<LJ>(err * rd);
+  if (l == LJ) {
+    qc[kj] = q;
+    ev[kj] = eb;
+  }
+#pragma unroll
+  for (int k = kj; k < CPL; ++k) w[k] = __builtin_fmaf(-eb, u[k], w[k]);
+  if (LJ + 1 < RL) {
+#pragma unroll
+    for (int k = kj; k < CPL; ++k) u[k] = un[k];
+  }
+  __builtin_amdgcn_sched_barrier(0);  // keep steps apart: bounded register pressure
+}
+
+template <int... LJ>
+__device__ inline void sweep_steps(int kj, int l, float s, float z, float rs, float qm, float rd,
+                                   const float* __restrict__ urow, float (&w)[CPL],
+                                   float (&u)[CPL], float (&qc)[CPL], float (&ev)[CPL],
+                                   std::integer_sequence<int, LJ...>) {
+  (sweep_step<LJ>(kj, l, s, z, rs, qm, rd, urow, w, u, qc, ev), ...);
 }
 
 // G: group size when it divides the block (16, 32, 64, 128); G == 0 means the
 // group spans several blocks (groupsize a multiple of 128).
 //
-// Column j = 16*kj + lj lives in register kj of lane lj.  The register group
-// kj is an unrolled outer loop (so every register index is a compile-time
-// constant) and the 16 steps inside it are a runtime loop whose owner lane lj
-// is wave-uniform.
+// Column j = 16*kj + lj lives in register kj of lane lj.  Both loops are
+// unrolled, so every register index and the DPP source lane are compile-time
+// constants.  Steps past the end of a short last block run on zero weights
+// and zero Hinv entries and change nothing.
 template <int G>
 __global__ __launch_bounds__(256) void sweep_kernel(float* __restrict__ Wk, int64_t ldk,
                                                     int64_t rows, int64_t cols, int i1,
@@ -170,9 +208,6 @@ __global__ __launch_bounds__(256) void sweep_kernel(float* __restrict__ Wk, int6
 
   const float qm = (float)((1 << bits) - 1);
   float s = 1.f, z = 0.f, rs = 1.f;
-  float rmask[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) rmask[r] = (rg == r) ? 1.f : 0.f;
   if (G == 0) {
     // group of groupsize columns spanning blocks
     const int64_t gi = i1 / groupsize;
@@ -223,36 +258,13 @@ __global__ __launch_bounds__(256) void sweep_kernel(float* __restrict__ Wk, int6
       group_stats(mn, mx, qm, s, z, rs, rv, l, row, ngroups, (i1 + RL * kj) / groupsize, scales,
                   zeros);
     }
-    const int jend = min(RL, nbc - RL * kj);
     // this lane's column 16*kj + l: its 1/Hinv[j][j] (only the owner's is used)
     const float rd = rdiag[RL * kj + l];
-    float u[CPL], un[CPL];
+    const float* urow = Ub + (RL * kj) * BC;
+    float u[CPL];
 #pragma unroll
-    for (int k = kj; k < CPL; ++k) u[k] = Ub[(RL * kj) * BC + l + RL * k];
-#pragma unroll 1
-    for (int lj = 0; lj < jend; ++lj) {
-      const int j = RL * kj + lj;
-      // next step's Hinv row segment, off the dependency chain
-      if (lj + 1 < jend) {
-#pragma unroll
-        for (int k = kj; k < CPL; ++k) un[k] = Ub[(j + 1) * BC + l + RL * k];
-      }
-      const float x = w[kj];
-      const float t = div_rn(x, s, rs) + z;
-      const float q = fminf(fmaxf(rintf(t), 0.f), qm);
-      const float err = __builtin_fmaf(-(q - z), s, x);
-      const float e = err * rd;
-      const float eb = bcast16(e, lj, rmask);
-      if (l == lj) {
-        qc[kj] = q;
-        ev[kj] = eb;
-      }
-#pragma unroll
-      for (int k = kj; k < CPL; ++k) {
-        w[k] = __builtin_fmaf(-eb, u[k], w[k]);
-        u[k] = un[k];
-      }
-    }
+    for (int k = kj; k < CPL; ++k) u[k] = urow[l + RL * k];
+    sweep_steps(kj, l, s, z, rs, qm, rd, urow, w, u, qc, ev, std::make_integer_sequence<int, RL>{});
   }
 
   // outputs
