@@ -490,6 +490,32 @@ __device__ inline double tri_mask(double v, int tr, int row, int col) {
   return v;
 }
 
+// Tile of a GEMM launch for workgroup `p`.  When the K range depends on the
+// tile (triangular operands), tiles are taken longest first, snaking over
+// groups of 256 workgroups (one per CU), so the tiles a CU holds at the
+// same time have mixed lengths.
+__device__ inline void gemm_tile(int p, int ntiles, int ntm, int ntn, int tri, int kmode, int& tm,
+                                 int& tn) {
+  int r = p;
+  if (kmode != 0) {
+    const int g = p >> 8, i = p & 255;
+    const int gsize = min(256, ntiles - (g << 8));
+    r = (g << 8) + ((g & 1) ? gsize - 1 - i : i);
+  }
+  if (tri) {
+    lower_tile(r, tm, tn);  // tm ascending: longest first for kmode 3
+  } else if (kmode == 1) {  // length K - n0: columns first
+    tn = r / ntm;
+    tm = r % ntm;
+  } else if (kmode == 2) {  // length m0 + tile: last rows first
+    tm = ntm - 1 - r / ntn;
+    tn = r % ntn;
+  } else {
+    tm = r / ntn;
+    tn = r % ntn;
+  }
+}
+
 // AK: A element (m,k) at A[m*lda+k] (else A[k*lda+m]).
 // BN: B element (k,n) at B[k*ldb+n] (else B[n*ldb+k]).
 // CN: C element (m,n) at C[m*ldc+n] (else C[n*ldc+m]).
@@ -503,13 +529,8 @@ __global__ __launch_bounds__(256) void gemm64_f64_kernel(GemmDesc g) {
   __shared__ double As[2][GK][PK];
   __shared__ double Bs[2][GK][PK];
   int tm, tn;
-  const int ntn = (int)ceil_div(g.N, GT);
-  if (g.tri) {
-    lower_tile(blockIdx.x, tm, tn);
-  } else {
-    tm = blockIdx.x / ntn;
-    tn = blockIdx.x % ntn;
-  }
+  const int ntm = (int)ceil_div(g.M, GT), ntn = (int)ceil_div(g.N, GT);
+  gemm_tile(blockIdx.x, gridDim.x, ntm, ntn, g.tri, g.kmode, tm, tn);
   const double* Ap = g.A + (int64_t)blockIdx.y * g.bsa;
   const double* Bp = g.B + (int64_t)blockIdx.y * g.bsb;
   double* Cp = g.C + (int64_t)blockIdx.y * g.bsc;
@@ -639,13 +660,8 @@ __global__ __launch_bounds__(256, 2) void gemm128_f64_kernel(GemmDesc g) {
     return BN ? Bs[buf][k * PK + n] : Bs[buf][n * PR + k];
   };
   int tm, tn;
-  const int ntn = (int)ceil_div(g.N, GT2);
-  if (g.tri) {
-    lower_tile(blockIdx.x, tm, tn);
-  } else {
-    tm = blockIdx.x / ntn;
-    tn = blockIdx.x % ntn;
-  }
+  const int ntm = (int)ceil_div(g.M, GT2), ntn = (int)ceil_div(g.N, GT2);
+  gemm_tile(blockIdx.x, gridDim.x, ntm, ntn, g.tri, g.kmode, tm, tn);
   const double* Ap = g.A + (int64_t)blockIdx.y * g.bsa;
   const double* Bp = g.B + (int64_t)blockIdx.y * g.bsb;
   double* Cp = g.C + (int64_t)blockIdx.y * g.bsc;
