@@ -14,14 +14,22 @@
 //     Hessians lose several digits.  fp64 MFMA (v_mfma_f64_16x16x4_f64)
 //     carries every O(d^3) product; the O(nb^3) panel work runs in LDS.
 //   * Blocked right-looking Cholesky with 64-wide panels: one workgroup
-//     factors the panel's diagonal block in LDS, one workgroup per 64-row
-//     block below solves against it, then one MFMA kernel applies the rank-64
-//     update to the lower triangle of the trailing matrix.
-//   * The triangular inverse uses recursive doubling: invert the 64x64
-//     diagonal blocks, then at each level combine neighbouring inverted
-//     blocks with X21 = -C^-1 (B A^-1), two batched MFMA launches per level.
+//     factors and inverts the panel's diagonal block (diag_factor), one
+//     workgroup per 64-row block below solves against it (a product with the
+//     inverse), then one MFMA kernel applies the rank-64 update to the lower
+//     triangle of the trailing matrix; its workgroup 0 updates the next
+//     diagonal block first and factors it while the others finish (lookahead
+//     of one panel).  Large matrices use two levels (see the host code).
+//   * The triangular inverse uses recursive doubling: the 64x64 diagonal
+//     blocks are inverted during the factorization, then each level combines
+//     neighbouring inverted blocks with X21 = -C^-1 (B A^-1), two batched MFMA
+//     launches per level.
 //   * L^-T L^-1 is one MFMA launch over the lower tiles, each tile with its
 //     own K range (the triangle of L^-1 makes the rest zero).
+//   * The products run on 64x64 or 128x128 fp64 MFMA tiles, chosen by size;
+//     tiles of triangular products are ordered longest first.
+//   * Only the lower triangle of A is ever read: the damped copy writes just
+//     that half.
 //   * A failed pivot (<= 0 or NaN) sets a device flag with atomicMin of its
 //     1-based index; the host reads it once at the end.
 #include <limits.h>
@@ -77,16 +85,17 @@ __global__ __launch_bounds__(256) void damp_lambda_kernel(const float* __restric
   }
 }
 
-// A = H + lambda I in fp64, both triangles taken from the lower triangle of H.
+// A = H + lambda I in fp64, lower triangle only (one workgroup per row; the
+// factorizations never read the upper triangle).
 __global__ __launch_bounds__(256) void damp_copy_kernel(const float* __restrict__ H, int d,
                                                         const double* lam, double* __restrict__ A) {
-  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (e >= (int64_t)d * d) return;
-  const int i = (int)(e / d), j = (int)(e % d);
-  const int r = i >= j ? i : j, c = i >= j ? j : i;
-  double v = (double)H[(int64_t)r * d + c];
-  if (i == j) v += *lam;
-  A[e] = v;
+  const int64_t i = blockIdx.x;
+  const double l = *lam;
+  for (int64_t j = threadIdx.x; j <= i; j += 256) {
+    double v = (double)H[i * d + j];
+    if (j == i) v += l;
+    A[i * d + j] = v;
+  }
 }
 
 // Row of the 16x16 fp64 MFMA result held in element i of lane `lane`
@@ -814,8 +823,7 @@ hipError_t launch_damp_to_f64(const float* H, int d, double percdamp, double* A,
   hipLaunchKernelGGL(damp_lambda_kernel, dim3(1), dim3(256), 0, s, H, d, percdamp, lam, flag);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int64_t n = (int64_t)d * d;
-  hipLaunchKernelGGL(damp_copy_kernel, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, s, H, d,
+  hipLaunchKernelGGL(damp_copy_kernel, dim3((unsigned)d), dim3(256), 0, s, H, d,
                      (const double*)lam, A);
   return hipGetLastError();
 }

@@ -439,14 +439,26 @@ __global__ __launch_bounds__(256) void convert_kernel(const T* __restrict__ W, i
     Wk[r * ldk + c] = (c < cols) ? (float)W[r * ldw + c] : 0.f;
 }
 
+// losses[c] = sum over parts p of lpart[p][c], in a fixed order: a workgroup
+// takes 16 columns; thread (s, c) sums parts s, s+16, ... and the 16 slices
+// are added in slice order.
 __global__ __launch_bounds__(256) void loss_reduce_kernel(const float* __restrict__ lpart,
                                                           int64_t nparts, int64_t ldk,
                                                           int64_t cols, float* __restrict__ out) {
-  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (c >= cols) return;
-  float s = 0.f;
-  for (int64_t p = 0; p < nparts; ++p) s += lpart[p * ldk + c];
-  out[c] = s;
+  __shared__ float part[16][17];
+  const int cl = threadIdx.x & 15, sl = threadIdx.x >> 4;
+  const int64_t c = (int64_t)blockIdx.x * 16 + cl;
+  float acc = 0.f;
+  if (c < cols)
+    for (int64_t p = sl; p < nparts; p += 16) acc += lpart[p * ldk + c];
+  part[sl][cl] = acc;
+  __syncthreads();
+  if (sl == 0 && c < cols) {
+    float tot = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) tot += part[i][cl];
+    out[c] = tot;
+  }
 }
 
 }  // namespace
@@ -502,7 +514,7 @@ hipError_t launch_lazy_update(float* Wk, int64_t ldk, int64_t rows, int64_t cols
 hipError_t launch_loss_reduce(const float* lpart, int64_t nparts, int64_t cols, float* losses,
                               hipStream_t s) {
   const int64_t ldk = round_up(cols, kBlock);
-  hipLaunchKernelGGL(loss_reduce_kernel, dim3((unsigned)ceil_div(cols, 256)), dim3(256), 0, s,
+  hipLaunchKernelGGL(loss_reduce_kernel, dim3((unsigned)ceil_div(cols, 16)), dim3(256), 0, s,
                      lpart, nparts, ldk, cols, losses);
   return hipGetLastError();
 }
