@@ -308,10 +308,12 @@ __global__ __launch_bounds__(256, 2) void lazy_kernel(float* __restrict__ Wk, in
                                                    int c0, int c1, const float* __restrict__ Err,
                                                    const float* __restrict__ Hinv) {
   constexpr int TM = 32 * MT;      // rows per workgroup tile
-  constexpr int PM = TM + 16;
+  constexpr int PA = LK + 4;       // A is m-major: a row of 32 k at pitch 36 floats, so
+                                   // float4 stores and the operand reads (16 rows x 4 k)
+                                   // hit distinct banks
   constexpr int AV = TM * LK / 4 / 256;  // float4 A loads per thread
-  __shared__ float As[2][LK][PM];  // [k][m]
-  __shared__ float Bs[2][LK][LP];  // [k][n]
+  __shared__ __attribute__((aligned(16))) float As[2][TM * PA];  // [m][k]
+  __shared__ __attribute__((aligned(16))) float Bs[2][LK][LP];   // [k][n]
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
@@ -358,10 +360,12 @@ __global__ __launch_bounds__(256, 2) void lazy_kernel(float* __restrict__ Wk, in
       const int e = tid + 256 * q;
       const int m = e >> 3, kk = (e & 7) * 4;
       const int gk = kc + kk;
-      As[buf][kk + 0][m] = (gk + 0 < K) ? av[q].x : 0.f;
-      As[buf][kk + 1][m] = (gk + 1 < K) ? av[q].y : 0.f;
-      As[buf][kk + 2][m] = (gk + 2 < K) ? av[q].z : 0.f;
-      As[buf][kk + 3][m] = (gk + 3 < K) ? av[q].w : 0.f;
+      float4 v = av[q];
+      v.x = (gk + 0 < K) ? v.x : 0.f;
+      v.y = (gk + 1 < K) ? v.y : 0.f;
+      v.z = (gk + 2 < K) ? v.z : 0.f;
+      v.w = (gk + 3 < K) ? v.w : 0.f;
+      *reinterpret_cast<float4*>(&As[buf][m * PA + kk]) = v;
     }
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -396,7 +400,7 @@ __global__ __launch_bounds__(256, 2) void lazy_kernel(float* __restrict__ Wk, in
       const int kr = ks + (lane >> 4);
       float af[MT], bf[4];
 #pragma unroll
-      for (int a = 0; a < MT; ++a) af[a] = As[buf][kr][16 * MT * wm + 16 * a + (lane & 15)];
+      for (int a = 0; a < MT; ++a) af[a] = As[buf][(16 * MT * wm + 16 * a + (lane & 15)) * PA + kr];
 #pragma unroll
       for (int b = 0; b < 4; ++b) bf[b] = Bs[buf][kr][64 * wn + 16 * b + (lane & 15)];
 #pragma unroll
