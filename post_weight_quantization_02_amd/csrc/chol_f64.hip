@@ -161,10 +161,17 @@ __device__ __attribute__((always_inline)) inline void factor16(double (&a)[16], 
 // LDS of the diagonal-block factorization; the trailing update reuses S and
 // Xs as its two panel tiles.
 struct DiagLds {
-  double S[NB][PP];      // A, then L (lower triangle)
+  double S[NB][PP];      // A (lower); L_IJ of the off-diagonal blocks, transposed, in the upper half
   double Xs[NB][PP];     // L^-1 (lower triangle)
-  double Wx[4][16][17];  // per-wave copy of X_JJ for the MFMA operand
+  double Ld[4][16][17];  // the four 16x16 diagonal blocks of L
 };
+
+// Element (m, 4s + kq) of a 16x16 block whose row m this lane holds in r[]
+// (lane = m + 16 kq): the MFMA A-operand of k-step s.
+__device__ inline double row_operand(const double (&r)[16], int s4, int kq) {
+  const double v0 = r[4 * s4], v1 = r[4 * s4 + 1], v2 = r[4 * s4 + 2], v3 = r[4 * s4 + 3];
+  return kq == 0 ? v0 : (kq == 1 ? v1 : (kq == 2 ? v2 : v3));
+}
 
 // Factor the 64x64 block in sh.S (lower triangle; rows past the matrix are
 // identity) and invert the factor: L goes to the lower triangle of the block
@@ -172,12 +179,14 @@ struct DiagLds {
 // and a barrier must separate its clearing and the filling of sh.S from the
 // call.
 //
-// The block is split into 4x4 sub-blocks of 16.  For each block column J:
-// every wave factors and inverts the 16x16 diagonal sub-block on its own
-// (factor16, no barrier), wave I > J forms L_IJ = A_IJ X_JJ^T, and after one
-// barrier applies A_IK -= L_IJ L_KJ^T for J < K <= I; all 16x16 products are
-// v_mfma_f64_16x16x4f64.  Finally wave J forms the inverse blocks of column
-// J, X_IJ = -X_II sum_{K=J..I-1} L_IK X_KJ.
+// Four phases J, one per 16-column block, one barrier each.  Every wave
+// factors and inverts the 16x16 diagonal block A_JJ on its own (factor16).
+// Wave I > J then forms the blocks L_KJ = A_KJ X_JJ^T it needs (K = J+1..I)
+// as the transposed product X_JJ A_KJ^T, which leaves them in the MFMA
+// operand layout, and updates its own row blocks A_IK -= L_IJ L_KJ^T; it
+// parks L_IJ, transposed, in the unused upper half of S.  Meanwhile wave
+// J' < J forms the inverse block X_JJ' = -X_JJ sum_{K=J'..J-1} L_JK X_KJ'
+// of its block column.  All 16x16 products are v_mfma_f64_16x16x4f64.
 __device__ __attribute__((always_inline)) inline void diag_factor(DiagLds& sh, double* __restrict__ A, int lda, int k, int kb,
                                    int* flag, int info_offset, double* __restrict__ Xd,
                                    int ldxd) {
@@ -194,90 +203,73 @@ __device__ __attribute__((always_inline)) inline void diag_factor(DiagLds& sh, d
 #pragma unroll
     for (int l = 0; l < 16; ++l) a[l] = (l <= m) ? S[r0 + m][r0 + l] : S[r0 + l][r0 + m];
     factor16(a, y, m, flag, info_offset + k + r0, wave == 0);
-    if (lane < 16) {
+    if (wave == J && lane < 16) {
 #pragma unroll
-      for (int l = 0; l < 16; ++l) sh.Wx[wave][m][l] = y[l];
-      if (wave == J) {
-#pragma unroll
-        for (int l = 0; l < 16; ++l) {
-          S[r0 + m][r0 + l] = a[l];
-          Xs[r0 + m][r0 + l] = y[l];
-        }
+      for (int l = 0; l < 16; ++l) {
+        sh.Ld[J][m][l] = a[l];
+        Xs[r0 + m][r0 + l] = y[l];
       }
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    if (wave > J) {
-      // L_IJ = A_IJ X_JJ^T, I = wave
-      f64x4 acc = {0.0, 0.0, 0.0, 0.0};
+    double xop[4];  // X_JJ as the A operand of the four k-steps
 #pragma unroll
-      for (int s4 = 0; s4 < 4; ++s4) {
-        const int kk = 4 * s4 + kq;
-        acc = __builtin_amdgcn_mfma_f64_16x16x4f64(S[16 * wave + m][r0 + kk], sh.Wx[wave][m][kk],
-                                                   acc, 0, 0, 0);
-      }
-#pragma unroll
-      for (int q = 0; q < 4; ++q) S[16 * wave + mfma64_row(lane, q)][r0 + m] = acc[q];
-    }
-    __syncthreads();
+    for (int s4 = 0; s4 < 4; ++s4) xop[s4] = row_operand(y, s4, kq);
     if (wave > J) {
-      // A_IK -= L_IJ L_KJ^T for J < K <= I
+      // L_KJ^T = X_JJ A_KJ^T: lane (m, kq) gets L_KJ[m][kq + 4i] in element i
+      auto l_block = [&](int K) {
+        f64x4 t = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4)
+          t = __builtin_amdgcn_mfma_f64_16x16x4f64(xop[s4], S[16 * K + m][r0 + 4 * s4 + kq], t, 0,
+                                                  0, 0);
+        return t;
+      };
+      const f64x4 li = l_block(wave);
 #pragma unroll 1
       for (int K = J + 1; K <= wave; ++K) {
-        f64x4 acc;
+        const f64x4 lk = (K == wave) ? li : l_block(K);
+        f64x4 c;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) acc[q] = S[16 * wave + mfma64_row(lane, q)][16 * K + m];
+        for (int q = 0; q < 4; ++q) c[q] = S[16 * wave + mfma64_row(lane, q)][16 * K + m];
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4)
+          c = __builtin_amdgcn_mfma_f64_16x16x4f64(-li[s4], lk[s4], c, 0, 0, 0);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) S[16 * wave + mfma64_row(lane, q)][16 * K + m] = c[q];
+      }
+      // L_IJ[m][kq + 4i] parked at S[r0 + kq + 4i][16 I + m] (upper half)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) S[r0 + kq + 4 * i][16 * wave + m] = li[i];
+    } else if (wave < J) {
+      // X_{J,J'} = -X_JJ T, T = sum_{K=J'..J-1} L_JK X_KJ', J' = wave
+      const int Jp = wave;
+      f64x4 t = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll 1
+      for (int K = Jp; K < J; ++K) {
 #pragma unroll
         for (int s4 = 0; s4 < 4; ++s4) {
           const int kk = 4 * s4 + kq;
-          acc = __builtin_amdgcn_mfma_f64_16x16x4f64(-S[16 * wave + m][r0 + kk],
-                                                     S[16 * K + m][r0 + kk], acc, 0, 0, 0);
+          t = __builtin_amdgcn_mfma_f64_16x16x4f64(S[16 * K + kk][r0 + m], Xs[16 * K + kk][16 * Jp + m],
+                                                  t, 0, 0, 0);
         }
-#pragma unroll
-        for (int q = 0; q < 4; ++q) S[16 * wave + mfma64_row(lane, q)][16 * K + m] = acc[q];
       }
+      f64x4 x = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4)
+        x = __builtin_amdgcn_mfma_f64_16x16x4f64(-xop[s4], t[s4], x, 0, 0, 0);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) Xs[r0 + mfma64_row(lane, q)][16 * Jp + m] = x[q];
     }
     __syncthreads();
   }
-
-  // off-diagonal blocks of L^-1: wave J owns block column J
-  if (wave < 3) {
-    const int J = wave;
-#pragma unroll 1
-    for (int I = J + 1; I < 4; ++I) {
-      f64x4 t = {0.0, 0.0, 0.0, 0.0};
-#pragma unroll 1
-      for (int K = J; K < I; ++K) {
-#pragma unroll
-        for (int s4 = 0; s4 < 4; ++s4) {
-          const int kk = 4 * s4 + kq;
-          t = __builtin_amdgcn_mfma_f64_16x16x4f64(S[16 * I + m][16 * K + kk],
-                                                   Xs[16 * K + kk][16 * J + m], t, 0, 0, 0);
-        }
-      }
-      // X_IJ = -X_II T; the D layout of T (rows kq + 4q) is the B layout of step q
-      f64x4 x = {0.0, 0.0, 0.0, 0.0};
-#pragma unroll
-      for (int s4 = 0; s4 < 4; ++s4) {
-        const int kk = 4 * s4 + kq;
-        x = __builtin_amdgcn_mfma_f64_16x16x4f64(-Xs[16 * I + m][16 * I + kk], t[s4], x, 0, 0, 0);
-      }
-#pragma unroll
-      for (int q = 0; q < 4; ++q) Xs[16 * I + mfma64_row(lane, q)][16 * J + m] = x[q];
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    }
-  }
-  __syncthreads();
 
 #pragma unroll
   for (int q = 0; q < 16; ++q) {
     const int e = tid + 256 * q;
     const int i = e >> 6, l = e & 63;
     if (i < kb && l < kb) {
-      if (l <= i) A[(int64_t)(k + i) * lda + k + l] = S[i][l];
+      if (l <= i)
+        A[(int64_t)(k + i) * lda + k + l] = ((i >> 4) == (l >> 4)) ? sh.Ld[i >> 4][i & 15][l & 15]
+                                                                   : S[l][i];
       Xd[(int64_t)i * ldxd + l] = (l <= i) ? Xs[i][l] : 0.0;
     }
   }

@@ -355,7 +355,9 @@ __global__ __launch_bounds__(256, 1) void syrk_fast_kernel(const _Float16* __res
 }
 
 // Sum the split partials of one 64x64 sub-block of a lower tile in split
-// order, add alpha * sum into H, and mirror into the upper triangle.
+// order, in fp64 (one rounding to fp32 per element), add alpha * sum into H,
+// and mirror into the upper triangle.  Each thread reads float4 runs of four
+// columns.
 __global__ __launch_bounds__(256) void syrk_reduce_kernel(const float* __restrict__ P, int d,
                                                           int splits, int ntiles, float alpha,
                                                           float* __restrict__ H) {
@@ -368,23 +370,36 @@ __global__ __launch_bounds__(256) void syrk_reduce_kernel(const float* __restric
   lower_tile(tile, bi, bj);
   if (bi == bj && qr < qc) return;  // strictly upper sub-block of a diagonal tile
   const int tid = threadIdx.x;
-  const int cx = tid & 63;
-  const int ry = tid >> 6;
   const int gr0 = bi * T + 64 * qr;
   const int gc0 = bj * T + 64 * qc;
   if (gr0 >= d || gc0 >= d) return;
   const bool on_diag = (bi == bj && qr == qc);
-  for (int rr = ry; rr < 64; rr += 4) {
-    const int lr = 64 * qr + rr, lc = 64 * qc + cx;
-    float v = 0.f;
-    for (int s = 0; s < splits; ++s)
-      v += P[((int64_t)s * ntiles + tile) * ((int64_t)T * T) + (int64_t)lr * T + lc];
-    v *= alpha;
-    st[rr][cx] = v;
-    const int gr = gr0 + rr, gc = gc0 + cx;
-    if (gr < d && gc < d && (!on_diag || gc <= gr)) H[(int64_t)gr * d + gc] += v;
+  const int c4 = (tid & 15) * 4;
+  const int64_t stride = (int64_t)ntiles * T * T;
+#pragma unroll 1
+  for (int pass = 0; pass < 4; ++pass) {
+    const int rr = 16 * pass + (tid >> 4);
+    const float* src = P + (int64_t)tile * T * T + (int64_t)(64 * qr + rr) * T + 64 * qc + c4;
+    double v0 = 0.0, v1 = 0.0, v2 = 0.0, v3 = 0.0;
+    for (int sp = 0; sp < splits; ++sp) {
+      const float4 p = *reinterpret_cast<const float4*>(src + sp * stride);
+      v0 += (double)p.x;
+      v1 += (double)p.y;
+      v2 += (double)p.z;
+      v3 += (double)p.w;
+    }
+    const float o[4] = {(float)((double)alpha * v0), (float)((double)alpha * v1),
+                        (float)((double)alpha * v2), (float)((double)alpha * v3)};
+    const int gr = gr0 + rr;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      st[rr][c4 + u] = o[u];
+      const int gc = gc0 + c4 + u;
+      if (gr < d && gc < d && (!on_diag || gc <= gr)) H[(int64_t)gr * d + gc] += o[u];
+    }
   }
   __syncthreads();
+  const int cx = tid & 63, ry = tid >> 6;
   for (int rr = ry; rr < 64; rr += 4) {
     const int gr = gr0 + cx;  // source row (lower)
     const int gc = gc0 + rr;  // source column
@@ -398,15 +413,22 @@ __global__ __launch_bounds__(256) void syrk_reduce_kernel(const float* __restric
 int syrk_splits(int64_t d, int64_t n) {
   // One 256x256 workgroup runs per CU at a time.  Pick the split count that
   // minimises (rounds of 256 workgroups) x (time of one split) plus the time
-  // to write and re-read the fp32 partial tiles.
+  // to write and re-read the fp32 partial tiles, with at most kMaxSplitChunks
+  // chunks (8192 tokens) per split: a partial sums its products in fp32, and
+  // shorter runs keep H within about 1e-7 of the exact sum.
   const int64_t nb = ceil_div(d, T);
   const int64_t tiles = nb * (nb + 1) / 2;
   const int64_t chunks = ceil_div(n, KC);
   const double t_tile = 2.0 * T * T * (double)(chunks * KC) / (4.0 * 1024.0 * 2.4e9);
   const double t_part = (double)T * T * 4.0 * 2.0 / 6.0e12;
-  int64_t best = 1;
+  constexpr int64_t kMaxSplitChunks = 256;
+  constexpr int64_t kMaxSplits = 128;
+  int64_t lo = ceil_div(chunks, kMaxSplitChunks);
+  if (lo < 1) lo = 1;
+  if (lo > kMaxSplits) lo = kMaxSplits;
+  int64_t best = lo;
   double best_cost = 1e30;
-  for (int64_t s = 1; s <= 64 && s <= chunks; ++s) {
+  for (int64_t s = lo; s <= kMaxSplits && s <= chunks; ++s) {
     const double rounds = (double)ceil_div(tiles * s, 256);
     const double cost = rounds * t_tile / (double)s + (double)(s * tiles) * t_part;
     if (cost < best_cost) {
