@@ -110,169 +110,291 @@ __device__ inline double row_bcast(double v) {
   return __builtin_amdgcn_update_dpp(0.0, v, 0x150 + J, 0xF, 0xF, true);
 }
 
-// Step J of the in-wave 16x16 Cholesky and inverse (see factor16).
+// ---- 16x16 blocks in registers ("CS layout")
+// Lane (m, g) = (lane % 16, lane / 16) holds B[m][g + 4i] in element i of a
+// double[4]: row m of the block, every fourth column.  This is the layout in
+// which v_mfma_f64_16x16x4f64 returns a product (its element i at lane
+// (n, q) is D[q + 4i][n], i.e. row n of D^T), and element s is also the
+// operand of k-step s when K = 16 runs as k = g + 4s.  So, for blocks in this
+// layout, MFMA(A = P[s], B = Q[s]) accumulates (Q P^T) into a block held in
+// this layout, and every product below stays in it.
+
+// Value of v at lane L of the wave (uniform).
+template <int L>
+__device__ inline double lane_value(double v) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)u, L);
+  const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(u >> 32), L);
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+// Value of v at lane addr / 4 (ds_bpermute: the LDS crossbar, no LDS memory).
+__device__ inline double lane_gather(double v, int addr) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = __builtin_amdgcn_ds_bpermute(addr, (int)(uint32_t)u);
+  const uint32_t hi = __builtin_amdgcn_ds_bpermute(addr, (int)(uint32_t)(u >> 32));
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+// Step J of the in-wave 16x16 Cholesky and inverse (see factor16).  gaddr[q]
+// is the byte address of lane (m, q) for ds_bpermute.
 template <int J>
-__device__ inline void factor16_step(double (&a)[16], double (&y)[16], double& ysc, int i,
-                                     int* flag, int info_base, bool report) {
-  const double p = row_bcast<J>(a[J]);
-  if (report && (threadIdx.x & 63) == 0 && !(p > 0.0)) atomicMin(flag, info_base + J + 1);
+__device__ inline void factor16_step(double (&a)[4], double (&y)[4], double& ysc, int& bad,
+                                     int m, int g, const int (&gaddr)[4]) {
+  constexpr int QJ = J & 3, IJ = J >> 2;
+  const double c = lane_gather(a[IJ], gaddr[QJ]);    // A[m][J], from lane group QJ
+  const double p = lane_value<J + 16 * QJ>(a[IJ]);   // pivot A[J][J]
+  bad = (p > 0.0) ? bad : min(bad, J);
   const double rs = rsqrt_f64(p);
-  const double cij = a[J];
-  const double t = (i > J) ? cij * (rs * rs) : 0.0;
+  const double r2 = (m > J) ? rs * rs : 0.0;
+  const double t = c * r2;                            // multiplier of row J for rows below it
+  // rows below J: the columns past J get the right-looking update with row J
 #pragma unroll
-  for (int l = J + 1; l < 16; ++l) a[l] = __builtin_fma(-t, row_bcast<J>(a[l]), a[l]);
-  const double lij = cij * rs;
-  const double coef = (i > J) ? -lij * rs : 0.0;
+  for (int i = IJ; i < 4; ++i) {
+    if (i == IJ && QJ == 3) continue;                 // element IJ holds no column past J
+    double b = row_bcast<J>(a[i]);                    // A[J][g + 4i]
+    if (i == IJ) b = (g > QJ) ? b : 0.0;
+    a[i] = __builtin_fma(-t, b, a[i]);
+  }
+  if (g == QJ) a[IJ] = c * rs;                        // column J of L (L[J][J] = p / sqrt(p))
+  // forward substitution L Y = I: rows below J lose t times row J of Y
 #pragma unroll
-  for (int l = 0; l <= J; ++l) y[l] = __builtin_fma(coef, row_bcast<J>(y[l]), y[l]);
-  if (i == J) ysc = rs;
-  a[J] = (i > J) ? lij : ((i == J) ? p * rs : 0.0);
-  __builtin_amdgcn_sched_barrier(0);  // keep steps apart: bounded register pressure
+  for (int i = 0; i <= IJ; ++i) y[i] = __builtin_fma(-t, row_bcast<J>(y[i]), y[i]);
+  if (m == J) ysc = rs;
 }
 
 template <int... J>
-__device__ inline void factor16_steps(double (&a)[16], double (&y)[16], double& ysc, int i,
-                                      int* flag, int info_base, bool report,
+__device__ inline void factor16_steps(double (&a)[4], double (&y)[4], double& ysc, int& bad, int m,
+                                      int g, const int (&gaddr)[4],
                                       std::integer_sequence<int, J...>) {
-  (factor16_step<J>(a, y, ysc, i, flag, info_base, report), ...);
+  (factor16_step<J>(a, y, ysc, bad, m, g, gaddr), ...);
 }
 
 // Cholesky factor and inverse of one symmetric 16x16 block held by a single
-// wave, with no barrier: lane i (and its copies i+16, i+32, i+48, one per row
-// of 16 lanes) keeps row i of the block in a[] and row i of Y in y[] (Y
-// starts as I).  Step j takes the pivot and row j from lane j of the row
-// (DPP broadcast), applies the unscaled right-looking update
-// a[i][l] -= (a[i][j] / p) a[j][l], and the forward substitution of L Y = I:
-// Y[i][:] -= L[i][j] X[j][:] below row j, with X[j][:] = Y[j][:] / L[j][j]
-// (row j itself is scaled once at the end).  On return a[] holds row i of L
-// and y[] row i of L^-1 (zeros above the diagonal in both).  Pivots that are
-// not > 0 (or NaN) are reported through atomicMin(flag, info_base + j + 1)
-// by lane 0 when `report` is set.
-__device__ __attribute__((always_inline)) inline void factor16(double (&a)[16], double (&y)[16], int i, int* flag, int info_base,
-                                bool report) {
+// wave in CS layout, with no barrier and no LDS memory.  Step j reads the
+// pivot with a readlane, column j of the block from its lane group
+// (ds_bpermute) and row j from lane j of each group (DPP row_newbcast),
+// applies the right-looking update a[i][l] -= (a[i][j] / p) a[j][l] to the
+// columns past j, and the forward substitution of L Y = I: rows below j lose
+// (L[i][j] / L[j][j]) times row j of Y, which is scaled by 1 / L[j][j] at the
+// end.  On return a[] holds L (entries above the diagonal are meaningless)
+// and y[] holds L^-1 (exact zeros above the diagonal).  The first pivot that
+// is not > 0 (or NaN) is reported through atomicMin(flag, info_base + j + 1)
+// when `report` is set.
+__device__ __attribute__((always_inline)) inline void factor16(double (&a)[4], double (&y)[4],
+                                                               int m, int g, int* flag,
+                                                               int info_base, bool report) {
 #pragma unroll
-  for (int l = 0; l < 16; ++l) y[l] = (l == i) ? 1.0 : 0.0;
+  for (int i = 0; i < 4; ++i) y[i] = (g + 4 * i == m) ? 1.0 : 0.0;
   double ysc = 1.0;
-  factor16_steps(a, y, ysc, i, flag, info_base, report, std::make_integer_sequence<int, 16>{});
+  int bad = 16;
+  int gaddr[4];
 #pragma unroll
-  for (int l = 0; l < 16; ++l) y[l] *= ysc;
+  for (int q = 0; q < 4; ++q) gaddr[q] = (m + 16 * q) * 4;
+  factor16_steps(a, y, ysc, bad, m, g, gaddr, std::make_integer_sequence<int, 16>{});
+#pragma unroll
+  for (int i = 0; i < 4; ++i) y[i] *= ysc;
+  if (report && bad < 16 && (threadIdx.x & 63) == 0) atomicMin(flag, info_base + bad + 1);
 }
 
 // LDS of the diagonal-block factorization; the trailing update reuses S and
 // Xs as its two panel tiles.
 struct DiagLds {
-  double S[NB][PP];      // A (lower); L_IJ of the off-diagonal blocks, transposed, in the upper half
-  double Xs[NB][PP];     // L^-1 (lower triangle)
-  double Ld[4][16][17];  // the four 16x16 diagonal blocks of L
+  double S[NB][PP];   // the block (lower triangle); blocks L_IJ below the diagonal as they form
+  double Xs[NB][PP];  // blocks of L^-1 on and below the diagonal, row-major
 };
 
-// Element (m, 4s + kq) of a 16x16 block whose row m this lane holds in r[]
-// (lane = m + 16 kq): the MFMA A-operand of k-step s.
-__device__ inline double row_operand(const double (&r)[16], int s4, int kq) {
-  const double v0 = r[4 * s4], v1 = r[4 * s4 + 1], v2 = r[4 * s4 + 2], v3 = r[4 * s4 + 3];
-  return kq == 0 ? v0 : (kq == 1 ? v1 : (kq == 2 ? v2 : v3));
+// Block (I, K) of a row-major LDS tile in CS layout.  With SYM, a diagonal
+// block is read from its lower triangle (the tile holds a symmetric matrix).
+template <bool SYM>
+__device__ inline void load_cs(const double (*S)[PP], int I, int K, int m, int g, double (&v)[4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int c = g + 4 * i;
+    const bool up = SYM && (I == K) && (c > m);
+    v[i] = up ? S[16 * I + c][16 * K + m] : S[16 * I + m][16 * K + c];
+  }
 }
 
-// Factor the 64x64 block in sh.S (lower triangle; rows past the matrix are
-// identity) and invert the factor: L goes to the lower triangle of the block
-// at A[k.., k..], L^-1 (zeros above its diagonal) to Xd.  sh.Xs must be zero
-// and a barrier must separate its clearing and the filling of sh.S from the
-// call.
+__device__ inline void store_cs(double (*S)[PP], int I, int K, int m, int g, const double (&v)[4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) S[16 * I + m][16 * K + g + 4 * i] = v[i];
+}
+
+// L_IJ = A_IJ X_JJ^T from X_JJ and A_IJ in CS layout.
+__device__ inline void l_block(const double (&x)[4], const double (&aij)[4], double (&l)[4]) {
+  f64x4 t = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+  for (int s = 0; s < 4; ++s) t = __builtin_amdgcn_mfma_f64_16x16x4f64(x[s], aij[s], t, 0, 0, 0);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) l[i] = t[i];
+}
+
+// A_IK -= L_IJ L_KJ^T, all in CS layout.
+__device__ inline void rank16_update(double (&aik)[4], const double (&lij)[4],
+                                     const double (&lkj)[4]) {
+  f64x4 c = {aik[0], aik[1], aik[2], aik[3]};
+#pragma unroll
+  for (int s = 0; s < 4; ++s) c = __builtin_amdgcn_mfma_f64_16x16x4f64(-lkj[s], lij[s], c, 0, 0, 0);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) aik[i] = c[i];
+}
+
+// T += L_JK X_KJ' with L_JK in CS layout (from S) and X_KJ' as the B operand
+// (from Xs); T comes back in MFMA result layout (element i at lane (m, g) is
+// T[g + 4i][m]), which is the B operand of the product with X_JJ that follows.
+__device__ inline void t_accum(const double (*S)[PP], const double (*Xs)[PP], int J, int K, int Jp,
+                               int m, int g, f64x4& t) {
+  double l[4];
+  load_cs<false>(S, J, K, m, g, l);
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+    t = __builtin_amdgcn_mfma_f64_16x16x4f64(l[s], Xs[16 * K + g + 4 * s][16 * Jp + m], t, 0, 0, 0);
+}
+
+// X_JJ' = -X_JJ T, to Xs and to global Xd (rows and columns below kb).
+__device__ inline void x_block(double (*Xs)[PP], int J, int Jp, int m, int g, const f64x4& t,
+                               double* __restrict__ Xd, int ldxd, int kb) {
+  double x[4];
+  load_cs<false>(Xs, J, J, m, g, x);
+  f64x4 r = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+  for (int s = 0; s < 4; ++s) r = __builtin_amdgcn_mfma_f64_16x16x4f64(-x[s], t[s], r, 0, 0, 0);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = 16 * J + g + 4 * i, col = 16 * Jp + m;
+    Xs[row][col] = r[i];
+    if (row < kb && col < kb) Xd[(int64_t)row * ldxd + col] = r[i];
+  }
+}
+
+// Global store of block (I, K) in CS layout, rows and columns below kb (and
+// on or below the diagonal with LOWER).
+template <bool LOWER>
+__device__ inline void store_block_global(double* __restrict__ G, int64_t ld, int I, int K, int m,
+                                          int g, const double (&v)[4], int kb) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = 16 * I + m, col = 16 * K + g + 4 * i;
+    if (row < kb && col < kb && (!LOWER || col <= row)) G[(int64_t)row * ld + col] = v[i];
+  }
+}
+
+struct DiagCtx {
+  double (*S)[PP];
+  double (*Xs)[PP];
+  double* Ak;   // A[k.., k..]
+  int lda;
+  double* Xd;
+  int ldxd;
+  int kb, w, m, g;
+  int* flag;
+  int info_base;  // info_offset + k
+};
+
+// Phase J of diag_factor (see there).
+template <int J>
+__device__ __attribute__((always_inline)) inline void diag_phase(const DiagCtx& cx,
+                                                                 double (&row)[4][4], f64x4& tsum) {
+  const int w = cx.w, m = cx.m, g = cx.g;
+  if (w == J) {
+    double y[4];
+    factor16(row[J], y, m, g, cx.flag, cx.info_base + 16 * J, true);
+    store_cs(cx.Xs, J, J, m, g, y);
+    store_block_global<true>(cx.Ak, cx.lda, J, J, m, g, row[J], cx.kb);
+    store_block_global<false>(cx.Xd, cx.ldxd, J, J, m, g, y, cx.kb);
+  }
+  __syncthreads();  // X_JJ published
+  if (w > J) {
+    double x[4], l[4];
+    load_cs<false>(cx.Xs, J, J, m, g, x);
+    l_block(x, row[J], l);
+    store_cs(cx.S, w, J, m, g, l);
+    store_block_global<false>(cx.Ak, cx.lda, w, J, m, g, l, cx.kb);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) row[J][i] = l[i];
+    if constexpr (J + 1 < 4) {
+      if (w == J + 1) rank16_update(row[J + 1], l, l);
+    }
+  } else if (w < J) {
+    x_block(cx.Xs, J, w, m, g, tsum, cx.Xd, cx.ldxd, cx.kb);
+  }
+  if constexpr (J < 3) {
+    __syncthreads();  // L_wJ published
+    if (w > J + 1) {
+      // the rest of this wave's row: A_wK -= L_wJ L_KJ^T, K = J+1..w
+#pragma unroll
+      for (int K = J + 1; K < 4; ++K) {
+        if (K < w) {
+          double lk[4];
+          load_cs<false>(cx.S, K, J, m, g, lk);
+          rank16_update(row[K], row[J], lk);
+        } else if (K == w) {
+          rank16_update(row[K], row[J], row[J]);
+        }
+      }
+    } else if (w <= J) {
+      // sum for X_{J+1, w}: L_{J+1,K} X_{K,w}, K = w..J
+      tsum = f64x4{0.0, 0.0, 0.0, 0.0};
+      for (int K = w; K <= J; ++K) t_accum(cx.S, cx.Xs, J + 1, K, w, m, g, tsum);
+    }
+  }
+}
+
+// Factor the 64x64 block in sh.S (lower triangle; rows past kb are identity)
+// and invert the factor: L goes to the lower triangle of the block at
+// A[k.., k..], L^-1 (zeros above its diagonal) to Xd.  A barrier must
+// separate the filling of sh.S from the call.
 //
-// Four phases J, one per 16-column block, one barrier each.  Every wave
-// factors and inverts the 16x16 diagonal block A_JJ on its own (factor16).
-// Wave I > J then forms the blocks L_KJ = A_KJ X_JJ^T it needs (K = J+1..I)
-// as the transposed product X_JJ A_KJ^T, which leaves them in the MFMA
-// operand layout, and updates its own row blocks A_IK -= L_IJ L_KJ^T; it
-// parks L_IJ, transposed, in the unused upper half of S.  Meanwhile wave
-// J' < J forms the inverse block X_JJ' = -X_JJ sum_{K=J'..J-1} L_JK X_KJ'
-// of its block column.  All 16x16 products are v_mfma_f64_16x16x4f64.
+// Wave w owns block row w of the tile and keeps its blocks A_w0..A_ww in
+// registers (CS layout).  Phase J: wave J factors and inverts A_JJ on its
+// own (factor16) and publishes X_JJ; each wave w > J then forms
+// L_wJ = A_wJ X_JJ^T and publishes it, and wave J+1 updates A_{J+1,J+1} with
+// its own L_{J+1,J} and goes straight on to the next factorization while the
+// others apply the remaining rank-16 updates of their rows.  The waves whose
+// rows are done build the blocks of L^-1 below the diagonal,
+// X_JJ' = -X_JJ sum_{K=J'..J-1} L_JK X_KJ', one block column each: the sum
+// before X_JJ is ready, the last product after.  Every block goes to global
+// memory as soon as it is final.  All 16x16 products are
+// v_mfma_f64_16x16x4f64.
 __device__ __attribute__((always_inline)) inline void diag_factor(DiagLds& sh, double* __restrict__ A, int lda, int k, int kb,
                                    int* flag, int info_offset, double* __restrict__ Xd,
                                    int ldxd) {
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int m = lane & 15, kq = lane >> 4;
-  double (*S)[PP] = sh.S;
-  double (*Xs)[PP] = sh.Xs;
+  const int lane = tid & 63;
+  DiagCtx cx;
+  cx.S = sh.S;
+  cx.Xs = sh.Xs;
+  cx.Ak = A + (int64_t)k * lda + k;
+  cx.lda = lda;
+  cx.Xd = Xd;
+  cx.ldxd = ldxd;
+  cx.kb = kb;
+  cx.w = tid >> 6;
+  cx.m = lane & 15;
+  cx.g = lane >> 4;
+  cx.flag = flag;
+  cx.info_base = info_offset + k;
 
-#pragma unroll 1
-  for (int J = 0; J < 4; ++J) {
-    const int r0 = 16 * J;
-    double a[16], y[16];
+  // this wave's block row A_w0 .. A_ww
+  double row[4][4];
 #pragma unroll
-    for (int l = 0; l < 16; ++l) a[l] = (l <= m) ? S[r0 + m][r0 + l] : S[r0 + l][r0 + m];
-    factor16(a, y, m, flag, info_offset + k + r0, wave == 0);
-    if (wave == J && lane < 16) {
+  for (int K = 0; K < 4; ++K)
+    if (K <= cx.w) load_cs<true>(sh.S, cx.w, K, cx.m, cx.g, row[K]);
+  // the blocks of Xd above the block diagonal are zero
 #pragma unroll
-      for (int l = 0; l < 16; ++l) {
-        sh.Ld[J][m][l] = a[l];
-        Xs[r0 + m][r0 + l] = y[l];
-      }
-    }
-    double xop[4];  // X_JJ as the A operand of the four k-steps
-#pragma unroll
-    for (int s4 = 0; s4 < 4; ++s4) xop[s4] = row_operand(y, s4, kq);
-    if (wave > J) {
-      // L_KJ^T = X_JJ A_KJ^T: lane (m, kq) gets L_KJ[m][kq + 4i] in element i
-      auto l_block = [&](int K) {
-        f64x4 t = {0.0, 0.0, 0.0, 0.0};
-#pragma unroll
-        for (int s4 = 0; s4 < 4; ++s4)
-          t = __builtin_amdgcn_mfma_f64_16x16x4f64(xop[s4], S[16 * K + m][r0 + 4 * s4 + kq], t, 0,
-                                                  0, 0);
-        return t;
-      };
-      const f64x4 li = l_block(wave);
-#pragma unroll 1
-      for (int K = J + 1; K <= wave; ++K) {
-        const f64x4 lk = (K == wave) ? li : l_block(K);
-        f64x4 c;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) c[q] = S[16 * wave + mfma64_row(lane, q)][16 * K + m];
-#pragma unroll
-        for (int s4 = 0; s4 < 4; ++s4)
-          c = __builtin_amdgcn_mfma_f64_16x16x4f64(-li[s4], lk[s4], c, 0, 0, 0);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) S[16 * wave + mfma64_row(lane, q)][16 * K + m] = c[q];
-      }
-      // L_IJ[m][kq + 4i] parked at S[r0 + kq + 4i][16 I + m] (upper half)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) S[r0 + kq + 4 * i][16 * wave + m] = li[i];
-    } else if (wave < J) {
-      // X_{J,J'} = -X_JJ T, T = sum_{K=J'..J-1} L_JK X_KJ', J' = wave
-      const int Jp = wave;
-      f64x4 t = {0.0, 0.0, 0.0, 0.0};
-#pragma unroll 1
-      for (int K = Jp; K < J; ++K) {
-#pragma unroll
-        for (int s4 = 0; s4 < 4; ++s4) {
-          const int kk = 4 * s4 + kq;
-          t = __builtin_amdgcn_mfma_f64_16x16x4f64(S[16 * K + kk][r0 + m], Xs[16 * K + kk][16 * Jp + m],
-                                                  t, 0, 0, 0);
-        }
-      }
-      f64x4 x = {0.0, 0.0, 0.0, 0.0};
-#pragma unroll
-      for (int s4 = 0; s4 < 4; ++s4)
-        x = __builtin_amdgcn_mfma_f64_16x16x4f64(-xop[s4], t[s4], x, 0, 0, 0);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) Xs[r0 + mfma64_row(lane, q)][16 * Jp + m] = x[q];
-    }
-    __syncthreads();
+  for (int q = 0; q < 6; ++q) {
+    const int I = q < 3 ? 0 : (q < 5 ? 1 : 2);
+    const int K = q < 3 ? q + 1 : (q < 5 ? q - 1 : 3);
+    const int r = 16 * I + (tid >> 4), c = 16 * K + (tid & 15);
+    if (r < kb && c < kb) Xd[(int64_t)r * ldxd + c] = 0.0;
   }
-
-#pragma unroll
-  for (int q = 0; q < 16; ++q) {
-    const int e = tid + 256 * q;
-    const int i = e >> 6, l = e & 63;
-    if (i < kb && l < kb) {
-      if (l <= i)
-        A[(int64_t)(k + i) * lda + k + l] = ((i >> 4) == (l >> 4)) ? sh.Ld[i >> 4][i & 15][l & 15]
-                                                                   : S[l][i];
-      Xd[(int64_t)i * ldxd + l] = (l <= i) ? Xs[i][l] : 0.0;
-    }
-  }
+  __syncthreads();  // every wave has its row before L blocks overwrite S
+  f64x4 tsum = {0.0, 0.0, 0.0, 0.0};
+  diag_phase<0>(cx, row, tsum);
+  diag_phase<1>(cx, row, tsum);
+  diag_phase<2>(cx, row, tsum);
+  diag_phase<3>(cx, row, tsum);
 }
 
 // One workgroup factors the 64x64 diagonal block of the panel at column k and
@@ -298,7 +420,6 @@ __global__ __launch_bounds__(256) void potrf_diag_kernel(double* __restrict__ A,
   for (int q = 0; q < 16; ++q) {
     const int e = tid + 256 * q;
     sh.S[e >> 6][e & 63] = v[q];
-    sh.Xs[e >> 6][e & 63] = 0.0;
   }
   __syncthreads();
   diag_factor(sh, A, lda, k, kb, flag, info_offset, Xd, ldxd);
@@ -457,11 +578,6 @@ __global__ __launch_bounds__(256, 2) void potrf_update_kernel(double* __restrict
         const int c = 32 * wn + 16 * b + (lane & 15);
         sh.S[r][c] = (r < kb && c < kb) ? cv[a][b][i] - acc[a][b][i] : ((r == c) ? 1.0 : 0.0);
       }
-#pragma unroll
-  for (int q = 0; q < 16; ++q) {
-    const int e = tid + 256 * q;
-    sh.Xs[e >> 6][e & 63] = 0.0;
-  }
   __syncthreads();
   diag_factor(sh, A, lda, t0, kb, flag, info_offset, Xn, ldxn);
 }
