@@ -46,15 +46,6 @@ constexpr int NB = kPanel;  // 64
 constexpr int PP = NB + 2;  // LDS pitch (doubles) of the 64x64 panel tiles: conflict-free
                             // MFMA operand reads (rows m = lane%16, columns k = lane/16)
 
-// 1/p to full fp64 accuracy: hardware reciprocal estimate + two Newton steps.
-__device__ inline double recip_f64(double p) {
-  double r = __builtin_amdgcn_rcp(p);
-  double e = __builtin_fma(-p, r, 1.0);
-  r = __builtin_fma(r, e, r);
-  e = __builtin_fma(-p, r, 1.0);
-  return __builtin_fma(r, e, r);
-}
-
 // 1/sqrt(p) to fp64 accuracy: hardware estimate + two Newton steps.
 __device__ inline double rsqrt_f64(double p) {
   double r = __builtin_amdgcn_rsq(p);

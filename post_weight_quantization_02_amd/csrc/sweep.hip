@@ -302,7 +302,11 @@ constexpr int LT = 128;  // output tile edge
 constexpr int LK = 32;   // K chunk
 constexpr int LP = LT + 16;
 
-template <int MT>  // 16x16 MFMA tiles per wave along rows: workgroup tile (32*MT) x 128
+// MT: 16x16 MFMA tiles per wave along rows (workgroup tile (32*MT) x 128).
+// ALL: K <= 4 chunks, and every chunk's loads and the W tile's loads are
+// issued up front (one memory round trip for the whole update instead of
+// one per chunk: the small updates inside a superblock are latency-bound).
+template <int MT, bool ALL>
 __global__ __launch_bounds__(256, 2) void lazy_kernel(float* __restrict__ Wk, int64_t ldk,
                                                    int64_t rows, int64_t cols, int k0, int k1,
                                                    int c0, int c1, const float* __restrict__ Err,
@@ -333,14 +337,15 @@ __global__ __launch_bounds__(256, 2) void lazy_kernel(float* __restrict__ Wk, in
   // A = Err[r0.., k0..k1]: the row stride ldk is a multiple of 128 and k0 a
   // multiple of 128, so a whole chunk stays inside each (clamped) row.
   // B = Hinv[k0..k1, n0..]: row and column indices are clamped.
-  float4 av[AV], bv[4];
-  auto gload = [&](int kc) {
+  constexpr int NR = ALL ? 4 : 1;  // register sets of chunk loads in flight
+  float4 av[NR][AV], bv[NR][4];
+  auto gload = [&](int set, int kc) {
 #pragma unroll
     for (int q = 0; q < AV; ++q) {
       const int e = tid + 256 * q;
       const int m = e >> 3, kk = (e & 7) * 4;  // A: 8 float4 per row
       const int64_t gr = (r0 + m < rows) ? r0 + m : rows - 1;
-      av[q] = *reinterpret_cast<const float4*>(Err + gr * ldk + k0 + kc + kk);
+      av[set][q] = *reinterpret_cast<const float4*>(Err + gr * ldk + k0 + kc + kk);
     }
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -350,17 +355,17 @@ __global__ __launch_bounds__(256, 2) void lazy_kernel(float* __restrict__ Wk, in
       const float* p = Hinv + (int64_t)krow * cols;
       const int64_t gc = n0 + nn;
       const int64_t cl = cols - 1;
-      bv[q] = make_float4(p[gc < cl ? gc : cl], p[gc + 1 < cl ? gc + 1 : cl],
-                          p[gc + 2 < cl ? gc + 2 : cl], p[gc + 3 < cl ? gc + 3 : cl]);
+      bv[set][q] = make_float4(p[gc < cl ? gc : cl], p[gc + 1 < cl ? gc + 1 : cl],
+                               p[gc + 2 < cl ? gc + 2 : cl], p[gc + 3 < cl ? gc + 3 : cl]);
     }
   };
-  auto lstore = [&](int buf, int kc) {
+  auto lstore = [&](int set, int buf, int kc) {
 #pragma unroll
     for (int q = 0; q < AV; ++q) {
       const int e = tid + 256 * q;
       const int m = e >> 3, kk = (e & 7) * 4;
       const int gk = kc + kk;
-      float4 v = av[q];
+      float4 v = av[set][q];
       v.x = (gk + 0 < K) ? v.x : 0.f;
       v.y = (gk + 1 < K) ? v.y : 0.f;
       v.z = (gk + 2 < K) ? v.z : 0.f;
@@ -373,7 +378,7 @@ __global__ __launch_bounds__(256, 2) void lazy_kernel(float* __restrict__ Wk, in
       const int kb = e >> 5, nn = (e & 31) * 4;
       const bool kv = kc + kb < K;
       const int64_t gc = n0 + nn;
-      float4 u = bv[q];
+      float4 u = bv[set][q];
       u.x = (kv && gc + 0 < c1) ? u.x : 0.f;
       u.y = (kv && gc + 1 < c1) ? u.y : 0.f;
       u.z = (kv && gc + 2 < c1) ? u.z : 0.f;
@@ -388,13 +393,7 @@ __global__ __launch_bounds__(256, 2) void lazy_kernel(float* __restrict__ Wk, in
   float* const wbase = Wk + rb * ldk + cb;
   const int ldi = (int)ldk;
   const int nchunks = (K + LK - 1) / LK;
-  gload(0);
-  lstore(0, 0);
-  __syncthreads();
-  int buf = 0;
-  for (int ch = 0; ch < nchunks; ++ch) {
-    const bool more = ch + 1 < nchunks;
-    if (more) gload((ch + 1) * LK);
+  auto mma_chunk = [&](int buf) {
 #pragma unroll
     for (int ks = 0; ks < LK; ks += 4) {
       const int kr = ks + (lane >> 4);
@@ -409,28 +408,57 @@ __global__ __launch_bounds__(256, 2) void lazy_kernel(float* __restrict__ Wk, in
         for (int b = 0; b < 4; ++b)
           acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[a], bf[b], acc[a][b], 0, 0, 0);
     }
-    if (more) lstore(buf ^ 1, (ch + 1) * LK);
-    __syncthreads();
-    buf ^= 1;
-  }
-  // read-modify-write of the W tile, all loads of a row block before its stores
+  };
+  // the W tile this lane updates: rows rb + 16a + i, columns cb + 16b
+  float cv[MT][4][4];
+  auto wload = [&]() {
 #pragma unroll
-  for (int a = 0; a < MT; ++a) {
-    float cv[4][4];
+    for (int a = 0; a < MT; ++a)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const bool rv = rb + 16 * a + i < rows;
+      for (int i = 0; i < 4; ++i) {
+        const bool rv = rb + 16 * a + i < rows;
 #pragma unroll
-      for (int b = 0; b < 4; ++b) cv[i][b] = rv ? wbase[(16 * a + i) * ldi + 16 * b] : 0.f;
+        for (int b = 0; b < 4; ++b) cv[a][i][b] = rv ? wbase[(16 * a + i) * ldi + 16 * b] : 0.f;
+      }
+  };
+  if (ALL) {
+    // every chunk (K <= 4 * LK) and the W tile in flight at once
+#pragma unroll
+    for (int c = 0; c < NR; ++c) gload(c, c * LK);
+    wload();
+#pragma unroll
+    for (int c = 0; c < NR; ++c) {
+      if (c < nchunks) {
+        lstore(c, c & 1, c * LK);
+        __syncthreads();
+        mma_chunk(c & 1);
+      }
     }
+  } else {
+    gload(0, 0);
+    lstore(0, 0, 0);
+    __syncthreads();
+    int buf = 0;
+    for (int ch = 0; ch < nchunks; ++ch) {
+      const bool more = ch + 1 < nchunks;
+      if (more) gload(0, (ch + 1) * LK);
+      mma_chunk(buf);
+      if (more) lstore(0, buf ^ 1, (ch + 1) * LK);
+      __syncthreads();
+      buf ^= 1;
+    }
+    wload();
+  }
+  // W tile update
+#pragma unroll
+  for (int a = 0; a < MT; ++a)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const bool rv = rb + 16 * a + i < rows;
 #pragma unroll
       for (int b = 0; b < 4; ++b)
-        if (rv && cb + 16 * b < c1) wbase[(16 * a + i) * ldi + 16 * b] = cv[i][b] - acc[a][b][i];
+        if (rv && cb + 16 * b < c1) wbase[(16 * a + i) * ldi + 16 * b] = cv[a][i][b] - acc[a][b][i];
     }
-  }
 }
 
 // ---------------------------------------------------------------- helpers
@@ -502,15 +530,20 @@ hipError_t launch_lazy_update(float* Wk, int64_t ldk, int64_t rows, int64_t cols
                               int c0, int c1, const float* Err, const float* Hinv, hipStream_t s) {
   if (c1 <= c0 || k1 <= k0) return hipSuccess;
   const int64_t ncol = ceil_div(c1 - c0, LT);
-  // big updates: 128x128 tiles; small ones: 32x128 tiles so more CUs take part
+  // big updates: 128x128 tiles; small ones: 32x128 tiles so more CUs take
+  // part, with all of K (at most 128) and the W tile loaded up front
   if (ncol * ceil_div(rows, 128) >= 512) {
     dim3 grid((unsigned)ncol, (unsigned)ceil_div(rows, 128));
-    hipLaunchKernelGGL(lazy_kernel<4>, grid, dim3(256), 0, s, Wk, ldk, rows, cols, k0, k1, c0, c1,
-                       Err, Hinv);
+    hipLaunchKernelGGL((lazy_kernel<4, false>), grid, dim3(256), 0, s, Wk, ldk, rows, cols, k0, k1,
+                       c0, c1, Err, Hinv);
   } else {
     dim3 grid((unsigned)ncol, (unsigned)ceil_div(rows, 32));
-    hipLaunchKernelGGL(lazy_kernel<1>, grid, dim3(256), 0, s, Wk, ldk, rows, cols, k0, k1, c0, c1,
-                       Err, Hinv);
+    if (k1 - k0 <= 4 * LK)
+      hipLaunchKernelGGL((lazy_kernel<1, true>), grid, dim3(256), 0, s, Wk, ldk, rows, cols, k0,
+                         k1, c0, c1, Err, Hinv);
+    else
+      hipLaunchKernelGGL((lazy_kernel<1, false>), grid, dim3(256), 0, s, Wk, ldk, rows, cols, k0,
+                         k1, c0, c1, Err, Hinv);
   }
   return hipGetLastError();
 }

@@ -223,7 +223,6 @@ __device__ inline bool xcd_tile(int t, int slots, int ntiles, int nb, int& bi, i
 // by sw(R) so the 16 rows one transposing read touches (R = 8g + r, g,r < 4)
 // use 16 distinct bank groups.
 constexpr int NS = 4;                 // LDS ring stages
-constexpr int RB = T * 2;             // bytes per LDS row (unpadded)
 constexpr int BLK = KC * T;           // halves per operand block per stage
 
 __device__ inline int swz(int row) { return 2 * ((row & 3) | (((row >> 3) & 3) << 2)); }
