@@ -667,27 +667,47 @@ __global__ __launch_bounds__(256) void gemm64_f64_kernel(GemmDesc g) {
 #pragma unroll
     for (int b = 0; b < 2; ++b) acc[a][b] = f64x4{0.0, 0.0, 0.0, 0.0};
 
-  // Loads read clamped (always valid) addresses and keep the raw values; the
-  // bounds and triangle masks are applied when the values go to LDS, so the
-  // MFMAs of the current chunk never wait for the next chunk's loads.
-  double av[4], bv[4];
-  auto gload = [&](int kc) {
+  // Loads: a uniform base per chunk plus a 32-bit per-thread byte offset
+  // (global_load with a scalar base).  The row part of each offset is fixed;
+  // the k part is clamped to the chunk's valid range, so every address is
+  // inside the operand (the bounds and triangle masks are applied at the LDS
+  // store), and the MFMAs of the current chunk never wait for these loads.
+  // Offsets stay below 2^31 for leading dimensions up to 65536.
+  constexpr int NLD = GT * GK / 256;
+  double av[NLD], bv[NLD];
+  uint32_t aro[NLD], bro[NLD];
+  int akk[NLD], bkk[NLD];
+  const uint32_t lda8 = (uint32_t)g.lda * 8u, ldb8 = (uint32_t)g.ldb * 8u;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int e = tid + 256 * q;
-      const int kk = AK ? (e % GK) : (e / GT);
-      const int mm = AK ? (e / GK) : (e % GT);
-      const int gm = min(m0 + mm, g.M - 1), gk = min(kc + kk, k1 - 1);
-      av[q] = AK ? Ap[(int64_t)gm * g.lda + gk] : Ap[(int64_t)gk * g.lda + gm];
-      const int kb = BN ? (e / GT) : (e % GK);
-      const int nn = BN ? (e % GT) : (e / GK);
-      const int gn = min(n0 + nn, g.N - 1), gk2 = min(kc + kb, k1 - 1);
-      bv[q] = BN ? Bp[(int64_t)gk2 * g.ldb + gn] : Bp[(int64_t)gn * g.ldb + gk2];
+  for (int q = 0; q < NLD; ++q) {
+    const int e = tid + 256 * q;
+    const int kk = AK ? (e % GK) : (e / GT);
+    const int mm = min(AK ? (e / GK) : (e % GT), g.M - 1 - m0);
+    aro[q] = AK ? (uint32_t)mm * lda8 : (uint32_t)mm * 8u;
+    akk[q] = kk;
+    const int kb = BN ? (e / GT) : (e % GK);
+    const int nn = min(BN ? (e % GT) : (e / GK), g.N - 1 - n0);
+    bro[q] = BN ? (uint32_t)nn * 8u : (uint32_t)nn * ldb8;
+    bkk[q] = kb;
+  }
+  auto gload = [&](int kc) {
+    const int lim = k1 - 1 - kc;
+    const char* abase = reinterpret_cast<const char*>(
+        Ap + (AK ? (int64_t)m0 * g.lda + kc : (int64_t)kc * g.lda + m0));
+    const char* bbase = reinterpret_cast<const char*>(
+        Bp + (BN ? (int64_t)kc * g.ldb + n0 : (int64_t)n0 * g.ldb + kc));
+#pragma unroll
+    for (int q = 0; q < NLD; ++q) {
+      const uint32_t ka = (uint32_t)min(akk[q], lim), kb = (uint32_t)min(bkk[q], lim);
+      const uint32_t oa = aro[q] + (AK ? ka * 8u : ka * lda8);
+      const uint32_t ob = bro[q] + (BN ? kb * ldb8 : kb * 8u);
+      av[q] = *reinterpret_cast<const double*>(abase + oa);
+      bv[q] = *reinterpret_cast<const double*>(bbase + ob);
     }
   };
   auto lstore = [&](int buf, int kc) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < NLD; ++q) {
       const int e = tid + 256 * q;
       const int kk = AK ? (e % GK) : (e / GT);
       const int mm = AK ? (e / GK) : (e % GT);
@@ -779,7 +799,6 @@ __global__ __launch_bounds__(256, 2) void gemm128_f64_kernel(GemmDesc g) {
   // ([m][k], pitch GK + 1), m-contiguous ones k-major ([k][m], pitch 144).
   constexpr int PK = GT2 + 16;
   constexpr int PR = GK + 1;
-  constexpr int NL = GT2 * GK / 256;  // elements per thread per operand per chunk
   constexpr int SA = AK ? GT2 * PR : GK * PK;  // doubles per buffer
   constexpr int SB = BN ? GK * PK : GT2 * PR;
   __shared__ double As[2][SA];
@@ -811,25 +830,47 @@ __global__ __launch_bounds__(256, 2) void gemm128_f64_kernel(GemmDesc g) {
 #pragma unroll
     for (int b = 0; b < 4; ++b) acc[a][b] = f64x4{0.0, 0.0, 0.0, 0.0};
 
-  // raw loads from clamped addresses; masks are applied at the LDS store
-  double av[NL], bv[NL];
-  auto gload = [&](int kc) {
+  // Loads: a uniform base per chunk plus a 32-bit per-thread byte offset
+  // (global_load with a scalar base).  The row part of each offset is fixed;
+  // the k part is clamped to the chunk's valid range, so every address is
+  // inside the operand (the bounds and triangle masks are applied at the LDS
+  // store), and the MFMAs of the current chunk never wait for these loads.
+  // Offsets stay below 2^31 for leading dimensions up to 65536.
+  constexpr int NLD = GT2 * GK / 256;
+  double av[NLD], bv[NLD];
+  uint32_t aro[NLD], bro[NLD];
+  int akk[NLD], bkk[NLD];
+  const uint32_t lda8 = (uint32_t)g.lda * 8u, ldb8 = (uint32_t)g.ldb * 8u;
 #pragma unroll
-    for (int q = 0; q < NL; ++q) {
-      const int e = tid + 256 * q;
-      const int kk = AK ? (e % GK) : (e / GT2);
-      const int mm = AK ? (e / GK) : (e % GT2);
-      const int gm = min(m0 + mm, g.M - 1), gk = min(kc + kk, k1 - 1);
-      av[q] = AK ? Ap[(int64_t)gm * g.lda + gk] : Ap[(int64_t)gk * g.lda + gm];
-      const int kb = BN ? (e / GT2) : (e % GK);
-      const int nn = BN ? (e % GT2) : (e / GK);
-      const int gn = min(n0 + nn, g.N - 1), gk2 = min(kc + kb, k1 - 1);
-      bv[q] = BN ? Bp[(int64_t)gk2 * g.ldb + gn] : Bp[(int64_t)gn * g.ldb + gk2];
+  for (int q = 0; q < NLD; ++q) {
+    const int e = tid + 256 * q;
+    const int kk = AK ? (e % GK) : (e / GT2);
+    const int mm = min(AK ? (e / GK) : (e % GT2), g.M - 1 - m0);
+    aro[q] = AK ? (uint32_t)mm * lda8 : (uint32_t)mm * 8u;
+    akk[q] = kk;
+    const int kb = BN ? (e / GT2) : (e % GK);
+    const int nn = min(BN ? (e % GT2) : (e / GK), g.N - 1 - n0);
+    bro[q] = BN ? (uint32_t)nn * 8u : (uint32_t)nn * ldb8;
+    bkk[q] = kb;
+  }
+  auto gload = [&](int kc) {
+    const int lim = k1 - 1 - kc;
+    const char* abase = reinterpret_cast<const char*>(
+        Ap + (AK ? (int64_t)m0 * g.lda + kc : (int64_t)kc * g.lda + m0));
+    const char* bbase = reinterpret_cast<const char*>(
+        Bp + (BN ? (int64_t)kc * g.ldb + n0 : (int64_t)n0 * g.ldb + kc));
+#pragma unroll
+    for (int q = 0; q < NLD; ++q) {
+      const uint32_t ka = (uint32_t)min(akk[q], lim), kb = (uint32_t)min(bkk[q], lim);
+      const uint32_t oa = aro[q] + (AK ? ka * 8u : ka * lda8);
+      const uint32_t ob = bro[q] + (BN ? kb * ldb8 : kb * 8u);
+      av[q] = *reinterpret_cast<const double*>(abase + oa);
+      bv[q] = *reinterpret_cast<const double*>(bbase + ob);
     }
   };
   auto lstore = [&](int buf, int kc) {
 #pragma unroll
-    for (int q = 0; q < NL; ++q) {
+    for (int q = 0; q < NLD; ++q) {
       const int e = tid + 256 * q;
       const int kk = AK ? (e % GK) : (e / GT2);
       const int mm = AK ? (e / GK) : (e % GT2);
