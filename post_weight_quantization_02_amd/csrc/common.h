@@ -63,7 +63,9 @@ constexpr int kOuterPanel = 512;  // columns per outer block of the two-level Ch
 // sweep
 hipError_t launch_convert_w(const void* W, int w_dtype, int64_t rows, int64_t cols, int64_t ldw,
                             float* Wk, int64_t ldk, hipStream_t s);
-hipError_t launch_sweep_block(float* Wk, int64_t ldk, int64_t rows, int64_t cols, int i1,
+// sweep of the block at column i1; with p0 < i1 (groups inside blocks), the
+// pending errors of blocks [p0, i1) are applied to the block first
+hipError_t launch_sweep_block(float* Wk, int64_t ldk, int64_t rows, int64_t cols, int i1, int p0,
                               const float* Hinv, int bits, int groupsize, uint8_t* codes,
                               float* scales, float* zeros, float* Err, float* loss_part,
                               hipStream_t s);

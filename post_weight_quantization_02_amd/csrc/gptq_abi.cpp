@@ -223,22 +223,29 @@ gptq_status gptq_quantize_layer(const void* W, int w_dtype, int64_t rows, int64_
 
   if (launch_convert_w(W, w_dtype, rows, cols, ldw, Wk, L.ldk, s) != hipSuccess) return GPTQ_ERR_HIP;
   // Two-level lazy batching.  Inside a superblock of SB columns each block's
-  // errors are applied at once to the rest of the superblock; the columns
-  // after the superblock receive all of its errors in one GEMM with K = SB.
-  // Every column still gets every update before its block is swept (and
-  // before its group's statistics are taken, since SB is a multiple of the
-  // group size when groups span blocks), so the result equals per-block lazy
-  // updates in exact arithmetic.
+  // errors reach the rest of the superblock before those columns are swept;
+  // the columns after the superblock receive all of its errors in one GEMM
+  // with K = SB.  Every column still gets every update before its block is
+  // swept (and before its group's statistics are taken, since SB is a
+  // multiple of the group size when groups span blocks), so the result
+  // equals per-block lazy updates in exact arithmetic.  When groups lie
+  // inside blocks, the sweep kernel applies a block's pending errors from the
+  // earlier blocks of its superblock itself (to its own rows, just before
+  // sweeping them); when groups span blocks, a group's statistics read
+  // columns of later blocks, so those get each block's errors right away in a
+  // separate lazy update.
   const int64_t SB = (groupsize > kBlock) ? (groupsize > kSuperBlock ? groupsize : kSuperBlock)
                                           : kSuperBlock;
+  const bool fused_near = groupsize <= kBlock;
   for (int64_t s0 = 0; s0 < cols; s0 += SB) {
     const int64_t s1 = (s0 + SB < cols) ? s0 + SB : cols;
     for (int64_t i1 = s0; i1 < s1; i1 += kBlock) {
       const int64_t i2 = (i1 + kBlock < s1) ? i1 + kBlock : s1;
-      if (launch_sweep_block(Wk, L.ldk, rows, cols, (int)i1, Hinv, bits, groupsize, codes, scales,
-                             zeros, Err, lpart, s) != hipSuccess)
+      if (launch_sweep_block(Wk, L.ldk, rows, cols, (int)i1, (int)(fused_near ? s0 : i1), Hinv,
+                             bits, groupsize, codes, scales, zeros, Err, lpart, s) != hipSuccess)
         return GPTQ_ERR_HIP;
-      if (launch_lazy_update(Wk, L.ldk, rows, cols, (int)i1, (int)i2, (int)i2, (int)s1, Err, Hinv,
+      if (!fused_near &&
+          launch_lazy_update(Wk, L.ldk, rows, cols, (int)i1, (int)i2, (int)i2, (int)s1, Err, Hinv,
                              s) != hipSuccess)
         return GPTQ_ERR_HIP;
     }

@@ -137,9 +137,57 @@ __device__ inline void sweep_steps(int kj, int l, float s, float z, float rs, fl
 // unrolled, so every register index and the DPP source lane are compile-time
 // constants.  Steps past the end of a short last block run on zero weights
 // and zero Hinv entries and change nothing.
+// Hinv[r0 + j][i1 + c] for j, c < 128 into a 128x128 LDS tile (row j at
+// U + 128 j), zero past column nbc; with TRI, also zero left of the diagonal
+// (the block's own diagonal tile).  16 float4 per thread, all loads first.
+template <bool TRI>
+__device__ inline void load_hinv_tile(float* __restrict__ U, const float* __restrict__ Hinv,
+                                      int64_t cols, int64_t r0, int i1, int nbc, int nrows,
+                                      int tid) {
+  float4 v[16];
+  const bool vec = (cols % 4 == 0) && (reinterpret_cast<uintptr_t>(Hinv) % 16 == 0);
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    const int e = tid + 256 * q;  // float4 index: row e/32, columns 4*(e%32)..
+    const int j = e >> 5, c = (e & 31) * 4;
+    const float* p = Hinv + (r0 + j) * cols + i1 + c;
+    float4 u = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (j < nrows) {
+      if (vec && c + 4 <= nbc) {
+        u = *reinterpret_cast<const float4*>(p);
+      } else {
+        if (c + 0 < nbc) u.x = p[0];
+        if (c + 1 < nbc) u.y = p[1];
+        if (c + 2 < nbc) u.z = p[2];
+        if (c + 3 < nbc) u.w = p[3];
+      }
+    }
+    v[q] = u;
+  }
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    const int e = tid + 256 * q;
+    const int j = e >> 5, c = (e & 31) * 4;
+    float4 u = v[q];
+    if (TRI) {
+      if (c + 0 < j) u.x = 0.f;
+      if (c + 1 < j) u.y = 0.f;
+      if (c + 2 < j) u.z = 0.f;
+      if (c + 3 < j) u.w = 0.f;
+    }
+    *reinterpret_cast<float4*>(U + j * BC + c) = u;
+  }
+}
+
+// p0 < i1 (groups inside blocks only): the blocks [p0, i1) of this
+// superblock were swept by earlier launches and their errors have not yet
+// been applied to this block; the workgroup applies them to its own rows
+// first, W[rows, block] -= Err[rows, p0:i1] Hinv[p0:i1, block], one 128x128
+// Hinv tile at a time through LDS and fp32 MFMA.  This replaces a separate
+// small lazy-update launch per block (the result is the same sum).
 template <int G>
 __global__ __launch_bounds__(256) void sweep_kernel(float* __restrict__ Wk, int64_t ldk,
-                                                    int64_t rows, int64_t cols, int i1,
+                                                    int64_t rows, int64_t cols, int i1, int p0,
                                                     const float* __restrict__ Hinv, int bits,
                                                     int groupsize, uint8_t* __restrict__ codes,
                                                     float* __restrict__ scales,
@@ -149,6 +197,8 @@ __global__ __launch_bounds__(256) void sweep_kernel(float* __restrict__ Wk, int6
   __shared__ __attribute__((aligned(16))) float Ub[BC * BC];  // Hinv block, row j at Ub + 128 j
   __shared__ float rdiag[BC];
   __shared__ float lsum[4][BC];
+  constexpr int EP = BC + 4;  // pitch of the Err slice / update tile (rows of 128 floats)
+  __shared__ __attribute__((aligned(16))) float Es[kSweepRows * EP];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -160,50 +210,58 @@ __global__ __launch_bounds__(256) void sweep_kernel(float* __restrict__ Wk, int6
   const int nbc = (int)((cols - i1) < BC ? (cols - i1) : BC);
   const int64_t ngroups = ceil_div(cols, groupsize);
 
-  // Hinv[i1:i1+128, i1:i1+128] with the part left of the diagonal (and past
-  // the last column) zeroed: 16 float4 per thread, all loads issued first
-  {
-    float4 v[16];
-    const bool vec = (cols % 4 == 0) && (reinterpret_cast<uintptr_t>(Hinv) % 16 == 0);
-#pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      const int e = tid + 256 * q;  // float4 index: row e/32, columns 4*(e%32)..
-      const int j = e >> 5, c = (e & 31) * 4;
-      const float* p = Hinv + (int64_t)(i1 + j) * cols + i1 + c;
-      float4 u = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (j < nbc) {
-        if (vec && c + 4 <= nbc) {
-          u = *reinterpret_cast<const float4*>(p);
-        } else {
-          if (c + 0 < nbc) u.x = p[0];
-          if (c + 1 < nbc) u.y = p[1];
-          if (c + 2 < nbc) u.z = p[2];
-          if (c + 3 < nbc) u.w = p[3];
-        }
-      }
-      v[q] = u;
-    }
-#pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      const int e = tid + 256 * q;
-      const int j = e >> 5, c = (e & 31) * 4;
-      float4 u = v[q];
-      if (c + 0 < j) u.x = 0.f;
-      if (c + 1 < j) u.y = 0.f;
-      if (c + 2 < j) u.z = 0.f;
-      if (c + 3 < j) u.w = 0.f;
-      *reinterpret_cast<float4*>(Ub + j * BC + c) = u;
-    }
-  }
-  for (int j = tid; j < BC; j += 256)
-    rdiag[j] = (j < nbc) ? 1.f / Hinv[(int64_t)(i1 + j) * cols + i1 + j] : 0.f;
-
   float w[CPL];
 #pragma unroll
   for (int k = 0; k < CPL; ++k) {
     const int c = l + RL * k;
     w[k] = (rv && c < nbc) ? Wk[row * ldk + i1 + c] : 0.f;
   }
+
+  if (G != 0 && p0 < i1) {
+    // pending errors of this superblock: dacc = Err[rows, p0:i1] Hinv[p0:i1, block],
+    // wave w forming columns 32w..32w+31 of the 16 rows
+    const int64_t row0 = (int64_t)blockIdx.x * kSweepRows;
+    f32x4 dacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    for (int c0 = p0; c0 < i1; c0 += BC) {
+      load_hinv_tile<false>(Ub, Hinv, cols, c0, i1, nbc, BC, tid);
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {  // Err slice: 16 rows x 32 float4
+        const int e = tid + 256 * q;
+        const int r = e >> 5, c = (e & 31) * 4;
+        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (row0 + r < rows) v = *reinterpret_cast<const float4*>(Err + (row0 + r) * ldk + c0 + c);
+        *reinterpret_cast<float4*>(Es + r * EP + c) = v;
+      }
+      __syncthreads();
+#pragma unroll 8
+      for (int s4 = 0; s4 < BC / 4; ++s4) {
+        const int kr = 4 * s4 + (lane >> 4);
+        const float a = Es[(lane & 15) * EP + kr];
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+          dacc[b] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, Ub[kr * BC + 32 * wave + 16 * b + (lane & 15)],
+                                                        dacc[b], 0, 0, 0);
+      }
+      __syncthreads();  // Ub and Es are refilled next
+    }
+    // element i of dacc[b] at lane (n, q) is the update of row 4q + i, column 32w + 16b + n
+    // (the fp32 16x16x4 result layout)
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        Es[(4 * (lane >> 4) + i) * EP + 32 * wave + 16 * b + (lane & 15)] = dacc[b][i];
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < CPL; ++k) w[k] -= Es[(wave * 4 + rg) * EP + l + RL * k];
+  }
+
+  // Hinv[i1:i1+128, i1:i1+128] with the part left of the diagonal (and past
+  // the last column) zeroed
+  load_hinv_tile<true>(Ub, Hinv, cols, i1, i1, nbc, nbc, tid);
+  for (int j = tid; j < BC; j += 256)
+    rdiag[j] = (j < nbc) ? 1.f / Hinv[(int64_t)(i1 + j) * cols + i1 + j] : 0.f;
+
   __syncthreads();
 
   const float qm = (float)((1 << bits) - 1);
@@ -507,14 +565,14 @@ hipError_t launch_convert_w(const void* W, int w_dtype, int64_t rows, int64_t co
   return hipGetLastError();
 }
 
-hipError_t launch_sweep_block(float* Wk, int64_t ldk, int64_t rows, int64_t cols, int i1,
+hipError_t launch_sweep_block(float* Wk, int64_t ldk, int64_t rows, int64_t cols, int i1, int p0,
                               const float* Hinv, int bits, int groupsize, uint8_t* codes,
                               float* scales, float* zeros, float* Err, float* lpart,
                               hipStream_t s) {
   dim3 grid((unsigned)ceil_div(rows, kSweepRows));
 #define GPTQ_SWEEP(G)                                                                          \
-  hipLaunchKernelGGL(sweep_kernel<G>, grid, dim3(256), 0, s, Wk, ldk, rows, cols, i1, Hinv,   \
-                     bits, groupsize, codes, scales, zeros, Err, lpart)
+  hipLaunchKernelGGL(sweep_kernel<G>, grid, dim3(256), 0, s, Wk, ldk, rows, cols, i1, p0,     \
+                     Hinv, bits, groupsize, codes, scales, zeros, Err, lpart)
   switch (groupsize) {
     case 16: GPTQ_SWEEP(16); break;
     case 32: GPTQ_SWEEP(32); break;
