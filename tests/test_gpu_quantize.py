@@ -48,6 +48,8 @@ def _gpu_quant(env, W, U32, bits, g):
     (24, 640, 4, 256, "f16"),     # groups spanning two blocks, short last group
     (5, 130, 4, 128, "f32"),      # 2-column last block
     (1, 64, 4, 128, "f32"),       # a single row, a single short block
+    (50, 1100, 4, 128, "f16"),    # three superblocks, the last one a ragged block
+    (30, 700, 3, 64, "f32"),      # two superblocks, pending in-superblock errors with g < 128
 ])
 def test_sweep_matches_oracle_given_hinv(env, rows, cols, bits, g, wdt):
     W, H, U32 = _case(rows, cols, 4 * cols, wdtype=wdt)
