@@ -529,6 +529,31 @@ __global__ __launch_bounds__(256) void convert_kernel(const T* __restrict__ W, i
     Wk[r * ldk + c] = (c < cols) ? (float)W[r * ldw + c] : 0.f;
 }
 
+// fp16 rows whose start is 16-byte aligned (ldw % 8 == 0): 8 columns per
+// thread with one 16-byte load and two 16-byte stores.  ldk is a multiple of
+// 128, so every 8-column run of Wk is whole.
+__global__ __launch_bounds__(256) void convert_f16x8_kernel(const _Float16* __restrict__ W,
+                                                            int64_t cols, int64_t ldw,
+                                                            float* __restrict__ Wk, int64_t ldk) {
+  typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+  const int64_t r = blockIdx.x;
+  for (int64_t c = ((int64_t)blockIdx.y * 256 + threadIdx.x) * 8; c < ldk;
+       c += (int64_t)gridDim.y * 256 * 8) {
+    float o[8];
+    if (c + 8 <= cols) {
+      const h8 v = *reinterpret_cast<const h8*>(W + r * ldw + c);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) o[u] = (float)v[u];
+    } else {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) o[u] = (c + u < cols) ? (float)W[r * ldw + c + u] : 0.f;
+    }
+    float4* dst = reinterpret_cast<float4*>(Wk + r * ldk + c);
+    dst[0] = make_float4(o[0], o[1], o[2], o[3]);
+    dst[1] = make_float4(o[4], o[5], o[6], o[7]);
+  }
+}
+
 // losses[c] = sum over parts p of lpart[p][c], in a fixed order: a workgroup
 // takes 16 columns; thread (s, c) sums parts s, s+16, ... and the 16 slices
 // are added in slice order.
@@ -556,7 +581,12 @@ __global__ __launch_bounds__(256) void loss_reduce_kernel(const float* __restric
 hipError_t launch_convert_w(const void* W, int w_dtype, int64_t rows, int64_t cols, int64_t ldw,
                             float* Wk, int64_t ldk, hipStream_t s) {
   dim3 grid((unsigned)rows, (unsigned)((ceil_div(ldk, 256) < 16) ? ceil_div(ldk, 256) : 16));
-  if (w_dtype == GPTQ_DTYPE_F16)
+  const bool v8 = (ldw % 8 == 0) && ((reinterpret_cast<uintptr_t>(W) & 15) == 0) &&
+                  ((reinterpret_cast<uintptr_t>(Wk) & 15) == 0);
+  if (w_dtype == GPTQ_DTYPE_F16 && v8)
+    hipLaunchKernelGGL(convert_f16x8_kernel, dim3((unsigned)rows, (unsigned)ceil_div(ldk, 2048)),
+                       dim3(256), 0, s, reinterpret_cast<const _Float16*>(W), cols, ldw, Wk, ldk);
+  else if (w_dtype == GPTQ_DTYPE_F16)
     hipLaunchKernelGGL(convert_kernel<_Float16>, grid, dim3(256), 0, s,
                        reinterpret_cast<const _Float16*>(W), rows, cols, ldw, Wk, ldk);
   else
