@@ -137,14 +137,10 @@ __device__ inline void sweep_steps(int kj, int l, float s, float z, float rs, fl
 // unrolled, so every register index and the DPP source lane are compile-time
 // constants.  Steps past the end of a short last block run on zero weights
 // and zero Hinv entries and change nothing.
-// Hinv[r0 + j][i1 + c] for j, c < 128 into a 128x128 LDS tile (row j at
-// U + 128 j), zero past column nbc; with TRI, also zero left of the diagonal
-// (the block's own diagonal tile).  16 float4 per thread, all loads first.
-template <bool TRI>
-__device__ inline void load_hinv_tile(float* __restrict__ U, const float* __restrict__ Hinv,
-                                      int64_t cols, int64_t r0, int i1, int nbc, int nrows,
-                                      int tid) {
-  float4 v[16];
+// Hinv[r0 + j][i1 + c] for j < nrows, c < nbc (zero elsewhere) as the 16
+// float4 this thread moves into a 128x128 LDS tile (row j at U + 128 j).
+__device__ inline void hinv_tile_load(float4 (&v)[16], const float* __restrict__ Hinv, int64_t cols,
+                                      int64_t r0, int i1, int nbc, int nrows, int tid) {
   const bool vec = (cols % 4 == 0) && (reinterpret_cast<uintptr_t>(Hinv) % 16 == 0);
 #pragma unroll
   for (int q = 0; q < 16; ++q) {
@@ -164,6 +160,12 @@ __device__ inline void load_hinv_tile(float* __restrict__ U, const float* __rest
     }
     v[q] = u;
   }
+}
+
+// The loaded tile into LDS; with TRI (the block's own diagonal tile) the part
+// left of the diagonal is zeroed.
+template <bool TRI>
+__device__ inline void hinv_tile_store(float* __restrict__ U, const float4 (&v)[16], int tid) {
 #pragma unroll
   for (int q = 0; q < 16; ++q) {
     const int e = tid + 256 * q;
@@ -176,6 +178,19 @@ __device__ inline void load_hinv_tile(float* __restrict__ U, const float* __rest
       if (c + 3 < j) u.w = 0.f;
     }
     *reinterpret_cast<float4*>(U + j * BC + c) = u;
+  }
+}
+
+// Err[row0 + r][c0 + c] for the workgroup's 16 rows x 128 columns: 2 float4
+// per thread (rows past `rows` read as zero).
+__device__ inline void err_slice_load(float4 (&v)[2], const float* __restrict__ Err, int64_t ldk,
+                                      int64_t rows, int64_t row0, int c0, int tid) {
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int e = tid + 256 * q;
+    const int r = e >> 5, c = (e & 31) * 4;
+    v[q] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (row0 + r < rows) v[q] = *reinterpret_cast<const float4*>(Err + (row0 + r) * ldk + c0 + c);
   }
 }
 
@@ -197,8 +212,7 @@ __global__ __launch_bounds__(256) void sweep_kernel(float* __restrict__ Wk, int6
   __shared__ __attribute__((aligned(16))) float Ub[BC * BC];  // Hinv block, row j at Ub + 128 j
   __shared__ float rdiag[BC];
   __shared__ float lsum[4][BC];
-  constexpr int EP = BC + 4;  // pitch of the Err slice / update tile (rows of 128 floats)
-  __shared__ __attribute__((aligned(16))) float Es[kSweepRows * EP];
+  __shared__ __attribute__((aligned(16))) float Es[kSweepRows * (BC + 4)];  // Err slice / update tile
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -217,22 +231,31 @@ __global__ __launch_bounds__(256) void sweep_kernel(float* __restrict__ Wk, int6
     w[k] = (rv && c < nbc) ? Wk[row * ldk + i1 + c] : 0.f;
   }
 
+  float4 hv[16];  // next Hinv tile on its way to LDS
   if (G != 0 && p0 < i1) {
     // pending errors of this superblock: dacc = Err[rows, p0:i1] Hinv[p0:i1, block],
-    // wave w forming columns 32w..32w+31 of the 16 rows
+    // wave w forming columns 32w..32w+31 of the 16 rows; the next tile (and
+    // finally the block's own diagonal tile) is loaded during each tile's MFMAs
     const int64_t row0 = (int64_t)blockIdx.x * kSweepRows;
+    constexpr int EP = BC + 4;
     f32x4 dacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    float4 ev4[2];
+    hinv_tile_load(hv, Hinv, cols, p0, i1, nbc, BC, tid);
+    err_slice_load(ev4, Err, ldk, rows, row0, p0, tid);
     for (int c0 = p0; c0 < i1; c0 += BC) {
-      load_hinv_tile<false>(Ub, Hinv, cols, c0, i1, nbc, BC, tid);
+      hinv_tile_store<false>(Ub, hv, tid);
 #pragma unroll
-      for (int q = 0; q < 2; ++q) {  // Err slice: 16 rows x 32 float4
+      for (int q = 0; q < 2; ++q) {
         const int e = tid + 256 * q;
-        const int r = e >> 5, c = (e & 31) * 4;
-        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (row0 + r < rows) v = *reinterpret_cast<const float4*>(Err + (row0 + r) * ldk + c0 + c);
-        *reinterpret_cast<float4*>(Es + r * EP + c) = v;
+        *reinterpret_cast<float4*>(Es + (e >> 5) * EP + (e & 31) * 4) = ev4[q];
       }
       __syncthreads();
+      if (c0 + BC < i1) {
+        hinv_tile_load(hv, Hinv, cols, c0 + BC, i1, nbc, BC, tid);
+        err_slice_load(ev4, Err, ldk, rows, row0, c0 + BC, tid);
+      } else {
+        hinv_tile_load(hv, Hinv, cols, i1, i1, nbc, nbc, tid);  // the diagonal tile
+      }
 #pragma unroll 8
       for (int s4 = 0; s4 < BC / 4; ++s4) {
         const int kr = 4 * s4 + (lane >> 4);
@@ -254,11 +277,12 @@ __global__ __launch_bounds__(256) void sweep_kernel(float* __restrict__ Wk, int6
     __syncthreads();
 #pragma unroll
     for (int k = 0; k < CPL; ++k) w[k] -= Es[(wave * 4 + rg) * EP + l + RL * k];
+  } else {
+    hinv_tile_load(hv, Hinv, cols, i1, i1, nbc, nbc, tid);
   }
-
   // Hinv[i1:i1+128, i1:i1+128] with the part left of the diagonal (and past
   // the last column) zeroed
-  load_hinv_tile<true>(Ub, Hinv, cols, i1, i1, nbc, nbc, tid);
+  hinv_tile_store<true>(Ub, hv, tid);
   for (int j = tid; j < BC; j += 256)
     rdiag[j] = (j < nbc) ? 1.f / Hinv[(int64_t)(i1 + j) * cols + i1 + j] : 0.f;
 
