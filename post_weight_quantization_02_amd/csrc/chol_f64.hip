@@ -12,7 +12,9 @@
 //   * Everything runs in fp64: the sweep's integer decisions are sensitive
 //     to the factor's accuracy, and fp32 factorizations of calibration
 //     Hessians lose several digits.  fp64 MFMA (v_mfma_f64_16x16x4_f64)
-//     carries every O(d^3) product; the O(nb^3) panel work runs in LDS.
+//     carries every O(d^3) product; each 64x64 diagonal block is factored and
+//     inverted by one workgroup, in registers (16-column steps on one wave
+//     with DPP, readlane and ds_bpermute) and LDS (the 16x16 L blocks).
 //   * Blocked right-looking Cholesky with 64-wide panels: one workgroup
 //     factors and inverts the panel's diagonal block (diag_factor), one
 //     workgroup per 64-row block below solves against it (a product with the

@@ -27,10 +27,14 @@
 //     across the 16 lanes of the row.
 //   * Per-column loss partials are reduced inside the workgroup and written
 //     per workgroup; a final kernel adds them in a fixed order.
+//   * With groups inside blocks, the workgroup first applies to its rows the
+//     errors of the earlier blocks of the same superblock (fp32 MFMA, one
+//     128x128 Hinv tile at a time through LDS), so no separate launch carries
+//     them.
 //
-// The lazy update W[:, i2:] -= Err[:, i1:i2] Hinv[i1:i2, i2:] is an fp32
-// MFMA GEMM (v_mfma_f32_16x16x4_f32), 128x128 output tiles, K = 128 streamed
-// through LDS in chunks of 16.
+// The lazy update W[:, c0:c1] -= Err[:, k0:k1] Hinv[k0:k1, c0:c1] is an fp32
+// MFMA GEMM (v_mfma_f32_16x16x4_f32) on (32*MT)x128 output tiles, K streamed
+// through double-buffered LDS in chunks of 32.
 #include "common.h"
 
 #include <utility>

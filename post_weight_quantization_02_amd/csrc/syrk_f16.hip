@@ -11,18 +11,22 @@
 //     owning a 128x128 quadrant as 8x8 tiles of v_mfma_f32_16x16x32_f16
 //     (256 fp32 accumulators per lane): 0.5 LDS fragment reads per MFMA keeps
 //     LDS traffic well under its bandwidth at full MFMA rate.
-//   * X chunks of 32 tokens are copied into LDS exactly as they sit in HBM
-//     (token-major, 16-byte loads, rows padded by 32 bytes).  MFMA wants each
-//     lane to hold a run of K (token) values for one channel; gfx950's
-//     transposing LDS read ds_read_b64_tr_b16 delivers exactly that from the
-//     token-major tile: in every 16-lane group, lane s addresses row s/4,
-//     columns 4*(s%4).., and lane i receives channel i at four consecutive
-//     rows.  Two such reads give the 8-token run of a 16x16x32 operand.
-//   * Double-buffered LDS; the next chunk's global loads are issued before
-//     the current chunk's MFMAs.
-//   * The token range is split so the grid fills every CU for several rounds;
-//     each split writes its own fp32 partial tile and a second kernel sums the
-//     partials in a fixed order (bitwise reproducible, no float atomics).
+//   * X chunks of 32 tokens go into LDS exactly as they sit in HBM
+//     (token-major).  MFMA wants each lane to hold a run of K (token) values
+//     for one channel; gfx950's transposing LDS read ds_read_b64_tr_b16
+//     delivers exactly that from the token-major tile: in every 16-lane
+//     group, lane s addresses row s/4, columns 4*(s%4).., and lane i receives
+//     channel i at four consecutive rows.  Two such reads give the 8-token run
+//     of a 16x16x32 operand.
+//   * Fast path (whole 256x256 tiles, whole chunks, 16-byte aligned X):
+//     global_load_lds_dwordx4 straight into a 4-stage LDS ring with an XOR
+//     swizzle, explicit vmcnt waits and a bare barrier (see fast_body).
+//     General path (ragged d or n, unaligned X): register-staged, double-
+//     buffered LDS with padded rows.
+//   * The token range is split so the grid fills every CU for several rounds
+//     (at most 8192 tokens per split: a split sums in fp32); each split
+//     writes its own fp32 partial tile and a second kernel sums the partials
+//     in a fixed order in fp64 (bitwise reproducible, no float atomics).
 //   * fp16 products are exact in fp32; accumulation is fp32.
 #include "common.h"
 
