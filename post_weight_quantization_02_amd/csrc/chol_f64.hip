@@ -486,65 +486,54 @@ __global__ __launch_bounds__(256) void potrf_trsm_kernel(double* __restrict__ A,
 
 // Update after panel k inside an outer panel: A_ij -= L_ik L_jk^T for the
 // 64x64 tiles i >= j of A[t0:, t0:], t0 = k + 64, whose column block j lies
-// in the first `ncol` blocks (the launch grid counts them), both panel blocks
-// in LDS.  Workgroup 0 takes tile (0, 0), the next panel's diagonal block,
-// keeps the updated block in LDS and goes on to factor and invert it
-// (diag_factor): the next panel's serial step runs while the other
+// in the first `ncol` blocks (`ntiles` tiles, numbered column by column),
+// both panel blocks in LDS.  Workgroup 0 takes tile (0, 0), the next panel's
+// diagonal block, keeps the updated block in LDS and goes on to factor and
+// invert it (diag_factor): the next panel's serial step runs while the other
 // workgroups are still updating, instead of after them (lookahead of one
-// panel).
+// panel).  The grid may be smaller than the tile count: workgroup b > 0 then
+// takes tiles b, b + G - 1, b + 2(G - 1), ... (G = gridDim.x) and loads the
+// next tile's panel blocks and C tile into registers before the current
+// tile's MFMAs, so a large early update is not a sequence of rounds that each
+// wait for their loads.
 __global__ __launch_bounds__(256, 2) void potrf_update_kernel(double* __restrict__ A, int lda, int d,
-                                                           int k, int nt, int* flag, int info_offset,
-                                                           double* __restrict__ Xn, int ldxn) {
+                                                           int k, int nt, int ntiles, int* flag,
+                                                           int info_offset, double* __restrict__ Xn,
+                                                           int ldxn) {
   __shared__ DiagLds sh;
   double (*Ps)[PP] = sh.S;
   double (*Qs)[PP] = sh.Xs;
-  // tile (ti, tj), ti >= tj, column by column: column tj holds nt - tj tiles
-  int ti = blockIdx.x, tj = 0;
-  while (ti >= nt - tj) {
-    ti -= nt - tj;
-    ++tj;
-  }
-  ti += tj;
   const int t0 = k + NB;
-  const int r0 = t0 + NB * ti, c0 = t0 + NB * tj;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const bool diag = (ti == tj);
-  const bool lookahead = (blockIdx.x == 0);
   const int j = tid & 63, i0 = tid >> 6;
-  double pv[16], qv[16];
+  // tile p -> (r0, c0) and whether it is a diagonal tile; column tj holds nt - tj tiles
+  auto coords = [&](int p, int& r0, int& c0) {
+    int ti = p, tj = 0;
+    while (ti >= nt - tj) {
+      ti -= nt - tj;
+      ++tj;
+    }
+    ti += tj;
+    r0 = t0 + NB * ti;
+    c0 = t0 + NB * tj;
+    return ti == tj;
+  };
+  // Every load is issued, with its row and column clamped into the matrix,
+  // so the compiler can count outstanding loads exactly and waits only for
+  // the registers each use needs.  Clamped values are not masked: output
+  // element (r, c) reads only P row r, Q row c and C(r, c), so they reach
+  // only elements with r >= d or c >= d, which are never stored (the
+  // diagonal block of workgroup 0 is masked when it goes to LDS).  A diagonal
+  // tile's Q rows are its P rows; its multiply reads P twice.
+  auto load = [&](int r0, int c0, double (&pv)[16], double (&qv)[16], f64x4 (&cv)[2][2]) {
 #pragma unroll
-  for (int q = 0; q < 16; ++q) {
-    const int i = i0 + 4 * q;
-    pv[q] = (r0 + i < d) ? A[(int64_t)(r0 + i) * lda + k + j] : 0.0;
-    qv[q] = (!diag && c0 + i < d) ? A[(int64_t)(c0 + i) * lda + k + j] : 0.0;
-  }
-  // C tile (read early so its latency overlaps the MFMA work)
-  f64x4 cv[2][2];
-#pragma unroll
-  for (int a = 0; a < 2; ++a)
-#pragma unroll
-    for (int b = 0; b < 2; ++b)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = r0 + 32 * wm + 16 * a + mfma64_row(lane, i);
-        const int c = c0 + 32 * wn + 16 * b + (lane & 15);
-        cv[a][b][i] = (r < d && c < d) ? A[(int64_t)r * lda + c] : 0.0;
-      }
-#pragma unroll
-  for (int q = 0; q < 16; ++q) {
-    Ps[i0 + 4 * q][j] = pv[q];
-    Qs[i0 + 4 * q][j] = qv[q];
-  }
-  __syncthreads();
-  f64x4 acc[2][2];
-#pragma unroll
-  for (int a = 0; a < 2; ++a)
-#pragma unroll
-    for (int b = 0; b < 2; ++b) acc[a][b] = f64x4{0.0, 0.0, 0.0, 0.0};
-  mma64_f64(Ps, diag ? Ps : Qs, NB, acc, lane, wm, wn);
-  if (!lookahead) {
+    for (int q = 0; q < 16; ++q) {
+      const int i = i0 + 4 * q;
+      pv[q] = A[(int64_t)min(r0 + i, d - 1) * lda + k + j];
+      qv[q] = A[(int64_t)min(c0 + i, d - 1) * lda + k + j];
+    }
 #pragma unroll
     for (int a = 0; a < 2; ++a)
 #pragma unroll
@@ -553,10 +542,73 @@ __global__ __launch_bounds__(256, 2) void potrf_update_kernel(double* __restrict
         for (int i = 0; i < 4; ++i) {
           const int r = r0 + 32 * wm + 16 * a + mfma64_row(lane, i);
           const int c = c0 + 32 * wn + 16 * b + (lane & 15);
-          if (r < d && c < d) A[(int64_t)r * lda + c] = cv[a][b][i] - acc[a][b][i];
+          cv[a][b][i] = A[(int64_t)min(r, d - 1) * lda + min(c, d - 1)];
         }
+  };
+  auto stage = [&](const double (&pv)[16], const double (&qv)[16]) {
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      Ps[i0 + 4 * q][j] = pv[q];
+      Qs[i0 + 4 * q][j] = qv[q];
+    }
+  };
+  double pv[16], qv[16];
+  f64x4 cv[2][2], acc[2][2];
+  int r0, c0;
+  bool diag = coords(blockIdx.x, r0, c0);
+  load(r0, c0, pv, qv, cv);
+  stage(pv, qv);
+  __syncthreads();
+  if (blockIdx.x != 0) {
+    const int stride = (int)gridDim.x - 1;
+    // One tile: issue the next tile's loads (its C tile into cvn), multiply
+    // from LDS, write this tile, then stage the next panel blocks.  The two C
+    // register sets alternate (loop unrolled by two), so no wait covers the
+    // stores just issued.
+    f64x4 cv2[2][2];
+    int p = blockIdx.x;
+    auto step = [&](const f64x4 (&cvc)[2][2], f64x4 (&cvn)[2][2]) {
+      const int pn = p + stride;
+      const bool more = pn < ntiles;
+      // the last step re-reads its own tile, so every step issues the same
+      // loads and the outstanding-load count stays exact
+      int r0n, c0n;
+      const bool diagn = coords(more ? pn : p, r0n, c0n);
+      load(r0n, c0n, pv, qv, cvn);
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b) acc[a][b] = f64x4{0.0, 0.0, 0.0, 0.0};
+      mma64_f64(Ps, diag ? Ps : Qs, NB, acc, lane, wm, wn);
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int r = r0 + 32 * wm + 16 * a + mfma64_row(lane, i);
+            const int c = c0 + 32 * wn + 16 * b + (lane & 15);
+            if (r < d && c < d) A[(int64_t)r * lda + c] = cvc[a][b][i] - acc[a][b][i];
+          }
+      if (!more) return false;
+      __syncthreads();  // every wave is done reading the panel tiles
+      stage(pv, qv);
+      __syncthreads();
+      r0 = r0n;
+      c0 = c0n;
+      diag = diagn;
+      p = pn;
+      return true;
+    };
+    while (step(cv, cv2) && step(cv2, cv)) {
+    }
     return;
   }
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b) acc[a][b] = f64x4{0.0, 0.0, 0.0, 0.0};
+  mma64_f64(Ps, Ps, NB, acc, lane, wm, wn);
   // workgroup 0: the updated diagonal block of the next panel goes to sh.S
   // (rows past the matrix become identity), then it is factored in place
   const int kb = min(NB, d - t0);
@@ -981,6 +1033,20 @@ __global__ __launch_bounds__(256) void store_upper_kernel(const double* __restri
   }
 }
 
+// Compute units of the current device (cached per device id).
+int device_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] <= 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
 }  // namespace
 
 hipError_t launch_damp_to_f64(const float* H, int d, double percdamp, double* A, int* flag,
@@ -1017,9 +1083,12 @@ hipError_t launch_potrf_update(double* A, int lda, int d, int k, int ncol, int* 
   if (nt <= 0 || ncol <= 0) return hipSuccess;
   const int64_t nc = ncol < nt ? ncol : nt;
   const int64_t tiles = nc * nt - nc * (nc - 1) / 2;
+  // two resident workgroups per CU (the LDS of the diagonal factorization)
+  const int64_t cap = 2 * (int64_t)device_cus();
+  const int64_t grid = tiles < cap ? tiles : cap;
   const int kn = k + NB;
-  hipLaunchKernelGGL(potrf_update_kernel, dim3((unsigned)tiles), dim3(256), 0, s, A, lda, d, k,
-                     (int)nt, flag, info_offset, Xi + (int64_t)kn * ldxi + kn, ldxi);
+  hipLaunchKernelGGL(potrf_update_kernel, dim3((unsigned)grid), dim3(256), 0, s, A, lda, d, k,
+                     (int)nt, (int)tiles, flag, info_offset, Xi + (int64_t)kn * ldxi + kn, ldxi);
   return hipGetLastError();
 }
 
