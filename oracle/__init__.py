@@ -19,4 +19,7 @@ from .gptq64 import (  # noqa: F401
     dequantize,
     output_error,
     layer_objective,
+    act_order_perm,
+    gptq_act_order,
+    dequantize_gidx,
 )

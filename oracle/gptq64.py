@@ -279,3 +279,76 @@ def layer_objective(W: np.ndarray, W_hat: np.ndarray, Hd: np.ndarray) -> np.ndar
     """Per-row 1/2 dw H_d dw^T (the quantity the per-column losses add up to)."""
     dW = np.asarray(W, np.float64) - np.asarray(W_hat, np.float64)
     return 0.5 * np.einsum("ij,jk,ik->i", dW, Hd, dW, optimize=True)
+
+
+# --------------------------------------------------------------------------
+# Act-order (desc_act): columns processed in decreasing order of H_qq
+#   "GPTQ: fixing errors as you go", "The tricks that make it fast" (the
+#   act-order addition: largest H_qq first, while many columns remain to
+#   absorb the error); "GPTQ > The GPTQ Algorithm", the note on quantization
+#   order (ActOrder = decreasing Hessian diagonal); "GPTQ, Line by Line", the
+#   AutoGPTQ configuration (desc_act).
+# Readings of what the pages leave open (also in the design notes):
+#   * ties in H_qq keep the original column order (a stable sort), so the
+#     order is a function of the diagonal alone;
+#   * the whole problem is carried into the processing order: W's columns
+#     and H's rows and columns are permuted, then GPTQ runs unchanged;
+#   * groups are runs of `groupsize` consecutive columns in processing
+#     order; scales and zeros are indexed by those groups, and g_idx maps
+#     each original column to its group;
+#   * codes, losses (and the trace) are returned in the original column
+#     order.
+# --------------------------------------------------------------------------
+def act_order_perm(diag) -> np.ndarray:
+    """perm[k] = the original column processed k-th: decreasing diagonal,
+    ties by increasing column index. The diagonal must be free of NaN."""
+    h = np.asarray(diag, dtype=np.float64).ravel()
+    return np.array(sorted(range(h.size), key=lambda c: (-h[c], c)), dtype=np.int64)
+
+
+def gptq_act_order(W: np.ndarray, H: np.ndarray, percdamp: float = 0.01, bits: int = 4,
+                   groupsize: int = 128, blocksize: int = 128, precision: str = "f64",
+                   diag: Optional[np.ndarray] = None, trace: bool = False,
+                   tie_distance: bool = False):
+    """GPTQ with act-order. `diag` (default: diag(H)) is the sort key; pass
+    the diagonal as the GPU reads it (fp32) when the order must match.
+
+    Returns dict(codes, losses[, trace][, tie_distance]) in original column
+    order, scales and zeros per processing-order group, g_idx (cols), perm,
+    and U, the Hinv of the permuted problem (its row k belongs to the
+    original column perm[k])."""
+    W = np.asarray(W, dtype=np.float64)
+    H = np.asarray(H, dtype=np.float64)
+    rows, cols = W.shape
+    perm = act_order_perm(np.diag(H) if diag is None else diag)
+    U, lam = hinv_upper(H[np.ix_(perm, perm)], percdamp)
+    r = gptq(W[:, perm], U, bits, groupsize, blocksize, precision, trace=trace,
+             tie_distance=tie_distance)
+    g = cols if groupsize <= 0 else groupsize
+    codes = np.empty_like(r["codes"])
+    codes[:, perm] = r["codes"]
+    losses = np.empty(cols)
+    losses[perm] = r["losses"]
+    g_idx = np.empty(cols, dtype=np.int64)
+    g_idx[perm] = np.arange(cols) // g
+    out = dict(codes=codes, scales=r["scales"], zeros=r["zeros"], losses=losses,
+               g_idx=g_idx, perm=perm, U=U, lam=lam)
+    if trace:
+        states = []
+        for S in r["trace"]:
+            T = np.empty_like(S)
+            T[:, perm] = S
+            states.append(T)
+        out["trace"] = states
+    if tie_distance:
+        td = np.empty_like(r["tie_distance"])
+        td[:, perm] = r["tie_distance"]
+        out["tie_distance"] = td
+    return out
+
+
+def dequantize_gidx(codes: np.ndarray, scales: np.ndarray, zeros: np.ndarray,
+                    g_idx: np.ndarray) -> np.ndarray:
+    """W_hat[:, c] = (code - zero[g_idx[c]]) * scale[g_idx[c]]."""
+    gi = np.asarray(g_idx, dtype=np.int64)
+    return (codes.astype(np.float64) - zeros[:, gi]) * scales[:, gi]
