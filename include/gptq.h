@@ -11,6 +11,10 @@
  *   gptq_quantize_layer      blocked column sweep + lazy updates -> codes,
  *                            scales, zeros, per-column losses
  *
+ * and the act-order variant (columns in decreasing order of H_qq):
+ *
+ *   gptq_act_order, gptq_prepare_hinv_perm, gptq_quantize_layer_perm
+ *
  * Sources (page titles and sections):
  *   "GPTQ: fixing errors as you go": "The algorithm, in words", "Objective",
  *       "The OBQ update", "The tricks that make it fast".
@@ -63,7 +67,8 @@ enum gptq_dtype { GPTQ_DTYPE_F16 = 0, GPTQ_DTYPE_F32 = 1 };
 enum gptq_op {
   GPTQ_OP_ACCUMULATE = 0, /* sizes: rows ignored, cols = d, n = tokens         */
   GPTQ_OP_PREPARE = 1,    /* sizes: rows ignored, cols = d, n ignored          */
-  GPTQ_OP_QUANTIZE = 2    /* sizes: rows, cols, n ignored                       */
+  GPTQ_OP_QUANTIZE = 2,   /* sizes: rows, cols, n ignored                       */
+  GPTQ_OP_QUANTIZE_PERM = 3 /* gptq_quantize_layer_perm: rows, cols, n ignored    */
 };
 
 /* Library version (major*10000 + minor*100 + patch). */
@@ -174,6 +179,83 @@ gptq_status gptq_quantize_layer(const void* W, int w_dtype, int64_t rows, int64_
                                 int blocksize, uint8_t* codes, float* scales, float* zeros,
                                 float* losses, void* workspace, size_t workspace_bytes,
                                 void* stream);
+
+/*
+ * Act-order (desc_act): columns processed in decreasing order of the Hessian
+ * diagonal H_qq, the most sensitive inputs first while many columns remain to
+ * absorb their error ("GPTQ: fixing errors as you go", "The tricks that make
+ * it fast"; "GPTQ > The GPTQ Algorithm", the note on quantization order;
+ * "GPTQ, Line by Line", the desc_act field of the AutoGPTQ configuration).
+ * The pages fix only the order.  This library also fixes:
+ *   - ties keep the original column order (the order depends on the
+ *     diagonal values alone);
+ *   - the whole problem is carried into the processing order: H's rows and
+ *     columns and W's columns are permuted, then the path runs unchanged;
+ *   - groups are runs of `groupsize` consecutive columns in processing order;
+ *   - codes and losses are returned in the original column order, with
+ *     g_idx[c] the group of original column c.
+ * A layer call is gptq_act_order, gptq_prepare_hinv_perm, then
+ * gptq_quantize_layer_perm with the same perm (layers that share H share
+ * perm and Hinv).
+ */
+
+/*
+ * gptq_act_order -- perm[k] = the original column processed k-th: decreasing
+ * H[c][c], ties by increasing c.
+ *
+ *   H      d x d fp32; only the diagonal is read.  Values are compared in
+ *          IEEE total order with -0 equal to +0; a NaN diagonal entry gets a
+ *          defined but unspecified place (perm is always a permutation).
+ *   perm   d int32 out (device).
+ *   Asynchronous; bitwise deterministic.
+ */
+gptq_status gptq_act_order(const float* H, int64_t d, int32_t* perm, void* stream);
+
+/*
+ * gptq_prepare_hinv_perm -- gptq_prepare_hinv of P H P^T, (P H P^T)[i][j] =
+ * H[perm[i]][perm[j]]: Hinv is the upper Cholesky factor of the damped,
+ * permuted Hessian's inverse, in processing order (row k belongs to original
+ * column perm[k]).  lambda = percdamp * mean(diag H) does not depend on the
+ * order.
+ *
+ *   H      d x d fp32 with BOTH triangles (as gptq_hessian_accumulate leaves
+ *          it); not modified.
+ *   perm   d int32 (device), a permutation of [0, d); NULL means the
+ *          identity.  It is checked on the device: if it is not a
+ *          permutation the call returns GPTQ_ERR_INVALID_ARG (after the
+ *          work, which reads perm clamped into [0, d)) and Hinv is undefined.
+ *   Other arguments, the workspace (GPTQ_OP_PREPARE), the single stream
+ *   synchronization and the NOT_PD reporting are those of gptq_prepare_hinv;
+ *   pivot indices refer to the processing order.
+ */
+gptq_status gptq_prepare_hinv_perm(const float* H, int64_t d, const int32_t* perm,
+                                   double percdamp, float* Hinv, void* workspace,
+                                   size_t workspace_bytes, int64_t* info, void* stream);
+
+/*
+ * gptq_quantize_layer_perm -- gptq_quantize_layer on the columns of W taken
+ * in the order perm, with the outputs returned in W's own column order.
+ *
+ *   perm       cols int32 (device), the permutation given to
+ *              gptq_prepare_hinv_perm (which checks it).  Entries are
+ *              clamped into [0, cols), so a bad perm gives undefined results
+ *              but no access outside the buffers.  NULL means the identity.
+ *   Hinv       from gptq_prepare_hinv_perm with the same perm.
+ *   codes      rows x cols uint8 out, column c = original column c.
+ *   scales,    rows x ceil(cols / groupsize) fp32 out; group k covers the
+ *   zeros      processed columns perm[k*groupsize .. (k+1)*groupsize - 1].
+ *   losses     cols fp32 out, losses[c] for original column c.
+ *   g_idx      cols int32 out (may be NULL): group of original column c, so
+ *              w_hat[r][c] = (codes[r][c] - zeros[r][g_idx[c]]) *
+ *              scales[r][g_idx[c]].
+ *   workspace  gptq_workspace_bytes(GPTQ_OP_QUANTIZE_PERM, rows, cols, 0).
+ *   Other arguments and behaviour as gptq_quantize_layer.  Asynchronous.
+ */
+gptq_status gptq_quantize_layer_perm(const void* W, int w_dtype, int64_t rows, int64_t cols,
+                                     int64_t ldw, const int32_t* perm, const float* Hinv,
+                                     int bits, int groupsize, int blocksize, uint8_t* codes,
+                                     float* scales, float* zeros, float* losses, int32_t* g_idx,
+                                     void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -18,10 +18,14 @@ from ._lib import (  # noqa: F401
     OP_ACCUMULATE,
     OP_PREPARE,
     OP_QUANTIZE,
+    OP_QUANTIZE_PERM,
+    act_order,
     hessian_accumulate,
     lib,
     prepare_hinv,
+    prepare_hinv_perm,
     quantize_layer,
+    quantize_layer_perm,
     status_string,
     version,
     workspace_bytes,

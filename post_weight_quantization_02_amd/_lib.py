@@ -26,6 +26,7 @@ GPTQ_DTYPE_F32 = 1
 OP_ACCUMULATE = 0
 OP_PREPARE = 1
 OP_QUANTIZE = 2
+OP_QUANTIZE_PERM = 3
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
@@ -58,6 +59,14 @@ lib.gptq_prepare_hinv.argtypes = [_p, _i64, ctypes.c_double, _p, _p, _sz,
 lib.gptq_quantize_layer.restype = _int
 lib.gptq_quantize_layer.argtypes = [_p, _int, _i64, _i64, _i64, _p, _int, _int, _int,
                                     _p, _p, _p, _p, _p, _sz, _p]
+lib.gptq_act_order.restype = _int
+lib.gptq_act_order.argtypes = [_p, _i64, _p, _p]
+lib.gptq_prepare_hinv_perm.restype = _int
+lib.gptq_prepare_hinv_perm.argtypes = [_p, _i64, _p, ctypes.c_double, _p, _p, _sz,
+                                       ctypes.POINTER(ctypes.c_int64), _p]
+lib.gptq_quantize_layer_perm.restype = _int
+lib.gptq_quantize_layer_perm.argtypes = [_p, _int, _i64, _i64, _i64, _p, _p, _int, _int, _int,
+                                         _p, _p, _p, _p, _p, _p, _sz, _p]
 
 
 class GPTQError(RuntimeError):
@@ -138,21 +147,64 @@ def hessian_accumulate(H, X, alpha: float = 2.0, workspace=None, stream=None):
     return H
 
 
-def prepare_hinv(H, percdamp: float = 0.01, out=None, workspace=None, stream=None):
-    """Hinv (d x d fp32, upper triangular) from H. Raises GPTQError with
-    status GPTQ_ERR_NOT_PD and the failing pivot in .info."""
+def _check_H(H):
     torch = _torch()
     if H.dtype != torch.float32 or not H.is_cuda or not H.is_contiguous() or H.dim() != 2:
         raise ValueError("H must be a contiguous fp32 CUDA tensor")
-    d = H.shape[0]
+    if H.shape[0] != H.shape[1]:
+        raise ValueError("H must be square")
+    return H.shape[0]
+
+
+def _check_perm(perm, n, device):
+    torch = _torch()
+    if perm is None:
+        return None
+    if perm.dtype != torch.int32 or perm.device != device or perm.shape != (n,) or \
+            not perm.is_contiguous():
+        raise ValueError(f"perm must be a contiguous int32 tensor of length {n} on {device}")
+    return perm
+
+
+def prepare_hinv(H, percdamp: float = 0.01, out=None, workspace=None, stream=None):
+    """Hinv (d x d fp32, upper triangular) from H. Raises GPTQError with
+    status GPTQ_ERR_NOT_PD and the failing pivot in .info."""
+    return prepare_hinv_perm(H, None, percdamp, out, workspace, stream)
+
+
+def act_order(H, out=None, stream=None):
+    """perm (d int32): the columns in decreasing order of H's diagonal, ties
+    by index (gptq_act_order)."""
+    torch = _torch()
+    d = _check_H(H)
+    if out is None:
+        out = torch.empty((d,), dtype=torch.int32, device=H.device)
+    _check_perm(out, d, H.device)
+    st = lib.gptq_act_order(H.data_ptr(), d, out.data_ptr(), _stream_ptr(stream, H.device))
+    _check(st, "gptq_act_order")
+    return out
+
+
+def prepare_hinv_perm(H, perm, percdamp: float = 0.01, out=None, workspace=None, stream=None):
+    """Hinv of H with rows and columns taken in the order perm (None: the
+    identity, i.e. gptq_prepare_hinv). H must hold both triangles."""
+    torch = _torch()
+    d = _check_H(H)
+    perm = _check_perm(perm, d, H.device)
     if out is None:
         out = torch.empty((d, d), dtype=torch.float32, device=H.device)
     ws, wsb = _workspace(workspace_bytes(OP_PREPARE, 0, d, 0), H.device, workspace)
     info = ctypes.c_int64(0)
-    st = lib.gptq_prepare_hinv(H.data_ptr(), d, float(percdamp), out.data_ptr(),
-                               ws.data_ptr(), wsb, ctypes.byref(info),
-                               _stream_ptr(stream, H.device))
-    _check(st, "gptq_prepare_hinv", info.value)
+    st_ptr = _stream_ptr(stream, H.device)
+    if perm is None:
+        st = lib.gptq_prepare_hinv(H.data_ptr(), d, float(percdamp), out.data_ptr(),
+                                   ws.data_ptr(), wsb, ctypes.byref(info), st_ptr)
+        _check(st, "gptq_prepare_hinv", info.value)
+    else:
+        st = lib.gptq_prepare_hinv_perm(H.data_ptr(), d, perm.data_ptr(), float(percdamp),
+                                        out.data_ptr(), ws.data_ptr(), wsb, ctypes.byref(info),
+                                        st_ptr)
+        _check(st, "gptq_prepare_hinv_perm", info.value)
     return out
 
 
@@ -190,3 +242,46 @@ def quantize_layer(W, Hinv, bits: int = 4, groupsize: int = 128, blocksize: int 
                                  _stream_ptr(stream, dev))
     _check(st, "gptq_quantize_layer")
     return codes, scales, zeros, losses
+
+
+def quantize_layer_perm(W, perm, Hinv, bits: int = 4, groupsize: int = 128, blocksize: int = 128,
+                        out=None, workspace=None, stream=None):
+    """Act-order sweep: W's columns processed in the order perm, with Hinv
+    from prepare_hinv_perm(H, perm). Returns (codes, scales, zeros, losses,
+    g_idx): codes, losses and g_idx (int32) in W's column order, scales and
+    zeros per processing-order group."""
+    torch = _torch()
+    if W.dim() != 2 or W.stride(1) != 1 or not W.is_cuda:
+        raise ValueError("W must be a 2-D CUDA tensor with unit column stride")
+    if W.dtype == torch.float16:
+        wdt = GPTQ_DTYPE_F16
+    elif W.dtype == torch.float32:
+        wdt = GPTQ_DTYPE_F32
+    else:
+        raise ValueError("W must be fp16 or fp32")
+    rows, cols = W.shape
+    perm = _check_perm(perm, cols, W.device)
+    if Hinv.shape != (cols, cols) or Hinv.dtype != torch.float32 or not Hinv.is_contiguous():
+        raise ValueError("Hinv must be a contiguous cols x cols fp32 tensor")
+    g = groupsize
+    ng = (cols + g - 1) // g
+    dev = W.device
+    if out is None:
+        codes = torch.empty((rows, cols), dtype=torch.uint8, device=dev)
+        scales = torch.empty((rows, ng), dtype=torch.float32, device=dev)
+        zeros = torch.empty((rows, ng), dtype=torch.float32, device=dev)
+        losses = torch.empty((cols,), dtype=torch.float32, device=dev)
+        g_idx = torch.empty((cols,), dtype=torch.int32, device=dev)
+    else:
+        codes, scales, zeros, losses, g_idx = out
+    ws, wsb = _workspace(workspace_bytes(OP_QUANTIZE_PERM, rows, cols, 0), dev, workspace)
+    ldw = W.stride(0) if rows > 1 else cols
+    st = lib.gptq_quantize_layer_perm(W.data_ptr(), wdt, rows, cols, ldw,
+                                      perm.data_ptr() if perm is not None else None,
+                                      Hinv.data_ptr(), bits, groupsize, blocksize,
+                                      codes.data_ptr(), scales.data_ptr(), zeros.data_ptr(),
+                                      losses.data_ptr(),
+                                      g_idx.data_ptr() if g_idx is not None else None,
+                                      ws.data_ptr(), wsb, _stream_ptr(stream, dev))
+    _check(st, "gptq_quantize_layer_perm")
+    return codes, scales, zeros, losses, g_idx

@@ -91,6 +91,25 @@ __global__ __launch_bounds__(256) void damp_copy_kernel(const float* __restrict_
   }
 }
 
+// Act-order variant: A = P H P^T + lambda I with (P H P^T)[i][j] =
+// H[perm[i]][perm[j]], lower triangle.  Row perm[i] of H is contiguous, so the
+// gathered columns of one row stay in cache; H must hold both triangles.
+// perm entries are clamped into [0, d).
+__global__ __launch_bounds__(256) void damp_copy_perm_kernel(const float* __restrict__ H, int d,
+                                                             const int* __restrict__ perm,
+                                                             const double* lam,
+                                                             double* __restrict__ A) {
+  const int64_t i = blockIdx.x;
+  const double l = *lam;
+  const int64_t pi = min(max(perm[i], 0), d - 1);
+  const float* hrow = H + pi * d;
+  for (int64_t j = threadIdx.x; j <= i; j += 256) {
+    double v = (double)hrow[min(max(perm[j], 0), d - 1)];
+    if (j == i) v += l;
+    A[i * d + j] = v;
+  }
+}
+
 // Row of the 16x16 fp64 MFMA result held in element i of lane `lane`
 // (the fp64 variant interleaves rows: lane/16, lane/16 + 4, ...).
 __device__ inline int mfma64_row(int lane, int i) { return (lane >> 4) + 4 * i; }
@@ -1049,14 +1068,18 @@ int device_cus() {
 
 }  // namespace
 
-hipError_t launch_damp_to_f64(const float* H, int d, double percdamp, double* A, int* flag,
-                              hipStream_t s) {
+hipError_t launch_damp_to_f64(const float* H, int d, double percdamp, const int* perm, double* A,
+                              int* flag, hipStream_t s) {
   double* lam = reinterpret_cast<double*>(reinterpret_cast<char*>(flag) + 8);
   hipLaunchKernelGGL(damp_lambda_kernel, dim3(1), dim3(256), 0, s, H, d, percdamp, lam, flag);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(damp_copy_kernel, dim3((unsigned)d), dim3(256), 0, s, H, d,
-                     (const double*)lam, A);
+  if (perm != nullptr)
+    hipLaunchKernelGGL(damp_copy_perm_kernel, dim3((unsigned)d), dim3(256), 0, s, H, d, perm,
+                       (const double*)lam, A);
+  else
+    hipLaunchKernelGGL(damp_copy_kernel, dim3((unsigned)d), dim3(256), 0, s, H, d,
+                       (const double*)lam, A);
   return hipGetLastError();
 }
 

@@ -39,8 +39,9 @@ int64_t syrk_kper(int64_t n, int splits);
 constexpr int kSyrkTile = 256;
 
 // fp64 Cholesky route
-hipError_t launch_damp_to_f64(const float* H, int d, double percdamp, double* A, int* flag,
-                              hipStream_t s);
+// perm == nullptr: A = H + lambda I; else A = P H P^T + lambda I (act-order)
+hipError_t launch_damp_to_f64(const float* H, int d, double percdamp, const int* perm, double* A,
+                              int* flag, hipStream_t s);
 // Cholesky of panel k's 64x64 diagonal block, with its inverse stored in Xi
 hipError_t launch_potrf_diag(double* A, int lda, int d, int k, int* flag, int info_offset,
                              double* Xi, int ldxi, hipStream_t s);
@@ -61,8 +62,9 @@ constexpr int kPanel = 64;
 constexpr int kOuterPanel = 512;  // columns per outer block of the two-level Cholesky
 
 // sweep
+// perm != nullptr gathers W's columns into processing order (act-order)
 hipError_t launch_convert_w(const void* W, int w_dtype, int64_t rows, int64_t cols, int64_t ldw,
-                            float* Wk, int64_t ldk, hipStream_t s);
+                            const int* perm, float* Wk, int64_t ldk, hipStream_t s);
 // sweep of the block at column i1; with p0 < i1 (groups inside blocks), the
 // pending errors of blocks [p0, i1) are applied to the block first
 hipError_t launch_sweep_block(float* Wk, int64_t ldk, int64_t rows, int64_t cols, int i1, int p0,
@@ -73,6 +75,15 @@ hipError_t launch_lazy_update(float* Wk, int64_t ldk, int64_t rows, int64_t cols
                               int c0, int c1, const float* Err, const float* Hinv, hipStream_t s);
 hipError_t launch_loss_reduce(const float* loss_part, int64_t nparts, int64_t cols,
                               float* losses, hipStream_t s);
+// act-order
+hipError_t launch_act_order(const float* H, int64_t d, int* perm, hipStream_t s);
+// *bad = 0 if perm is a permutation of [0, n), else 1 (inv: n ints of scratch)
+hipError_t launch_perm_check(const int* perm, int64_t n, int* inv, int* bad, hipStream_t s);
+hipError_t launch_perm_inverse(const int* perm, int64_t n, int* inv, hipStream_t s);
+hipError_t launch_unpermute_outputs(const uint8_t* cp, int64_t rows, int64_t cols, const int* inv,
+                                    uint8_t* codes, const float* lp, float* losses, int g,
+                                    int* g_idx, hipStream_t s);
+hipError_t launch_group_index(int64_t cols, int g, int* g_idx, hipStream_t s);
 constexpr int kSweepRows = 16;  // rows per sweep workgroup
 constexpr int kBlock = 128;     // columns per block
 constexpr int kSuperBlock = 512;  // columns per superblock of the two-level lazy update

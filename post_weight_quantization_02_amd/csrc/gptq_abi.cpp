@@ -38,6 +38,8 @@ struct QuantLayout {
   int64_t ldk;        // row stride of the fp32 working copy and of Err
   size_t wk_off, err_off, loss_off, total;
   int64_t nparts;     // loss partial rows
+  // act-order: codes and losses in processing order, and the inverse order
+  size_t cp_off, lp_off, inv_off, total_perm;
 };
 
 QuantLayout quant_layout(int64_t rows, int64_t cols) {
@@ -48,12 +50,17 @@ QuantLayout quant_layout(int64_t rows, int64_t cols) {
   L.err_off = L.wk_off + align_up((size_t)rows * L.ldk * sizeof(float));
   L.loss_off = L.err_off + align_up((size_t)rows * L.ldk * sizeof(float));
   L.total = L.loss_off + align_up((size_t)L.nparts * L.ldk * sizeof(float));
+  L.cp_off = L.total;
+  L.lp_off = L.cp_off + align_up((size_t)rows * cols);
+  L.inv_off = L.lp_off + align_up((size_t)cols * sizeof(float));
+  L.total_perm = L.inv_off + align_up((size_t)cols * sizeof(int));
   return L;
 }
 
-size_t quant_bytes(int64_t rows, int64_t cols) {
+size_t quant_bytes(int64_t rows, int64_t cols, bool perm) {
   if (rows < 1 || cols < 1 || rows > kMaxDim || cols > kMaxDim) return 0;
-  return quant_layout(rows, cols).total;
+  const QuantLayout L = quant_layout(rows, cols);
+  return perm ? L.total_perm : L.total;
 }
 
 bool group_ok(int g) {
@@ -119,7 +126,8 @@ size_t gptq_workspace_bytes(int op, int64_t rows, int64_t cols, int64_t n) {
   switch (op) {
     case GPTQ_OP_ACCUMULATE: return acc_bytes(cols, n);
     case GPTQ_OP_PREPARE: return prep_bytes(cols);
-    case GPTQ_OP_QUANTIZE: return quant_bytes(rows, cols);
+    case GPTQ_OP_QUANTIZE: return quant_bytes(rows, cols, false);
+    case GPTQ_OP_QUANTIZE_PERM: return quant_bytes(rows, cols, true);
     default: return 0;
   }
 }
@@ -146,13 +154,18 @@ gptq_status gptq_hessian_accumulate(float* H, int64_t d, const void* X, int64_t 
   return GPTQ_OK;
 }
 
-gptq_status gptq_prepare_hinv(const float* H, int64_t d, double percdamp, float* Hinv,
-                              void* workspace, size_t workspace_bytes, int64_t* info,
-                              void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The preparation with an optional act-order permutation (perm == nullptr:
+// the identity).  Validation of the scalar arguments is done by the callers.
+gptq_status prepare_impl(const float* H, int64_t d, const int* perm, double percdamp, float* Hinv,
+                         void* workspace, size_t workspace_bytes, int64_t* info, void* stream) {
   if (info) *info = 0;
   if (d < 1 || d > 65536 || H == nullptr || Hinv == nullptr) return GPTQ_ERR_INVALID_ARG;
   if (!(percdamp >= 0.0) || percdamp > 1e6) return GPTQ_ERR_INVALID_ARG;
-  if (!aligned(H, 4) || !aligned(Hinv, 4)) return GPTQ_ERR_INVALID_ARG;
+  if (!aligned(H, 4) || !aligned(Hinv, 4) || !aligned(perm, 4)) return GPTQ_ERR_INVALID_ARG;
   const size_t need = prep_bytes(d);
   if (workspace == nullptr || workspace_bytes < need) return GPTQ_ERR_WORKSPACE;
   if (!aligned(workspace, kAlign)) return GPTQ_ERR_INVALID_ARG;
@@ -161,15 +174,20 @@ gptq_status gptq_prepare_hinv(const float* H, int64_t d, double percdamp, float*
   const size_t mat = align_up((size_t)d * d * sizeof(double));
   double* A = reinterpret_cast<double*>(workspace);
   double* Xi = reinterpret_cast<double*>(reinterpret_cast<char*>(workspace) + mat);
+  // flag words: [0] pivot flag (int), [8] lambda (double), [16] perm check (int)
   int* flag = reinterpret_cast<int*>(reinterpret_cast<char*>(workspace) + 2 * mat);
+  int* permbad = reinterpret_cast<int*>(reinterpret_cast<char*>(flag) + 16);
 
 #define GPTQ_TRY(call) \
   do {                 \
     if ((call) != hipSuccess) return GPTQ_ERR_HIP; \
   } while (0)
 
-  // A = H + lambda I (fp64, lower triangle); resets the pivot flag.
-  GPTQ_TRY(launch_damp_to_f64(H, di, percdamp, A, flag, s));
+  // act-order: check that perm is a permutation (Xi is free scratch until the
+  // first factorization writes its block inverses)
+  if (perm != nullptr) GPTQ_TRY(launch_perm_check(perm, d, reinterpret_cast<int*>(Xi), permbad, s));
+  // A = H + lambda I, or P H P^T + lambda I (fp64, lower triangle); resets the pivot flag.
+  GPTQ_TRY(launch_damp_to_f64(H, di, percdamp, perm, A, flag, s));
   // L = chol(A), in place; the inverted 64x64 diagonal blocks of L land in Xi.
   GPTQ_TRY(potrf(A, di, flag, 0, Xi, s));
   // Xi = L^{-1}: combine the inverted diagonal blocks level by level
@@ -180,22 +198,27 @@ gptq_status gptq_prepare_hinv(const float* H, int64_t d, double percdamp, float*
   GPTQ_TRY(potrf(A, di, flag, di, Xi, s));
   // Hinv = L2^T (upper), fp32
   GPTQ_TRY(launch_store_upper_f32(A, di, Hinv, di, s));
-  int hflag = 0;
-  GPTQ_TRY(hipMemcpyAsync(&hflag, flag, sizeof(int), hipMemcpyDeviceToHost, s));
+  int hflag[5] = {0, 0, 0, 0, 0};
+  GPTQ_TRY(hipMemcpyAsync(hflag, flag, sizeof(hflag), hipMemcpyDeviceToHost, s));
   GPTQ_TRY(hipStreamSynchronize(s));
 #undef GPTQ_TRY
-  if (hflag != 0x7fffffff) {
-    if (info) *info = hflag;
+  if (perm != nullptr && hflag[4] != 0) return GPTQ_ERR_INVALID_ARG;
+  if (hflag[0] != 0x7fffffff) {
+    if (info) *info = hflag[0];
     return GPTQ_ERR_NOT_PD;
   }
   return GPTQ_OK;
 }
 
-gptq_status gptq_quantize_layer(const void* W, int w_dtype, int64_t rows, int64_t cols,
-                                int64_t ldw, const float* Hinv, int bits, int groupsize,
-                                int blocksize, uint8_t* codes, float* scales, float* zeros,
-                                float* losses, void* workspace, size_t workspace_bytes,
-                                void* stream) {
+// The sweep with an optional act-order permutation.  With perm, W's columns
+// are gathered into processing order, the sweep's codes and losses go to the
+// workspace, and one kernel writes them back in the original column order
+// together with g_idx.
+gptq_status quantize_impl(const void* W, int w_dtype, int64_t rows, int64_t cols, int64_t ldw,
+                          const int* perm, const float* Hinv, int bits, int groupsize,
+                          int blocksize, uint8_t* codes, float* scales, float* zeros,
+                          float* losses, int* g_idx, void* workspace, size_t workspace_bytes,
+                          void* stream) {
   if (rows < 1 || cols < 1 || rows > kMaxDim || cols > kMaxDim || ldw < cols)
     return GPTQ_ERR_INVALID_ARG;
   if (W == nullptr || Hinv == nullptr || codes == nullptr || scales == nullptr ||
@@ -209,19 +232,25 @@ gptq_status gptq_quantize_layer(const void* W, int w_dtype, int64_t rows, int64_
   if (groupsize % blocksize != 0 && blocksize % groupsize != 0) return GPTQ_ERR_INVALID_ARG;
   if (rows > kMaxElems / ldw) return GPTQ_ERR_INVALID_ARG;
   if (!aligned(W, w_dtype == GPTQ_DTYPE_F16 ? 2 : 4) || !aligned(Hinv, 4) ||
-      !aligned(scales, 4) || !aligned(zeros, 4) || !aligned(losses, 4))
+      !aligned(scales, 4) || !aligned(zeros, 4) || !aligned(losses, 4) || !aligned(perm, 4) ||
+      !aligned(g_idx, 4))
     return GPTQ_ERR_INVALID_ARG;
   if (blocksize != kBlock || !group_ok(groupsize)) return GPTQ_ERR_UNSUPPORTED;
   const QuantLayout L = quant_layout(rows, cols);
-  if (workspace == nullptr || workspace_bytes < L.total) return GPTQ_ERR_WORKSPACE;
+  const size_t need = perm != nullptr ? L.total_perm : L.total;
+  if (workspace == nullptr || workspace_bytes < need) return GPTQ_ERR_WORKSPACE;
   if (!aligned(workspace, kAlign)) return GPTQ_ERR_INVALID_ARG;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   char* ws = reinterpret_cast<char*>(workspace);
   float* Wk = reinterpret_cast<float*>(ws + L.wk_off);
   float* Err = reinterpret_cast<float*>(ws + L.err_off);
   float* lpart = reinterpret_cast<float*>(ws + L.loss_off);
+  // with act-order the sweep writes processing-order codes and losses here
+  uint8_t* sweep_codes = perm != nullptr ? reinterpret_cast<uint8_t*>(ws + L.cp_off) : codes;
+  float* sweep_losses = perm != nullptr ? reinterpret_cast<float*>(ws + L.lp_off) : losses;
 
-  if (launch_convert_w(W, w_dtype, rows, cols, ldw, Wk, L.ldk, s) != hipSuccess) return GPTQ_ERR_HIP;
+  if (launch_convert_w(W, w_dtype, rows, cols, ldw, perm, Wk, L.ldk, s) != hipSuccess)
+    return GPTQ_ERR_HIP;
   // Two-level lazy batching.  Inside a superblock of SB columns each block's
   // errors reach the rest of the superblock before those columns are swept;
   // the columns after the superblock receive all of its errors in one GEMM
@@ -242,7 +271,8 @@ gptq_status gptq_quantize_layer(const void* W, int w_dtype, int64_t rows, int64_
     for (int64_t i1 = s0; i1 < s1; i1 += kBlock) {
       const int64_t i2 = (i1 + kBlock < s1) ? i1 + kBlock : s1;
       if (launch_sweep_block(Wk, L.ldk, rows, cols, (int)i1, (int)(fused_near ? s0 : i1), Hinv,
-                             bits, groupsize, codes, scales, zeros, Err, lpart, s) != hipSuccess)
+                             bits, groupsize, sweep_codes, scales, zeros, Err, lpart, s) !=
+          hipSuccess)
         return GPTQ_ERR_HIP;
       if (!fused_near &&
           launch_lazy_update(Wk, L.ldk, rows, cols, (int)i1, (int)i2, (int)i2, (int)s1, Err, Hinv,
@@ -253,8 +283,59 @@ gptq_status gptq_quantize_layer(const void* W, int w_dtype, int64_t rows, int64_
                            s) != hipSuccess)
       return GPTQ_ERR_HIP;
   }
-  if (launch_loss_reduce(lpart, L.nparts, cols, losses, s) != hipSuccess) return GPTQ_ERR_HIP;
+  if (launch_loss_reduce(lpart, L.nparts, cols, sweep_losses, s) != hipSuccess) return GPTQ_ERR_HIP;
+  if (perm != nullptr) {
+    int* inv = reinterpret_cast<int*>(ws + L.inv_off);
+    if (launch_perm_inverse(perm, cols, inv, s) != hipSuccess) return GPTQ_ERR_HIP;
+    if (launch_unpermute_outputs(sweep_codes, rows, cols, inv, codes, sweep_losses, losses,
+                                 groupsize, g_idx, s) != hipSuccess)
+      return GPTQ_ERR_HIP;
+  } else if (g_idx != nullptr) {
+    if (launch_group_index(cols, groupsize, g_idx, s) != hipSuccess) return GPTQ_ERR_HIP;
+  }
   return GPTQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+gptq_status gptq_prepare_hinv(const float* H, int64_t d, double percdamp, float* Hinv,
+                              void* workspace, size_t workspace_bytes, int64_t* info,
+                              void* stream) {
+  return prepare_impl(H, d, nullptr, percdamp, Hinv, workspace, workspace_bytes, info, stream);
+}
+
+gptq_status gptq_quantize_layer(const void* W, int w_dtype, int64_t rows, int64_t cols,
+                                int64_t ldw, const float* Hinv, int bits, int groupsize,
+                                int blocksize, uint8_t* codes, float* scales, float* zeros,
+                                float* losses, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+  return quantize_impl(W, w_dtype, rows, cols, ldw, nullptr, Hinv, bits, groupsize, blocksize,
+                       codes, scales, zeros, losses, nullptr, workspace, workspace_bytes, stream);
+}
+
+gptq_status gptq_act_order(const float* H, int64_t d, int32_t* perm, void* stream) {
+  if (d < 1 || d > kMaxDim || H == nullptr || perm == nullptr) return GPTQ_ERR_INVALID_ARG;
+  if (!aligned(H, 4) || !aligned(perm, 4)) return GPTQ_ERR_INVALID_ARG;
+  if (launch_act_order(H, d, perm, reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
+    return GPTQ_ERR_HIP;
+  return GPTQ_OK;
+}
+
+gptq_status gptq_prepare_hinv_perm(const float* H, int64_t d, const int32_t* perm,
+                                   double percdamp, float* Hinv, void* workspace,
+                                   size_t workspace_bytes, int64_t* info, void* stream) {
+  return prepare_impl(H, d, perm, percdamp, Hinv, workspace, workspace_bytes, info, stream);
+}
+
+gptq_status gptq_quantize_layer_perm(const void* W, int w_dtype, int64_t rows, int64_t cols,
+                                     int64_t ldw, const int32_t* perm, const float* Hinv,
+                                     int bits, int groupsize, int blocksize, uint8_t* codes,
+                                     float* scales, float* zeros, float* losses, int32_t* g_idx,
+                                     void* workspace, size_t workspace_bytes, void* stream) {
+  return quantize_impl(W, w_dtype, rows, cols, ldw, perm, Hinv, bits, groupsize, blocksize,
+                       codes, scales, zeros, losses, g_idx, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -557,6 +557,19 @@ __global__ __launch_bounds__(256) void convert_kernel(const T* __restrict__ W, i
     Wk[r * ldk + c] = (c < cols) ? (float)W[r * ldw + c] : 0.f;
 }
 
+// Act-order variant: Wk[r][j] = W[r][perm[j]] (columns in processing order;
+// perm entries clamped into [0, cols)).
+template <typename T>
+__global__ __launch_bounds__(256) void convert_perm_kernel(const T* __restrict__ W, int64_t rows,
+                                                           int64_t cols, int64_t ldw,
+                                                           const int* __restrict__ perm,
+                                                           float* __restrict__ Wk, int64_t ldk) {
+  const int64_t r = blockIdx.x;
+  const int cmax = (int)(cols - 1);
+  for (int64_t c = (int64_t)blockIdx.y * 256 + threadIdx.x; c < ldk; c += (int64_t)gridDim.y * 256)
+    Wk[r * ldk + c] = (c < cols) ? (float)W[r * ldw + min(max(perm[c], 0), cmax)] : 0.f;
+}
+
 // fp16 rows whose start is 16-byte aligned (ldw % 8 == 0): 8 columns per
 // thread with one 16-byte load and two 16-byte stores.  ldk is a multiple of
 // 128, so every 8-column run of Wk is whole.
@@ -607,8 +620,17 @@ __global__ __launch_bounds__(256) void loss_reduce_kernel(const float* __restric
 }  // namespace
 
 hipError_t launch_convert_w(const void* W, int w_dtype, int64_t rows, int64_t cols, int64_t ldw,
-                            float* Wk, int64_t ldk, hipStream_t s) {
+                            const int* perm, float* Wk, int64_t ldk, hipStream_t s) {
   dim3 grid((unsigned)rows, (unsigned)((ceil_div(ldk, 256) < 16) ? ceil_div(ldk, 256) : 16));
+  if (perm != nullptr) {
+    if (w_dtype == GPTQ_DTYPE_F16)
+      hipLaunchKernelGGL(convert_perm_kernel<_Float16>, grid, dim3(256), 0, s,
+                         reinterpret_cast<const _Float16*>(W), rows, cols, ldw, perm, Wk, ldk);
+    else
+      hipLaunchKernelGGL(convert_perm_kernel<float>, grid, dim3(256), 0, s,
+                         reinterpret_cast<const float*>(W), rows, cols, ldw, perm, Wk, ldk);
+    return hipGetLastError();
+  }
   const bool v8 = (ldw % 8 == 0) && ((reinterpret_cast<uintptr_t>(W) & 15) == 0) &&
                   ((reinterpret_cast<uintptr_t>(Wk) & 15) == 0);
   if (w_dtype == GPTQ_DTYPE_F16 && v8)
