@@ -114,11 +114,12 @@ def measured_peaks(torch, dev):
     return out
 
 
-def cpu_baseline(layer, X, W, budget_s=8.0):
+def cpu_baseline(layer, X, W, budget_s=8.0, act_order=False):
     """The fp64 oracle, as it is, on a bounded sample of the same layer,
     scaled to one full layer: H on as many 8192-token chunks as fit in about
-    budget_s seconds, the full Hinv preparation, and the sweep on a doubling
-    number of rows until a call takes about budget_s seconds."""
+    budget_s seconds, the full Hinv preparation (with act-order: the order and
+    the permuted H first), and the sweep on a doubling number of rows until a
+    call takes about budget_s seconds."""
     import numpy as np
 
     import oracle
@@ -138,7 +139,12 @@ def cpu_baseline(layer, X, W, budget_s=8.0):
     Hfull = Hs * (n / toks)  # an H of the full layer's scale for timing prep and sweep
     # prep
     t0 = time.perf_counter()
-    U, _ = oracle.hinv_upper(Hfull, layer.percdamp)
+    if act_order:
+        perm = oracle.act_order_perm(np.diag(Hfull))
+        U, _ = oracle.hinv_upper(Hfull[np.ix_(perm, perm)], layer.percdamp)
+        W = W[:, perm]
+    else:
+        U, _ = oracle.hinv_upper(Hfull, layer.percdamp)
     t_p = time.perf_counter() - t0
     # sweep
     r = min(16, rows)
@@ -165,8 +171,9 @@ class Job:
     shares one Hinv.  One workspace of the largest size serves every call.
     """
 
-    def __init__(self, torch, gq, synth, groups, dev):
+    def __init__(self, torch, gq, synth, groups, dev, act_order=False):
         self.torch, self.gq = torch, gq
+        self.act_order = act_order
         self.groups = []
         ws_bytes = 0
         threads = min(16, len(os.sched_getaffinity(0)))
@@ -176,6 +183,7 @@ class Job:
             Xd = torch.from_numpy(X).to(dev)
             H = torch.empty((xs.d, xs.d), dtype=torch.float32, device=dev)
             U = torch.empty((xs.d, xs.d), dtype=torch.float32, device=dev)
+            perm = torch.empty((xs.d,), dtype=torch.int32, device=dev) if act_order else None
             ls = []
             for L in layers:
                 W = synth.weights(L.w)
@@ -184,11 +192,14 @@ class Job:
                         torch.empty((L.w.rows, ng), dtype=torch.float32, device=dev),
                         torch.empty((L.w.rows, ng), dtype=torch.float32, device=dev),
                         torch.empty((L.w.cols,), dtype=torch.float32, device=dev))
+                if act_order:
+                    outs = outs + (torch.empty((L.w.cols,), dtype=torch.int32, device=dev),)
                 ls.append((L, W, torch.from_numpy(W).to(dev), outs))
-                ws_bytes = max(ws_bytes, gq.workspace_bytes(gq.OP_QUANTIZE, L.w.rows, xs.d, 0))
+                op = gq.OP_QUANTIZE_PERM if act_order else gq.OP_QUANTIZE
+                ws_bytes = max(ws_bytes, gq.workspace_bytes(op, L.w.rows, xs.d, 0))
             ws_bytes = max(ws_bytes, gq.workspace_bytes(gq.OP_ACCUMULATE, 0, xs.d, xs.n),
                            gq.workspace_bytes(gq.OP_PREPARE, 0, xs.d, 0))
-            self.groups.append((xs, X, Xd, H, U, ls))
+            self.groups.append((xs, X, Xd, H, U, perm, ls))
         raw = torch.empty(ws_bytes + 256, dtype=torch.uint8, device=dev)
         off = (-raw.data_ptr()) % 256
         self.ws = raw[off:off + ws_bytes]
@@ -197,7 +208,7 @@ class Job:
 
     def step(self, record):
         torch, gq = self.torch, self.gq
-        for xs, X, Xd, H, U, ls in self.groups:
+        for xs, X, Xd, H, U, perm, ls in self.groups:
             H.zero_()
             e = [torch.cuda.Event(enable_timing=True) for _ in range(3)] if record else None
             if record:
@@ -205,7 +216,11 @@ class Job:
             gq.hessian_accumulate(H, Xd, 2.0, workspace=self.ws)
             if record:
                 e[1].record(self.stream)
-            gq.prepare_hinv(H, ls[0][0].percdamp, out=U, workspace=self.ws)
+            if self.act_order:
+                gq.act_order(H, out=perm)
+                gq.prepare_hinv_perm(H, perm, ls[0][0].percdamp, out=U, workspace=self.ws)
+            else:
+                gq.prepare_hinv(H, ls[0][0].percdamp, out=U, workspace=self.ws)
             if record:
                 e[2].record(self.stream)
                 self.ev["acc"].append((e[0], e[1]))
@@ -215,8 +230,12 @@ class Job:
                     q0 = torch.cuda.Event(enable_timing=True)
                     q1 = torch.cuda.Event(enable_timing=True)
                     q0.record(self.stream)
-                gq.quantize_layer(Wd, U, L.bits, L.groupsize, L.blocksize, out=outs,
-                                  workspace=self.ws)
+                if self.act_order:
+                    gq.quantize_layer_perm(Wd, perm, U, L.bits, L.groupsize, L.blocksize,
+                                           out=outs, workspace=self.ws)
+                else:
+                    gq.quantize_layer(Wd, U, L.bits, L.groupsize, L.blocksize, out=outs,
+                                      workspace=self.ws)
                 if record:
                     q1.record(self.stream)
                     self.ev["quant"].append((q0, q1))
@@ -229,6 +248,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--layer", default="attn",
                     choices=["attn", "mlp_up", "mlp_down", "tiny", "block"])
+    ap.add_argument("--act-order", action="store_true",
+                    help="process columns in decreasing order of diag(H) (desc_act)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
     ap.add_argument("--no-peaks", action="store_true", help="skip the library peak probes")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -281,12 +302,18 @@ def main():
         metric = "ms per 4096x4096 int4 g128 GPTQ layer (incl. H accumulate); % MFMA roofline"
         if args.layer != "attn":
             metric = f"ms per {rows}x{d} int{L.bits} g{L.groupsize} GPTQ layer (incl. H accumulate)"
+    if args.act_order:
+        workload += "; act-order (columns in decreasing order of diag(H), groups in that order)"
+        metric = metric.replace(" GPTQ layer", " GPTQ layer with act-order").replace(
+            " GPTQ layers", " GPTQ layers with act-order")
+        if args.layer == "block":
+            metric = metric.replace("block (", "block with act-order (")
 
     peaks = None if args.no_peaks else measured_peaks(torch, dev)
     if peaks:
         log("measured peaks:", peaks)
 
-    job = Job(torch, gq, synth, groups, dev)
+    job = Job(torch, gq, synth, groups, dev, act_order=args.act_order)
     log(f"warmup {args.warmup}")
     for _ in range(args.warmup):
         job.step(False)
@@ -304,7 +331,7 @@ def main():
 
     # algorithmic work per step
     work = dict(syrk=0.0, prep=0.0, lazy=0.0, sweep=0.0)
-    for xs, X, Xd, H, U, ls in job.groups:
+    for xs, X, Xd, H, U, _, ls in job.groups:
         w0 = algorithmic_work(0, xs.d, xs.n)
         work["syrk"] += w0["syrk"]
         work["prep"] += w0["prep"]
@@ -323,13 +350,13 @@ def main():
     acc_ms = float(np.mean(acc_calls))
     syrk_flops_call = work["syrk"] / len(job.groups)
     syrk_tflops = syrk_flops_call / (acc_ms * 1e-3) / 1e12
-    traffic = recorded_traffic() if args.layer == "attn" else None
+    traffic = recorded_traffic() if args.layer == "attn" and not args.act_order else None
 
     cpu = None
     if not args.no_cpu and args.layer != "block":
         log("cpu baseline (oracle on a bounded sample)")
         xs, X, *_ = job.groups[0]
-        cpu = cpu_baseline(layers[0], X, job.groups[0][5][0][1])
+        cpu = cpu_baseline(layers[0], X, job.groups[0][6][0][1], act_order=args.act_order)
         log("  ", cpu)
 
     line = {

@@ -184,12 +184,15 @@ def test_identity_and_null_perm_equal_the_plain_sweep(env, g):
 
 
 # ------------------------------------------------------------ end to end
-def _gpu_act_order_layer(env, W, X, bits, g, perm=None):
+def _gpu_act_order_layer(env, W, X, bits, g, perm=None, chunk=None):
+    """accumulate (one call over all tokens unless `chunk`) -> act_order (or
+    the given perm) -> prepare_hinv_perm -> quantize_layer_perm."""
     torch, gq = env
     d = X.shape[1]
     H = torch.zeros((d, d), dtype=torch.float32, device="cuda")
-    for t0 in range(0, X.shape[0], 8192):
-        gq.hessian_accumulate(H, _cuda(env, X[t0:t0 + 8192]), 2.0)
+    step = chunk or X.shape[0]
+    for t0 in range(0, X.shape[0], step):
+        gq.hessian_accumulate(H, _cuda(env, X[t0:t0 + step]), 2.0)
     p = gq.act_order(H) if perm is None else _cuda(env, perm, np.int32)
     U = gq.prepare_hinv_perm(H, p, 0.01)
     out = gq.quantize_layer_perm(_cuda(env, W), p, U, bits, g, 128)
@@ -248,9 +251,9 @@ def test_act_order_layer_end_to_end(env, name, rows, cols, n):
     W = synth.weights(L.w)
     Href = oracle.hessian([X], cols)
     ref = oracle.gptq_act_order(W, Href, 0.01, L.bits, 128, precision="f32", tie_distance=True)
-    out = _gpu_act_order_layer(env, W, X, L.bits, 128, perm=ref["perm"])
+    out = _gpu_act_order_layer(env, W, X, L.bits, 128, perm=ref["perm"], chunk=5000)
     rep = check_act_order_result(W, out, ref, 128, Href)
-    own = _gpu_act_order_layer(env, W, X, L.bits, 128)
+    own = _gpu_act_order_layer(env, W, X, L.bits, 128, chunk=5000)
     moved = check_gpu_order(own["perm"], own["H"], Href)
     Wg = oracle.dequantize_gidx(own["codes"], own["scales"].astype(np.float64),
                                 own["zeros"].astype(np.float64), own["g_idx"])

@@ -103,6 +103,30 @@ def test_full_attention_layer_sampled_rows(env, attn_inputs):
     print("attn full", rep)
 
 
+def test_full_attention_layer_act_order(env, attn_inputs):
+    """The benchmark's act-order configuration: 4096x4096 int4 g128 at
+    262144 tokens, columns in decreasing order of diag(H). Run once with the
+    oracle's order passed in (96 sampled rows compared element by element in
+    processing order) and once with the GPU's own order from its own H
+    (checked by its properties; near-equal diagonal entries may swap within
+    the fp32 accumulation error), both scored by the layer output error."""
+    from test_gpu_act_order import _gpu_act_order_layer, check_act_order_result, check_gpu_order
+    L = synth.LAYERS["attn"]
+    X, Href = attn_inputs
+    W = synth.weights(L.w)
+    rows = np.sort(np.random.default_rng(3).choice(4096, 96, replace=False))
+    ref = oracle.gptq_act_order(W[rows], Href, 0.01, 4, 128, precision="f32", tie_distance=True)
+    out = _gpu_act_order_layer(env, W, X, 4, 128, perm=ref["perm"])
+    rep = check_act_order_result(W, out, ref, 128, Href, rows=rows)
+    own = _gpu_act_order_layer(env, W, X, 4, 128)
+    moved = check_gpu_order(own["perm"], own["H"], Href)
+    Wg = oracle.dequantize_gidx(own["codes"][rows], own["scales"][rows].astype(np.float64),
+                                own["zeros"][rows].astype(np.float64), own["g_idx"])
+    e_own = oracle.output_error(W[rows], Wg, Href)
+    assert abs(e_own - rep["e_ref"]) <= 0.01 * rep["e_ref"], (e_own, rep["e_ref"])
+    print("attn full act-order", rep, "own order: positions differing", moved, "e_own", e_own)
+
+
 def test_full_mlp_up_layer_sampled_rows(env, attn_inputs):
     """11008x4096 int3 g128 on the attention activations (the MLP input has the
     same generator), full size; 96 sampled rows against the oracle."""
