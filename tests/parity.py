@@ -69,3 +69,28 @@ def assert_sweep_parity(codes, scales, zeros, ref, groupsize, **kw):
 def h_rel_error(H_gpu, H_ref):
     H_gpu = np.asarray(H_gpu, np.float64)
     return float(np.linalg.norm(H_gpu - H_ref) / np.linalg.norm(H_ref))
+
+
+# Scoring of GPU results.  These evaluate the GPU's outputs; the oracle
+# module only ever receives oracle-side data.
+def dequant(codes, scales, zeros, groupsize=None, g_idx=None):
+    """w_hat = (code - zero) * scale, with the group of column c given by
+    g_idx[c] (act-order) or c // groupsize."""
+    codes = np.asarray(codes, dtype=np.float64)
+    if g_idx is None:
+        cols = codes.shape[1]
+        g = cols if groupsize is None or groupsize <= 0 else groupsize
+        g_idx = np.arange(cols) // g
+    gi = np.asarray(g_idx, dtype=np.int64)
+    return (codes - np.asarray(zeros, np.float64)[:, gi]) * np.asarray(scales, np.float64)[:, gi]
+
+
+def output_error(W, W_hat, H):
+    """||(W - W_hat) X||^2 written with H = 2 X X^T: 1/2 tr(dW H dW^T)."""
+    dW = np.asarray(W, np.float64) - np.asarray(W_hat, np.float64)
+    return 0.5 * float(np.sum((dW @ np.asarray(H, np.float64)) * dW))
+
+
+def damped_objective(W, W_hat, Hd):
+    """Sum over rows of 1/2 dw H_d dw^T."""
+    return output_error(W, W_hat, Hd)

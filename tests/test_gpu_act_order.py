@@ -14,7 +14,7 @@ import pytest
 
 import oracle
 import synth
-from parity import assert_sweep_parity
+from parity import assert_sweep_parity, dequant, output_error
 
 pytestmark = pytest.mark.gpu
 
@@ -226,10 +226,9 @@ def check_act_order_result(W, out, ref, g, Href, rows=None):
     rep = assert_sweep_parity(sel(out["codes"])[:, perm], sel(out["scales"]),
                               sel(out["zeros"]), refp, g)
     assert np.array_equal(out["g_idx"], ref["g_idx"])
-    Wg = oracle.dequantize_gidx(sel(out["codes"]), sel(out["scales"]).astype(np.float64),
-                                sel(out["zeros"]).astype(np.float64), out["g_idx"])
+    Wg = dequant(sel(out["codes"]), sel(out["scales"]), sel(out["zeros"]), g_idx=out["g_idx"])
     Wo = oracle.dequantize_gidx(ref["codes"], ref["scales"], ref["zeros"], ref["g_idx"])
-    e_gpu = oracle.output_error(Wr, Wg, Href)
+    e_gpu = output_error(Wr, Wg, Href)
     e_ref = oracle.output_error(Wr, Wo, Href)
     assert abs(e_gpu - e_ref) <= 0.01 * e_ref, (e_gpu, e_ref)
     rep.update(e_gpu=e_gpu, e_ref=e_ref)
@@ -255,8 +254,7 @@ def test_act_order_layer_end_to_end(env, name, rows, cols, n):
     rep = check_act_order_result(W, out, ref, 128, Href)
     own = _gpu_act_order_layer(env, W, X, L.bits, 128, chunk=5000)
     moved = check_gpu_order(own["perm"], own["H"], Href)
-    Wg = oracle.dequantize_gidx(own["codes"], own["scales"].astype(np.float64),
-                                own["zeros"].astype(np.float64), own["g_idx"])
-    e_own = oracle.output_error(W, Wg, Href)
+    Wg = dequant(own["codes"], own["scales"], own["zeros"], g_idx=own["g_idx"])
+    e_own = output_error(W, Wg, Href)
     assert abs(e_own - rep["e_ref"]) <= 0.01 * rep["e_ref"], (e_own, rep["e_ref"])
     print(name, rep, "own order: positions differing from the oracle's", moved)

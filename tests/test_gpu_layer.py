@@ -5,7 +5,7 @@ import pytest
 
 import oracle
 import synth
-from parity import assert_sweep_parity, h_rel_error
+from parity import assert_sweep_parity, dequant, h_rel_error, output_error
 
 pytestmark = pytest.mark.gpu
 
@@ -45,10 +45,9 @@ def _check(W, X, out, bits, g, Href=None, rows=None):
     ref = oracle.gptq(Wr, U, bits, g, 128, precision="f32", tie_distance=True)
     sel = (lambda a: a) if rows is None else (lambda a: a[rows])
     rep = assert_sweep_parity(sel(out["codes"]), sel(out["scales"]), sel(out["zeros"]), ref, g)
-    Wg = oracle.dequantize(sel(out["codes"]), sel(out["scales"]).astype(np.float64),
-                           sel(out["zeros"]).astype(np.float64), g)
+    Wg = dequant(sel(out["codes"]), sel(out["scales"]), sel(out["zeros"]), g)
     Wo = oracle.dequantize(ref["codes"], ref["scales"], ref["zeros"], g)
-    e_gpu = oracle.output_error(Wr, Wg, Href)
+    e_gpu = output_error(Wr, Wg, Href)
     e_ref = oracle.output_error(Wr, Wo, Href)
     assert abs(e_gpu - e_ref) <= 0.01 * e_ref, (e_gpu, e_ref)
     rt = oracle.rtn(Wr, bits, g, precision="f32")
@@ -120,9 +119,8 @@ def test_full_attention_layer_act_order(env, attn_inputs):
     rep = check_act_order_result(W, out, ref, 128, Href, rows=rows)
     own = _gpu_act_order_layer(env, W, X, 4, 128)
     moved = check_gpu_order(own["perm"], own["H"], Href)
-    Wg = oracle.dequantize_gidx(own["codes"][rows], own["scales"][rows].astype(np.float64),
-                                own["zeros"][rows].astype(np.float64), own["g_idx"])
-    e_own = oracle.output_error(W[rows], Wg, Href)
+    Wg = dequant(own["codes"][rows], own["scales"][rows], own["zeros"][rows], g_idx=own["g_idx"])
+    e_own = output_error(W[rows], Wg, Href)
     assert abs(e_own - rep["e_ref"]) <= 0.01 * rep["e_ref"], (e_own, rep["e_ref"])
     print("attn full act-order", rep, "own order: positions differing", moved, "e_own", e_own)
 
@@ -143,19 +141,23 @@ def test_full_mlp_down_layer_sampled(env):
     """4096x11008 int4 g128 at 262144 tokens with 60% zeros and 220 dead
     channels (H singular before damping), full size. A full fp64 H is 6e13
     flops on the host, so:
-      * H is compared on 3000 sampled entries, each an fp64 dot product over
-        all tokens (diagonal entries of dead channels included);
-      * Hinv is compared with the oracle's route run on the GPU's H (fp32 ->
-        fp64), which isolates the preparation;
-      * the sweep is compared on 64 sampled rows given the oracle's Hinv, and
-        the output error is scored with the GPU's H in fp64."""
+      * the GPU path runs as the benchmark runs it (one accumulate call over
+        all tokens, the preparation, the sweep), and its H is compared on 3000
+        sampled entries, each an fp64 dot product over all tokens (diagonal
+        entries of dead channels included);
+      * the preparation and the sweep are compared at full size on an H the
+        oracle forms itself, from the first 65536 tokens (rounded to fp32 for
+        both sides; the launch configuration of both depends only on the
+        shapes): Hinv against the oracle's, and the sweep of every row with
+        the oracle's Hinv against the oracle's sweep on 128 sampled rows,
+        scored by the output error under that H."""
     torch, gq = env
     L = synth.LAYERS["mlp_down"]
     X = synth.activations(L.x, threads=16)
     W = synth.weights(L.w)
     out = _gpu_layer(env, W, X, 4, 128)
     d = L.x.d
-    Hg = out["H"].astype(np.float64)
+    Hg = out["H"]
     rng = np.random.default_rng(2)
     dead = synth.dead_channels(L.x)
     ii = np.concatenate([rng.integers(0, d, 2900), dead[:50], rng.integers(0, d, 50)])
@@ -165,22 +167,33 @@ def test_full_mlp_down_layer_sampled(env):
         href += np.einsum("ti,ti->i", X[t:t + 16384, ii].astype(np.float64),
                           X[t:t + 16384, jj].astype(np.float64))
     href *= 2.0
-    hgpu = Hg[ii, jj]
+    hgpu = Hg[ii, jj].astype(np.float64)
     scale = np.abs(np.diag(Hg)).max()
     assert np.abs(hgpu - href).max() <= 1e-4 * scale
     assert np.all(hgpu[2900:2950] == 0.0)  # dead channel diagonal entries
-    U, lam = oracle.hinv_upper(Hg, 0.01)
-    err = np.abs(out["U"] - U).max() / np.abs(U).max()
+    del out, Hg
+    # the oracle's H on a token subset, its Hinv, and both stages on the GPU
+    Hs = oracle.hessian((X[t:t + 16384] for t in range(0, 65536, 16384)), d).astype(np.float32)
+    U, lam = oracle.hinv_upper(Hs.astype(np.float64), 0.01)
+    Ug = gq.prepare_hinv(torch.from_numpy(Hs).cuda(), 0.01)
+    torch.cuda.synchronize()
+    err = np.abs(Ug.cpu().numpy() - U).max() / np.abs(U).max()
     assert err <= 2e-6, err
-    rows = np.sort(rng.choice(L.w.rows, 64, replace=False))
-    ref = oracle.gptq(W[rows], U, 4, 128, 128, precision="f32", tie_distance=True)
-    rep = assert_sweep_parity(out["codes"][rows], out["scales"][rows], out["zeros"][rows], ref, 128)
+    del Ug
+    U32 = U.astype(np.float32)
+    codes, scales, zeros, _ = gq.quantize_layer(torch.from_numpy(W).cuda(),
+                                                torch.from_numpy(U32).cuda(), 4, 128, 128)
+    torch.cuda.synchronize()
+    codes, scales, zeros = codes.cpu().numpy(), scales.cpu().numpy(), zeros.cpu().numpy()
+    rows = np.sort(rng.choice(L.w.rows, 128, replace=False))
+    ref = oracle.gptq(W[rows], U32.astype(np.float64), 4, 128, 128, precision="f32",
+                      tie_distance=True)
+    rep = assert_sweep_parity(codes[rows], scales[rows], zeros[rows], ref, 128)
+    Hs64 = Hs.astype(np.float64)
     Wr = W[rows]
-    Wg = oracle.dequantize(out["codes"][rows], out["scales"][rows].astype(np.float64),
-                           out["zeros"][rows].astype(np.float64), 128)
-    Wo = oracle.dequantize(ref["codes"], ref["scales"], ref["zeros"], 128)
-    e_gpu = oracle.output_error(Wr, Wg, Hg)
-    e_ref = oracle.output_error(Wr, Wo, Hg)
+    e_gpu = output_error(Wr, dequant(codes[rows], scales[rows], zeros[rows], 128), Hs64)
+    e_ref = oracle.output_error(Wr, oracle.dequantize(ref["codes"], ref["scales"], ref["zeros"],
+                                                      128), Hs64)
     assert abs(e_gpu - e_ref) <= 0.01 * e_ref, (e_gpu, e_ref)
-    rep.update(e_gpu=e_gpu, e_ref=e_ref)
+    rep.update(e_gpu=e_gpu, e_ref=e_ref, hinv_err=err)
     print("mlp_down full", rep)

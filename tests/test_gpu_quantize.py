@@ -6,7 +6,7 @@ import pytest
 
 import oracle
 import synth
-from parity import assert_sweep_parity
+from parity import assert_sweep_parity, damped_objective, dequant
 
 pytestmark = pytest.mark.gpu
 
@@ -71,8 +71,8 @@ def test_losses_sum_to_objective_of_gpu_result(env):
     codes, scales, zeros, losses = _gpu_quant(env, W, U32, 4, 128)
     Uf = U32.astype(np.float64)
     Hd = np.linalg.inv(Uf.T @ Uf)  # the damped H the fp32 Hinv stands for
-    What = oracle.dequantize(codes, scales.astype(np.float64), zeros.astype(np.float64), 128)
-    obj = oracle.layer_objective(W, What, Hd).sum()
+    What = dequant(codes, scales, zeros, 128)
+    obj = damped_objective(W, What, Hd)
     assert losses.sum() == pytest.approx(obj, rel=2e-3)
 
 
