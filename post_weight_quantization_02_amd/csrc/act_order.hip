@@ -30,31 +30,39 @@ __device__ inline uint32_t order_key(float x) {
 }
 
 constexpr int kRankChunk = 2048;
+constexpr int kRankCols = 16;  // columns per workgroup, 16 lanes each
 
 // rank(c) = #{c' : key(c') > key(c), or key(c') == key(c) and c' < c};
-// perm[rank(c)] = c.  One thread per column; the diagonal streams through
-// LDS in chunks that every thread compares against (broadcast reads).
+// perm[rank(c)] = c.  A workgroup ranks 16 columns; lane s of a column's 16
+// compares the keys s, s + 16, ... of each chunk of the diagonal staged in
+// LDS (in a wave, lanes of one slice read the same word and the 16 slices
+// read 16 consecutive words), and the 16 partial counts are summed with lane
+// shuffles.
 __global__ __launch_bounds__(256) void act_order_rank_kernel(const float* __restrict__ H,
                                                              int64_t d, int* __restrict__ perm) {
   __shared__ uint32_t keys[kRankChunk];
-  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int tid = threadIdx.x;
+  const int sl = tid & (kRankCols - 1);
+  const int64_t c = (int64_t)blockIdx.x * kRankCols + (tid >> 4);
   const bool valid = c < d;
   const uint32_t kc = valid ? order_key(H[c * d + c]) : 0u;
   int rank = 0;
   for (int64_t base = 0; base < d; base += kRankChunk) {
     const int n = (int)((d - base < kRankChunk) ? d - base : kRankChunk);
     __syncthreads();
-    for (int t = threadIdx.x; t < n; t += 256) keys[t] = order_key(H[(base + t) * d + base + t]);
+    for (int t = tid; t < n; t += 256) keys[t] = order_key(H[(base + t) * d + base + t]);
     __syncthreads();
     // columns of this chunk before c (all of them when the chunk ends at or
     // before c) win ties
     const int64_t before = c - base;
-    for (int t = 0; t < n; ++t) {
+    for (int t = sl; t < n; t += kRankCols) {
       const uint32_t k = keys[t];
       rank += (k > kc) | ((k == kc) & (t < before));
     }
   }
-  if (valid) perm[rank] = (int)c;
+#pragma unroll
+  for (int m = kRankCols / 2; m > 0; m >>= 1) rank += __shfl_xor(rank, m, kRankCols);
+  if (valid && sl == 0) perm[rank] = (int)c;
 }
 
 // ---- checks of a caller's perm (values in range, each index exactly once)
@@ -100,38 +108,45 @@ __global__ __launch_bounds__(256) void perm_inverse_kernel(const int* __restrict
 }
 
 // Outputs back to the original column order: codes[r][c] = cp[r][inv[c]]
-// (cp: codes in processing order); row 0's workgroups also write
-// losses[c] = lp[inv[c]] and g_idx[c] = inv[c] / g.  Four columns per
-// thread; each thread writes one 32-bit word of codes when the rows are
-// 4-byte aligned (vec4: cols % 4 == 0 and codes 4-byte aligned).
+// (cp: codes in processing order); workgroup 0 also writes
+// losses[c] = lp[inv[c]] and g_idx[c] = inv[c] / g.  One workgroup per row:
+// with `stage` the row of cp is first copied to LDS (dynamic, cols bytes) so
+// the gather reads LDS; four columns per thread, written as one 32-bit word
+// when vec4 (cols % 4 == 0 and codes 4-byte aligned).
 __global__ __launch_bounds__(256) void unpermute_outputs_kernel(
     const uint8_t* __restrict__ cp, int64_t rows, int64_t cols, const int* __restrict__ inv,
     uint8_t* __restrict__ codes, const float* __restrict__ lp, float* __restrict__ losses,
-    int g, int* __restrict__ g_idx, bool vec4) {
-  const int64_t r = blockIdx.y;
-  const int64_t c0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
-  if (c0 >= cols) return;
+    int g, int* __restrict__ g_idx, bool vec4, bool stage) {
+  extern __shared__ uint8_t rowbuf[];
+  const int64_t r = blockIdx.x;
   const uint8_t* src = cp + r * cols;
-  int k[4];
-#pragma unroll
-  for (int u = 0; u < 4; ++u)
-    k[u] = (c0 + u < cols) ? min(max(inv[c0 + u], 0), (int)(cols - 1)) : 0;
-  uint8_t* dst = codes + r * cols + c0;
-  if (vec4 && c0 + 4 <= cols) {
-    const uint32_t w = (uint32_t)src[k[0]] | ((uint32_t)src[k[1]] << 8) |
-                       ((uint32_t)src[k[2]] << 16) | ((uint32_t)src[k[3]] << 24);
-    *reinterpret_cast<uint32_t*>(dst) = w;
-  } else {
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-      if (c0 + u < cols) dst[u] = src[k[u]];
+  if (stage) {
+    for (int64_t c = threadIdx.x; c < cols; c += 256) rowbuf[c] = src[c];
+    __syncthreads();
+    src = rowbuf;
   }
-  if (r == 0) {
+  const int cmax = (int)(cols - 1);
+  for (int64_t c0 = (int64_t)threadIdx.x * 4; c0 < cols; c0 += 1024) {
+    int k[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      if (c0 + u >= cols) break;
-      losses[c0 + u] = lp[k[u]];
-      if (g_idx != nullptr) g_idx[c0 + u] = k[u] / g;
+    for (int u = 0; u < 4; ++u) k[u] = (c0 + u < cols) ? min(max(inv[c0 + u], 0), cmax) : 0;
+    uint8_t* dst = codes + r * cols + c0;
+    if (vec4 && c0 + 4 <= cols) {
+      const uint32_t w = (uint32_t)src[k[0]] | ((uint32_t)src[k[1]] << 8) |
+                         ((uint32_t)src[k[2]] << 16) | ((uint32_t)src[k[3]] << 24);
+      *reinterpret_cast<uint32_t*>(dst) = w;
+    } else {
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (c0 + u < cols) dst[u] = src[k[u]];
+    }
+    if (r == 0) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (c0 + u >= cols) break;
+        losses[c0 + u] = lp[k[u]];
+        if (g_idx != nullptr) g_idx[c0 + u] = k[u] / g;
+      }
     }
   }
 }
@@ -146,8 +161,8 @@ __global__ __launch_bounds__(256) void group_index_kernel(int64_t cols, int g,
 }  // namespace
 
 hipError_t launch_act_order(const float* H, int64_t d, int* perm, hipStream_t s) {
-  hipLaunchKernelGGL(act_order_rank_kernel, dim3((unsigned)ceil_div(d, 256)), dim3(256), 0, s, H,
-                     d, perm);
+  hipLaunchKernelGGL(act_order_rank_kernel, dim3((unsigned)ceil_div(d, kRankCols)), dim3(256), 0,
+                     s, H, d, perm);
   return hipGetLastError();
 }
 
@@ -172,10 +187,11 @@ hipError_t launch_perm_inverse(const int* perm, int64_t n, int* inv, hipStream_t
 hipError_t launch_unpermute_outputs(const uint8_t* cp, int64_t rows, int64_t cols, const int* inv,
                                     uint8_t* codes, const float* lp, float* losses, int g,
                                     int* g_idx, hipStream_t s) {
-  const dim3 grid((unsigned)ceil_div(cols, 1024), (unsigned)rows);
   const bool vec4 = (cols % 4 == 0) && ((reinterpret_cast<uintptr_t>(codes) & 3) == 0);
-  hipLaunchKernelGGL(unpermute_outputs_kernel, grid, dim3(256), 0, s, cp, rows, cols, inv, codes,
-                     lp, losses, g, g_idx, vec4);
+  const bool stage = cols <= kStageBytes;
+  hipLaunchKernelGGL(unpermute_outputs_kernel, dim3((unsigned)rows), dim3(256),
+                     stage ? (unsigned)cols : 0u, s, cp, rows, cols, inv, codes, lp, losses, g,
+                     g_idx, vec4, stage);
   return hipGetLastError();
 }
 

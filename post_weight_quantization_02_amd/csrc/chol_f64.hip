@@ -92,17 +92,24 @@ __global__ __launch_bounds__(256) void damp_copy_kernel(const float* __restrict_
 }
 
 // Act-order variant: A = P H P^T + lambda I with (P H P^T)[i][j] =
-// H[perm[i]][perm[j]], lower triangle.  Row perm[i] of H is contiguous, so the
-// gathered columns of one row stay in cache; H must hold both triangles.
-// perm entries are clamped into [0, d).
+// H[perm[i]][perm[j]], lower triangle; H must hold both triangles.  One
+// workgroup per row i; with `stage` row perm[i] of H is first copied to LDS
+// (dynamic, d floats) so the gather reads LDS.  perm entries are clamped into
+// [0, d).
 __global__ __launch_bounds__(256) void damp_copy_perm_kernel(const float* __restrict__ H, int d,
                                                              const int* __restrict__ perm,
                                                              const double* lam,
-                                                             double* __restrict__ A) {
+                                                             double* __restrict__ A, bool stage) {
+  extern __shared__ float hrowbuf[];
   const int64_t i = blockIdx.x;
   const double l = *lam;
   const int64_t pi = min(max(perm[i], 0), d - 1);
   const float* hrow = H + pi * d;
+  if (stage) {
+    for (int64_t j = threadIdx.x; j < d; j += 256) hrowbuf[j] = hrow[j];
+    __syncthreads();
+    hrow = hrowbuf;
+  }
   for (int64_t j = threadIdx.x; j <= i; j += 256) {
     double v = (double)hrow[min(max(perm[j], 0), d - 1)];
     if (j == i) v += l;
@@ -1074,9 +1081,12 @@ hipError_t launch_damp_to_f64(const float* H, int d, double percdamp, const int*
   hipLaunchKernelGGL(damp_lambda_kernel, dim3(1), dim3(256), 0, s, H, d, percdamp, lam, flag);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (perm != nullptr)
-    hipLaunchKernelGGL(damp_copy_perm_kernel, dim3((unsigned)d), dim3(256), 0, s, H, d, perm,
-                       (const double*)lam, A);
+  if (perm != nullptr) {
+    const bool stage = (int64_t)d * 4 <= kStageBytes;
+    hipLaunchKernelGGL(damp_copy_perm_kernel, dim3((unsigned)d), dim3(256),
+                       stage ? (unsigned)d * 4u : 0u, s, H, d, perm, (const double*)lam, A,
+                       stage);
+  }
   else
     hipLaunchKernelGGL(damp_copy_kernel, dim3((unsigned)d), dim3(256), 0, s, H, d,
                        (const double*)lam, A);

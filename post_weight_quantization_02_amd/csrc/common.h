@@ -76,6 +76,7 @@ hipError_t launch_lazy_update(float* Wk, int64_t ldk, int64_t rows, int64_t cols
 hipError_t launch_loss_reduce(const float* loss_part, int64_t nparts, int64_t cols,
                               float* losses, hipStream_t s);
 // act-order
+constexpr int64_t kStageBytes = 48 * 1024;  // largest row a gather kernel stages in LDS
 hipError_t launch_act_order(const float* H, int64_t d, int* perm, hipStream_t s);
 // *bad = 0 if perm is a permutation of [0, n), else 1 (inv: n ints of scratch)
 hipError_t launch_perm_check(const int* perm, int64_t n, int* inv, int* bad, hipStream_t s);

@@ -558,16 +558,27 @@ __global__ __launch_bounds__(256) void convert_kernel(const T* __restrict__ W, i
 }
 
 // Act-order variant: Wk[r][j] = W[r][perm[j]] (columns in processing order;
-// perm entries clamped into [0, cols)).
+// perm entries clamped into [0, cols)).  One workgroup per row; with `stage`
+// the row of W is first copied to LDS (dynamic, cols * sizeof(T) bytes) so
+// the gather reads LDS and both global passes are coalesced.
 template <typename T>
 __global__ __launch_bounds__(256) void convert_perm_kernel(const T* __restrict__ W, int64_t rows,
                                                            int64_t cols, int64_t ldw,
                                                            const int* __restrict__ perm,
-                                                           float* __restrict__ Wk, int64_t ldk) {
+                                                           float* __restrict__ Wk, int64_t ldk,
+                                                           bool stage) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t convert_row[];
+  T* rowbuf = reinterpret_cast<T*>(convert_row);
   const int64_t r = blockIdx.x;
+  const T* src = W + r * ldw;
+  if (stage) {
+    for (int64_t c = threadIdx.x; c < cols; c += 256) rowbuf[c] = src[c];
+    __syncthreads();
+    src = rowbuf;
+  }
   const int cmax = (int)(cols - 1);
-  for (int64_t c = (int64_t)blockIdx.y * 256 + threadIdx.x; c < ldk; c += (int64_t)gridDim.y * 256)
-    Wk[r * ldk + c] = (c < cols) ? (float)W[r * ldw + min(max(perm[c], 0), cmax)] : 0.f;
+  for (int64_t c = threadIdx.x; c < ldk; c += 256)
+    Wk[r * ldk + c] = (c < cols) ? (float)src[min(max(perm[c], 0), cmax)] : 0.f;
 }
 
 // fp16 rows whose start is 16-byte aligned (ldw % 8 == 0): 8 columns per
@@ -623,12 +634,16 @@ hipError_t launch_convert_w(const void* W, int w_dtype, int64_t rows, int64_t co
                             const int* perm, float* Wk, int64_t ldk, hipStream_t s) {
   dim3 grid((unsigned)rows, (unsigned)((ceil_div(ldk, 256) < 16) ? ceil_div(ldk, 256) : 16));
   if (perm != nullptr) {
+    const int64_t rb = cols * (w_dtype == GPTQ_DTYPE_F16 ? 2 : 4);
+    const bool stage = rb <= kStageBytes;
+    const unsigned lds = stage ? (unsigned)rb : 0u;
     if (w_dtype == GPTQ_DTYPE_F16)
-      hipLaunchKernelGGL(convert_perm_kernel<_Float16>, grid, dim3(256), 0, s,
-                         reinterpret_cast<const _Float16*>(W), rows, cols, ldw, perm, Wk, ldk);
+      hipLaunchKernelGGL(convert_perm_kernel<_Float16>, dim3((unsigned)rows), dim3(256), lds, s,
+                         reinterpret_cast<const _Float16*>(W), rows, cols, ldw, perm, Wk, ldk,
+                         stage);
     else
-      hipLaunchKernelGGL(convert_perm_kernel<float>, grid, dim3(256), 0, s,
-                         reinterpret_cast<const float*>(W), rows, cols, ldw, perm, Wk, ldk);
+      hipLaunchKernelGGL(convert_perm_kernel<float>, dim3((unsigned)rows), dim3(256), lds, s,
+                         reinterpret_cast<const float*>(W), rows, cols, ldw, perm, Wk, ldk, stage);
     return hipGetLastError();
   }
   const bool v8 = (ldw % 8 == 0) && ((reinterpret_cast<uintptr_t>(W) & 15) == 0) &&
