@@ -21,6 +21,7 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--layer NAME]
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -250,6 +251,9 @@ def main():
                     choices=["attn", "mlp_up", "mlp_down", "tiny", "block"])
     ap.add_argument("--act-order", action="store_true",
                     help="process columns in decreasing order of diag(H) (desc_act)")
+    ap.add_argument("--groupsize", type=int, default=None,
+                    help="override the layer's group size (0: one group per row, per-channel)")
+    ap.add_argument("--bits", type=int, default=None, help="override the layer's bit width")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
     ap.add_argument("--no-peaks", action="store_true", help="skip the library peak probes")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -291,6 +295,10 @@ def main():
         metric = "ms per Llama-7B-shaped block (7 layers, 4 H's incl. accumulate)"
     else:
         L = synth.LAYERS[args.layer]
+        if args.groupsize is not None or args.bits is not None:
+            g = L.groupsize if args.groupsize is None else args.groupsize
+            L = dataclasses.replace(L, groupsize=(L.w.cols if g <= 0 else g),
+                                    bits=L.bits if args.bits is None else args.bits)
         groups = [(L.x, [L])]
         layers = [L]
         rows, d, n = L.w.rows, L.x.d, L.x.n
@@ -300,7 +308,7 @@ def main():
         workload = (f"{L.name}: W {rows}x{d} {L.w.dtype}, X {n}x{d} fp16{extra}, "
                     f"int{L.bits} g{L.groupsize} B{L.blocksize} percdamp {L.percdamp}")
         metric = "ms per 4096x4096 int4 g128 GPTQ layer (incl. H accumulate); % MFMA roofline"
-        if args.layer != "attn":
+        if args.layer != "attn" or args.groupsize is not None or args.bits is not None:
             metric = f"ms per {rows}x{d} int{L.bits} g{L.groupsize} GPTQ layer (incl. H accumulate)"
     if args.act_order:
         workload += "; act-order (columns in decreasing order of diag(H), groups in that order)"

@@ -163,7 +163,10 @@ gptq_status gptq_prepare_hinv(const float* H, int64_t d, double percdamp, float*
  *              triangle (including the diagonal) is read.
  *   bits       2..8.
  *   groupsize  16, 32, 64 or a multiple of 128 (the last group may be
- *              short when cols is not a multiple of groupsize).
+ *              short when cols is not a multiple of groupsize), or any value
+ *              >= cols: one group per row over all columns (per-channel;
+ *              "GPTQ, Line by Line", the qwix port supports per-channel and
+ *              grouped scales), with the statistics of the weights as given.
  *   blocksize  128.  Other values return GPTQ_ERR_UNSUPPORTED.  The result
  *              does not depend on it in exact arithmetic.
  *   codes      rows x cols uint8 out, values in [0, 2^bits - 1].

@@ -211,7 +211,8 @@ def prepare_hinv_perm(H, perm, percdamp: float = 0.01, out=None, workspace=None,
 def quantize_layer(W, Hinv, bits: int = 4, groupsize: int = 128, blocksize: int = 128,
                    out=None, workspace=None, stream=None):
     """GPTQ sweep. W: rows x cols fp16/fp32 (unit column stride); Hinv from
-    prepare_hinv. Returns (codes uint8, scales fp32, zeros fp32, losses fp32)."""
+    prepare_hinv; groupsize <= 0 means one group per row (per-channel).
+    Returns (codes uint8, scales fp32, zeros fp32, losses fp32)."""
     torch = _torch()
     if W.dim() != 2 or W.stride(1) != 1 or not W.is_cuda:
         raise ValueError("W must be a 2-D CUDA tensor with unit column stride")
@@ -224,6 +225,8 @@ def quantize_layer(W, Hinv, bits: int = 4, groupsize: int = 128, blocksize: int 
     rows, cols = W.shape
     if Hinv.shape != (cols, cols) or Hinv.dtype != torch.float32 or not Hinv.is_contiguous():
         raise ValueError("Hinv must be a contiguous cols x cols fp32 tensor")
+    if groupsize <= 0:  # per-channel: one group over all columns
+        groupsize = cols
     g = groupsize
     ng = (cols + g - 1) // g
     dev = W.device
@@ -263,6 +266,8 @@ def quantize_layer_perm(W, perm, Hinv, bits: int = 4, groupsize: int = 128, bloc
     perm = _check_perm(perm, cols, W.device)
     if Hinv.shape != (cols, cols) or Hinv.dtype != torch.float32 or not Hinv.is_contiguous():
         raise ValueError("Hinv must be a contiguous cols x cols fp32 tensor")
+    if groupsize <= 0:  # per-channel: one group over all columns
+        groupsize = cols
     g = groupsize
     ng = (cols + g - 1) // g
     dev = W.device

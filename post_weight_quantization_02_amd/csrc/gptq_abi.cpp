@@ -227,15 +227,19 @@ gptq_status quantize_impl(const void* W, int w_dtype, int64_t rows, int64_t cols
   if (w_dtype != GPTQ_DTYPE_F16 && w_dtype != GPTQ_DTYPE_F32) return GPTQ_ERR_INVALID_ARG;
   if (bits < 2 || bits > 8) return GPTQ_ERR_INVALID_ARG;
   if (groupsize < 1 || blocksize < 1) return GPTQ_ERR_INVALID_ARG;
+  // groupsize >= cols: one group per row (per-channel), statistics at
+  // column 0 only, before any update
+  const bool per_channel = groupsize >= cols;
   // group statistics taken at a group start must see every pending update:
   // either groups lie inside blocks or blocks inside groups
-  if (groupsize % blocksize != 0 && blocksize % groupsize != 0) return GPTQ_ERR_INVALID_ARG;
+  if (!per_channel && groupsize % blocksize != 0 && blocksize % groupsize != 0)
+    return GPTQ_ERR_INVALID_ARG;
   if (rows > kMaxElems / ldw) return GPTQ_ERR_INVALID_ARG;
   if (!aligned(W, w_dtype == GPTQ_DTYPE_F16 ? 2 : 4) || !aligned(Hinv, 4) ||
       !aligned(scales, 4) || !aligned(zeros, 4) || !aligned(losses, 4) || !aligned(perm, 4) ||
       !aligned(g_idx, 4))
     return GPTQ_ERR_INVALID_ARG;
-  if (blocksize != kBlock || !group_ok(groupsize)) return GPTQ_ERR_UNSUPPORTED;
+  if (blocksize != kBlock || (!per_channel && !group_ok(groupsize))) return GPTQ_ERR_UNSUPPORTED;
   const QuantLayout L = quant_layout(rows, cols);
   const size_t need = perm != nullptr ? L.total_perm : L.total;
   if (workspace == nullptr || workspace_bytes < need) return GPTQ_ERR_WORKSPACE;
@@ -263,8 +267,11 @@ gptq_status quantize_impl(const void* W, int w_dtype, int64_t rows, int64_t cols
   // sweeping them); when groups span blocks, a group's statistics read
   // columns of later blocks, so those get each block's errors right away in a
   // separate lazy update.
-  const int64_t SB = (groupsize > kBlock) ? (groupsize > kSuperBlock ? groupsize : kSuperBlock)
-                                          : kSuperBlock;
+  // (A single per-channel group takes its statistics before any update, so
+  // it puts no constraint on the superblock.)
+  const int64_t SB = (groupsize > kBlock && !per_channel)
+                         ? (groupsize > kSuperBlock ? groupsize : kSuperBlock)
+                         : kSuperBlock;
   const bool fused_near = groupsize <= kBlock;
   for (int64_t s0 = 0; s0 < cols; s0 += SB) {
     const int64_t s1 = (s0 + SB < cols) ? s0 + SB : cols;

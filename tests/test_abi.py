@@ -125,3 +125,37 @@ def test_quantize_validation():
     assert _quant(ws=None) == WS
     assert _quant(wsb=1024) == WS
     assert _quant(dt=1, W=FAKE + 2) == E  # fp32 W must be 4-byte aligned
+
+
+def test_quantize_per_channel_group_passes_the_group_checks():
+    """groupsize >= cols is one group per row: accepted whatever its
+    divisibility (the call then stops at the too-small workspace, before
+    any launch); a group below cols must still align with the block."""
+    E, WS = gq.GPTQ_ERR_INVALID_ARG, gq.GPTQ_ERR_WORKSPACE
+    assert _quant(g=200) == E
+    assert _quant(g=256, wsb=1024) == WS
+    assert _quant(g=300, wsb=1024) == WS
+    assert _quant(cols=200, ldw=200, g=200, wsb=1024) == WS
+
+
+def test_act_order_entry_points_validation():
+    E, WS = gq.GPTQ_ERR_INVALID_ARG, gq.GPTQ_ERR_WORKSPACE
+    assert lib.gptq_act_order(None, 16, FAKE, None) == E
+    assert lib.gptq_act_order(FAKE, 16, None, None) == E
+    assert lib.gptq_act_order(FAKE, 0, FAKE, None) == E
+    assert lib.gptq_act_order(FAKE, 16, FAKE + 2, None) == E
+    info = ctypes.c_int64(5)
+    need = gq.workspace_bytes(gq.OP_PREPARE, 0, 64, 0)
+    assert lib.gptq_prepare_hinv_perm(FAKE, 64, FAKE + 2, 0.01, FAKE, FAKE, need,
+                                      ctypes.byref(info), None) == E
+    assert info.value == 0
+    assert lib.gptq_prepare_hinv_perm(FAKE, 64, FAKE, 0.01, FAKE, None, need,
+                                      ctypes.byref(info), None) == WS
+    q = gq.workspace_bytes(gq.OP_QUANTIZE, 8, 256, 0)
+    qp = gq.workspace_bytes(gq.OP_QUANTIZE_PERM, 8, 256, 0)
+    assert qp >= q + 8 * 256 + 256 * 4 + 256 * 4
+    args = [FAKE, 0, 8, 256, 256, FAKE, FAKE, 4, 128, 128, FAKE, FAKE, FAKE, FAKE, FAKE]
+    # the plain workspace is too small once a perm is given
+    assert lib.gptq_quantize_layer_perm(*args, FAKE, q, None) == WS
+    assert lib.gptq_quantize_layer_perm(*args[:5], FAKE + 2, *args[6:], FAKE, qp, None) == E
+    assert lib.gptq_quantize_layer_perm(*args[:14], FAKE + 2, FAKE, qp, None) == E  # g_idx

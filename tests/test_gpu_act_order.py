@@ -148,6 +148,7 @@ def _gpu_quant_perm(env, W, perm, U32, bits, g):
     (24, 640, 4, 256, "f16"),     # groups spanning two blocks, short last group
     (50, 1100, 3, 64, "f32"),     # three superblocks with pending in-superblock errors
     (1, 64, 4, 128, "f32"),       # one row, one short block
+    (30, 700, 4, 700, "f16"),     # per-channel (one group in processing order)
 ])
 def test_sweep_perm_matches_oracle_given_hinv(env, rows, cols, bits, g, wdt):
     W, H, perm, U32 = _perm_case(rows, cols, 4 * cols, wdt)

@@ -50,6 +50,11 @@ def _gpu_quant(env, W, U32, bits, g):
     (1, 64, 4, 128, "f32"),       # a single row, a single short block
     (50, 1100, 4, 128, "f16"),    # three superblocks, the last one a ragged block
     (30, 700, 3, 64, "f32"),      # two superblocks, pending in-superblock errors with g < 128
+    (37, 200, 4, 200, "f32"),     # per-channel (g = cols), ragged
+    (24, 700, 3, 700, "f16"),     # per-channel over two superblocks
+    (16, 1100, 2, 1100, "f32"),   # per-channel, 2 bits, three superblocks
+    (256, 256, 8, 4096, "f16"),   # per-channel (g > cols), 8 bits; 256 rows so the
+                                  # 99.9% bar is measured on a layer-sized sample
 ])
 def test_sweep_matches_oracle_given_hinv(env, rows, cols, bits, g, wdt):
     W, H, U32 = _case(rows, cols, 4 * cols, wdtype=wdt)

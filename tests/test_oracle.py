@@ -373,3 +373,42 @@ def test_sweep_rounds_exact_ties_to_even(precision):
     r = oracle.gptq(np.array([[-1.0, -0.5, 0.5, 1.5, 2.0]]), np.eye(5), bits=2, groupsize=5,
                     precision=precision)
     assert r["codes"][0].tolist() == [0, 0, 2, 2, 3]
+
+
+# ---------------------------------------------------------------- per-channel
+def test_per_channel_is_one_group_over_all_columns():
+    """Per-channel scales ("GPTQ, Line by Line": the qwix port supports
+    per-channel and grouped scales): groupsize <= 0, = cols or > cols all mean
+    one group per row whose statistics are those of the weights as given
+    (column 0 is the group start, before any update)."""
+    L = synth.LAYERS["tiny"]
+    x = L.x.scaled(d=200, n=800, rank=16)
+    W = synth.weights(L.w.scaled(rows=20, cols=200))
+    U, _ = oracle.hinv_upper(oracle.hessian([synth.activations(x)], 200), 0.01)
+    ref = oracle.gptq(W, U, 3, 0, 128)
+    assert ref["scales"].shape == (20, 1)
+    s, z = oracle.group_params(W, 3)
+    np.testing.assert_array_equal(ref["scales"][:, 0], s)
+    np.testing.assert_array_equal(ref["zeros"][:, 0], z)
+    for g in (200, 1000):
+        r = oracle.gptq(W, U, 3, g, 128)
+        for k in ("codes", "scales", "zeros", "losses"):
+            assert np.array_equal(r[k], ref[k]), (g, k)
+
+
+def test_per_channel_diagonal_hessian_gives_rtn_and_blocksize_is_free():
+    rng = np.random.default_rng(23)
+    d = 300
+    H = np.diag(rng.uniform(0.1, 10.0, d))
+    W = rng.standard_normal((16, d)) * 0.02
+    U, _ = oracle.hinv_upper(H, 0.01)
+    r = oracle.gptq(W, U, 4, 0, 128)
+    rt = oracle.rtn(W, 4, 0)
+    assert np.array_equal(r["codes"], rt["codes"])
+    x = synth.LAYERS["tiny"].x.scaled(d=d, n=4 * d, rank=16)
+    U2, _ = oracle.hinv_upper(oracle.hessian([synth.activations(x)], d), 0.01)
+    ref = oracle.gptq(W, U2, 4, 0, 128)
+    for B in (1, 7, 64):
+        r = oracle.gptq(W, U2, 4, 0, B)
+        assert np.array_equal(r["codes"], ref["codes"]), B
+        np.testing.assert_allclose(r["losses"], ref["losses"], rtol=1e-9, atol=1e-18)
