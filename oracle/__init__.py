@@ -23,3 +23,11 @@ from .gptq64 import (  # noqa: F401
     gptq_act_order,
     dequantize_gidx,
 )
+from .infer64 import (  # noqa: F401
+    codes_per_word,
+    pack_codes,
+    unpack_codes,
+    dequant_weights,
+    dequant_matmul,
+    abs_products,
+)
