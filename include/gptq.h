@@ -260,6 +260,62 @@ gptq_status gptq_quantize_layer_perm(const void* W, int w_dtype, int64_t rows, i
                                      float* scales, float* zeros, float* losses, int32_t* g_idx,
                                      void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Inference with the stored quantized weights.  The pages fix what is
+ * stored -- the low-bit integers and one scale per group of 128 weights --
+ * and that inference reads the weights in that form, which is what makes
+ * memory-bound decode faster ("GPTQ: fixing errors as you go", the 4-bit
+ * Llama layer example and "What it's good and bad at"; "GPTQ, Line by Line",
+ * the AutoGPTQ example).  The word layout below is this library's.
+ *
+ * Packed layout: row r of the codes is stored along the input dimension in
+ * 32-bit words of K = floor(32 / bits) codes (8 at 4 bits, 10 at 3 bits, 16
+ * at 2 bits, 4 at 8 bits); the code of column c is at bits
+ * [bits*(c % K), bits*(c % K) + bits) of word c / K; unused high bits are 0.
+ */
+
+/* Words per packed row: ceil(cols / floor(32 / bits)); 0 for invalid sizes. */
+int64_t gptq_packed_words(int64_t cols, int bits);
+
+/*
+ * gptq_pack_codes -- packed[r][w] for the codes of gptq_quantize_layer (or
+ * _perm, in the original column order).
+ *
+ *   codes   rows x cols uint8 (row stride cols); each code is masked to
+ *           `bits` bits.
+ *   bits    2..8.
+ *   packed  rows x gptq_packed_words(cols, bits) uint32 out (row stride
+ *           gptq_packed_words), 4-byte aligned.
+ *   Asynchronous; bitwise deterministic.
+ */
+gptq_status gptq_pack_codes(const uint8_t* codes, int64_t rows, int64_t cols, int bits,
+                            uint32_t* packed, void* stream);
+
+/*
+ * gptq_dequant_gemm -- y = x W_hat^T, W_hat[r][c] = (code - zero[r][g]) *
+ * scale[r][g] with g = g_idx[c] if g_idx is given (act-order), else
+ * c / groupsize.  Written for decode (a few tokens): the weights are read
+ * once per pass of up to 4 tokens.
+ *
+ *   x          m x cols fp16, row t at x + t*ldx (ldx >= cols); m >= 0
+ *              (0 is a no-op, and x and y may then be NULL).
+ *   packed     rows x gptq_packed_words(cols, bits) uint32 from
+ *              gptq_pack_codes.
+ *   scales,    rows x ceil(cols / groupsize) fp32 (the quantizer's outputs;
+ *   zeros      groupsize >= cols: one group).
+ *   g_idx      cols int32 or NULL; entries are clamped to the group range.
+ *   y          m x rows fp32 out, row t at y + t*ldy (ldy >= rows).
+ *   W_hat is formed in fp32 (one rounding) and the products are summed with
+ *   fp32 FMAs: each output adds 64 lane partial sums in a tree of depth 6, a
+ *   lane summing the K codes of each of at most ceil(words / 64) words, so
+ *   the error is at most (ceil(words / 64) * K + 8) * 2^-24 * sum |x W_hat|.
+ *   Asynchronous.
+ */
+gptq_status gptq_dequant_gemm(const void* x, int64_t m, int64_t cols, int64_t ldx,
+                              const uint32_t* packed, int bits, int64_t rows, const float* scales,
+                              const float* zeros, int groupsize, const int32_t* g_idx, float* y,
+                              int64_t ldy, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

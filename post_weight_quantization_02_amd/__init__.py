@@ -20,8 +20,11 @@ from ._lib import (  # noqa: F401
     OP_QUANTIZE,
     OP_QUANTIZE_PERM,
     act_order,
+    dequant_gemm,
     hessian_accumulate,
     lib,
+    pack_codes,
+    packed_words,
     prepare_hinv,
     prepare_hinv_perm,
     quantize_layer,

@@ -64,6 +64,13 @@ lib.gptq_act_order.argtypes = [_p, _i64, _p, _p]
 lib.gptq_prepare_hinv_perm.restype = _int
 lib.gptq_prepare_hinv_perm.argtypes = [_p, _i64, _p, ctypes.c_double, _p, _p, _sz,
                                        ctypes.POINTER(ctypes.c_int64), _p]
+lib.gptq_packed_words.restype = _i64
+lib.gptq_packed_words.argtypes = [_i64, _int]
+lib.gptq_pack_codes.restype = _int
+lib.gptq_pack_codes.argtypes = [_p, _i64, _i64, _int, _p, _p]
+lib.gptq_dequant_gemm.restype = _int
+lib.gptq_dequant_gemm.argtypes = [_p, _i64, _i64, _i64, _p, _int, _i64, _p, _p, _int, _p, _p,
+                                  _i64, _p]
 lib.gptq_quantize_layer_perm.restype = _int
 lib.gptq_quantize_layer_perm.argtypes = [_p, _int, _i64, _i64, _i64, _p, _p, _int, _int, _int,
                                          _p, _p, _p, _p, _p, _p, _sz, _p]
@@ -290,3 +297,55 @@ def quantize_layer_perm(W, perm, Hinv, bits: int = 4, groupsize: int = 128, bloc
                                       ws.data_ptr(), wsb, _stream_ptr(stream, dev))
     _check(st, "gptq_quantize_layer_perm")
     return codes, scales, zeros, losses, g_idx
+
+
+def packed_words(cols: int, bits: int) -> int:
+    return int(lib.gptq_packed_words(cols, bits))
+
+
+def pack_codes(codes, bits: int, out=None, stream=None):
+    """rows x packed_words(cols, bits) int32 tensor holding the codes'
+    uint32 words (gptq_pack_codes)."""
+    torch = _torch()
+    if codes.dtype != torch.uint8 or not codes.is_cuda or not codes.is_contiguous() or \
+            codes.dim() != 2:
+        raise ValueError("codes must be a contiguous 2-D uint8 CUDA tensor")
+    rows, cols = codes.shape
+    nw = packed_words(cols, bits)
+    if out is None:
+        out = torch.empty((rows, nw), dtype=torch.int32, device=codes.device)
+    st = lib.gptq_pack_codes(codes.data_ptr(), rows, cols, bits, out.data_ptr(),
+                             _stream_ptr(stream, codes.device))
+    _check(st, "gptq_pack_codes")
+    return out
+
+
+def dequant_gemm(x, packed, bits: int, cols: int, scales, zeros, groupsize: int, g_idx=None,
+                 out=None, stream=None):
+    """y = x W_hat^T (m x rows fp32) for fp16 x (m x cols) and the packed
+    codes with their scales and zeros (gptq_dequant_gemm)."""
+    torch = _torch()
+    if x.dtype != torch.float16 or not x.is_cuda or x.dim() != 2 or x.stride(1) != 1 or \
+            x.shape[1] != cols:
+        raise ValueError("x must be an m x cols fp16 CUDA tensor with unit column stride")
+    rows = packed.shape[0]
+    if packed.dtype != torch.int32 or not packed.is_contiguous() or \
+            packed.shape[1] != packed_words(cols, bits):
+        raise ValueError("packed must come from pack_codes for these cols and bits")
+    if groupsize <= 0:
+        groupsize = cols
+    ng = (cols + groupsize - 1) // groupsize
+    for t in (scales, zeros):
+        if t.dtype != torch.float32 or t.shape != (rows, ng) or not t.is_contiguous():
+            raise ValueError("scales and zeros must be contiguous rows x ngroups fp32")
+    g_idx = _check_perm(g_idx, cols, x.device)
+    m = x.shape[0]
+    if out is None:
+        out = torch.empty((m, rows), dtype=torch.float32, device=x.device)
+    ldx = x.stride(0) if m > 1 else cols
+    st = lib.gptq_dequant_gemm(x.data_ptr(), m, cols, ldx, packed.data_ptr(), bits, rows,
+                               scales.data_ptr(), zeros.data_ptr(), groupsize,
+                               g_idx.data_ptr() if g_idx is not None else None, out.data_ptr(),
+                               out.stride(0) if m > 1 else rows, _stream_ptr(stream, x.device))
+    _check(st, "gptq_dequant_gemm")
+    return out

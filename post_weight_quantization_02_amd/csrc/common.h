@@ -85,6 +85,14 @@ hipError_t launch_unpermute_outputs(const uint8_t* cp, int64_t rows, int64_t col
                                     uint8_t* codes, const float* lp, float* losses, int g,
                                     int* g_idx, hipStream_t s);
 hipError_t launch_group_index(int64_t cols, int g, int* g_idx, hipStream_t s);
+// inference with the packed codes
+int64_t packed_words(int64_t cols, int bits);
+hipError_t launch_pack_codes(const uint8_t* codes, int64_t rows, int64_t cols, int bits,
+                             uint32_t* packed, hipStream_t s);
+hipError_t launch_dequant_gemv(const _Float16* x, int64_t ldx, int64_t m, const uint32_t* packed,
+                               int bits, int64_t rows, int64_t cols, const float* scales,
+                               const float* zeros, int groupsize, const int* g_idx, float* y,
+                               int64_t ldy, hipStream_t s);
 constexpr int kSweepRows = 16;  // rows per sweep workgroup
 constexpr int kBlock = 128;     // columns per block
 constexpr int kSuperBlock = 512;  // columns per superblock of the two-level lazy update

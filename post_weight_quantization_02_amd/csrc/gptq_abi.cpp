@@ -345,4 +345,41 @@ gptq_status gptq_quantize_layer_perm(const void* W, int w_dtype, int64_t rows, i
                        codes, scales, zeros, losses, g_idx, workspace, workspace_bytes, stream);
 }
 
+int64_t gptq_packed_words(int64_t cols, int bits) {
+  if (cols < 1 || cols > kMaxDim || bits < 2 || bits > 8) return 0;
+  return packed_words(cols, bits);
+}
+
+gptq_status gptq_pack_codes(const uint8_t* codes, int64_t rows, int64_t cols, int bits,
+                            uint32_t* packed, void* stream) {
+  if (rows < 1 || cols < 1 || rows > kMaxDim || cols > kMaxDim || bits < 2 || bits > 8)
+    return GPTQ_ERR_INVALID_ARG;
+  if (codes == nullptr || packed == nullptr || !aligned(packed, 4)) return GPTQ_ERR_INVALID_ARG;
+  if (launch_pack_codes(codes, rows, cols, bits, packed, reinterpret_cast<hipStream_t>(stream)) !=
+      hipSuccess)
+    return GPTQ_ERR_HIP;
+  return GPTQ_OK;
+}
+
+gptq_status gptq_dequant_gemm(const void* x, int64_t m, int64_t cols, int64_t ldx,
+                              const uint32_t* packed, int bits, int64_t rows, const float* scales,
+                              const float* zeros, int groupsize, const int32_t* g_idx, float* y,
+                              int64_t ldy, void* stream) {
+  if (m < 0 || rows < 1 || cols < 1 || rows > kMaxDim || cols > kMaxDim) return GPTQ_ERR_INVALID_ARG;
+  if (bits < 2 || bits > 8 || groupsize < 1 || ldy < rows || (m > 0 && ldx < cols))
+    return GPTQ_ERR_INVALID_ARG;
+  if (m > kMaxElems / (ldx > ldy ? ldx : ldy)) return GPTQ_ERR_INVALID_ARG;
+  if (packed == nullptr || scales == nullptr || zeros == nullptr) return GPTQ_ERR_INVALID_ARG;
+  if (m > 0 && (x == nullptr || y == nullptr)) return GPTQ_ERR_INVALID_ARG;  // m = 0: never read
+  if (!aligned(x, 2) || !aligned(packed, 4) || !aligned(scales, 4) || !aligned(zeros, 4) ||
+      !aligned(g_idx, 4) || !aligned(y, 4))
+    return GPTQ_ERR_INVALID_ARG;
+  if (m == 0) return GPTQ_OK;
+  if (launch_dequant_gemv(reinterpret_cast<const _Float16*>(x), ldx, m, packed, bits, rows, cols,
+                          scales, zeros, groupsize, g_idx, y, ldy,
+                          reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
+    return GPTQ_ERR_HIP;
+  return GPTQ_OK;
+}
+
 }  // extern "C"

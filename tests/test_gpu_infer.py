@@ -1,0 +1,143 @@
+"""Packed storage and the dequantizing product on the GPU against the oracle.
+
+Inputs come from the oracle (its round-to-nearest codes, scales and zeros,
+seeded fp16 activations) and go to both sides. Packing is integer work and
+must be bit-exact. The product is compared output by output within the
+rounding bound of its arithmetic: W_hat is formed in fp32 with one rounding
+and the products are summed in fp32 FMAs, each output as 64 lane partial
+sums added in a tree of depth 6, a lane summing the K = floor(32 / bits)
+columns of each of at most ceil(nw / 64) words (nw words per row), so
+
+    |y_gpu - y| <= (ceil(nw / 64) * K + 8) * 2^-24 * sum_c |x_c W_hat_c|.
+"""
+import numpy as np
+import pytest
+
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def env():
+    import torch
+    import post_weight_quantization_02_amd as gq
+    return torch, gq
+
+
+def _cuda(env, a, dtype=None):
+    torch, _ = env
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=dtype)).cuda()
+
+
+def _layer(rows, cols, bits, g, seed):
+    rng = np.random.default_rng(seed)
+    W = rng.standard_normal((rows, cols)) * 0.02
+    r = oracle.rtn(W, bits, g)
+    return r["codes"], r["scales"], r["zeros"]
+
+
+def _bound(x, W_hat, cols, bits):
+    k = 32 // bits
+    nw = -(-cols // k)
+    return (-(-nw // 64) * k + 8) * 2.0 ** -24 * oracle.abs_products(x, W_hat)
+
+
+@pytest.mark.parametrize("bits,rows,cols", [(4, 37, 300), (3, 5, 1001), (2, 8, 17), (8, 3, 4096),
+                                            (5, 2, 77), (4, 1, 5)])
+def test_pack_bit_exact(env, bits, rows, cols):
+    torch, gq = env
+    rng = np.random.default_rng(bits * 1000 + cols)
+    codes = rng.integers(0, 256, size=(rows, cols)).astype(np.uint8)  # high bits must be masked
+    p = gq.pack_codes(_cuda(env, codes), bits)
+    torch.cuda.synchronize()
+    ref = oracle.pack_codes(codes & ((1 << bits) - 1), bits)
+    assert np.array_equal(p.cpu().numpy().view(np.uint32), ref)
+    assert p.shape[1] == gq.packed_words(cols, bits) == ref.shape[1]
+
+
+def _gemm_case(env, rows, cols, bits, g, m, seed, act_order=False):
+    torch, gq = env
+    codes, scales, zeros = _layer(rows, cols, bits, g, seed)
+    g_idx = None
+    if act_order:
+        perm = np.random.default_rng(seed + 1).permutation(cols)
+        g_idx = np.empty(cols, np.int64)
+        g_idx[perm] = np.arange(cols) // g
+    rng = np.random.default_rng(seed + 2)
+    x = rng.standard_normal((m, cols)).astype(np.float16)
+    packed = gq.pack_codes(_cuda(env, codes.astype(np.uint8)), bits)
+    y = gq.dequant_gemm(_cuda(env, x), packed, bits, cols, _cuda(env, scales, np.float32),
+                        _cuda(env, zeros, np.float32), g,
+                        None if g_idx is None else _cuda(env, g_idx, np.int32))
+    torch.cuda.synchronize()
+    y = y.cpu().numpy()
+    s32 = scales.astype(np.float32).astype(np.float64)
+    z32 = zeros.astype(np.float32).astype(np.float64)
+    ref = oracle.dequant_matmul(x, oracle.pack_codes(codes, bits), bits, cols, s32, z32, g, g_idx)
+    W_hat = oracle.dequant_weights(codes, s32, z32, g, g_idx)
+    err = np.abs(y - ref)
+    bound = _bound(x, W_hat, cols, bits)
+    assert np.all(err <= bound), (err.max(), bound[err > bound][:5])
+    return float((err / np.maximum(bound, 1e-300)).max())
+
+
+@pytest.mark.parametrize("rows,cols,bits,g,m", [
+    (64, 256, 4, 128, 1),
+    (37, 300, 4, 128, 3),      # ragged rows, ragged last word and group, one pass of 3 tokens
+    (50, 1000, 3, 128, 5),     # 10 codes per word, words straddle groups; two passes
+    (16, 512, 2, 32, 2),
+    (9, 640, 8, 64, 4),
+    (7, 200, 4, 200, 9),       # per-channel, three passes
+    (1, 5, 4, 128, 1),         # a single row, one partial word
+])
+def test_dequant_gemm_matches_oracle(env, rows, cols, bits, g, m):
+    _gemm_case(env, rows, cols, bits, g, m, seed=rows * 7 + cols)
+
+
+@pytest.mark.parametrize("bits", [3, 4])
+def test_dequant_gemm_with_g_idx(env, bits):
+    """Act-order groups: the group of each column comes from g_idx."""
+    _gemm_case(env, 40, 768, bits, 128, 2, seed=5, act_order=True)
+
+
+@pytest.mark.parametrize("rows,cols,m", [(4096, 4096, 1), (4096, 4096, 4), (11008, 4096, 1),
+                                         (4096, 11008, 2)])
+def test_dequant_gemm_full_layer_shapes(env, rows, cols, m):
+    """The Llama-7B-shaped projections of the decode benchmark, int4 g128,
+    every output compared."""
+    _gemm_case(env, rows, cols, 4, 128, m, seed=rows + cols + m)
+
+
+def test_dequant_gemm_zero_tokens_is_a_no_op(env):
+    torch, gq = env
+    codes, scales, zeros = _layer(8, 128, 4, 128, 1)
+    packed = gq.pack_codes(_cuda(env, codes.astype(np.uint8)), 4)
+    y = gq.dequant_gemm(torch.empty((0, 128), dtype=torch.float16, device="cuda"), packed, 4, 128,
+                        _cuda(env, scales, np.float32), _cuda(env, zeros, np.float32), 128)
+    torch.cuda.synchronize()
+    assert y.shape == (0, 8)
+
+
+def test_quantize_pack_product_end_to_end(env):
+    """The GPU's own quantizer output, packed and multiplied on the GPU,
+    equals the dense product with the GPU's dequantized weights (a property
+    of the GPU outputs, no oracle input from them)."""
+    torch, gq = env
+    import synth
+    from parity import dequant
+    L = synth.LAYERS["tiny"]
+    X = synth.activations(L.x)
+    W = synth.weights(L.w)
+    H = torch.zeros((L.x.d, L.x.d), dtype=torch.float32, device="cuda")
+    gq.hessian_accumulate(H, _cuda(env, X), 2.0)
+    U = gq.prepare_hinv(H, 0.01)
+    codes, scales, zeros, _ = gq.quantize_layer(_cuda(env, W), U, 4, 128, 128)
+    x = _cuda(env, X[:3])
+    y = gq.dequant_gemm(x, gq.pack_codes(codes, 4), 4, L.x.d, scales, zeros, 128)
+    torch.cuda.synchronize()
+    Wq = dequant(codes.cpu().numpy(), scales.cpu().numpy(), zeros.cpu().numpy(), 128)
+    xd = X[:3].astype(np.float64)
+    ref = xd @ Wq.T
+    bound = (-(-(L.x.d // 8) // 64) * 8 + 8) * 2.0 ** -24 * (np.abs(xd) @ np.abs(Wq).T)
+    assert np.all(np.abs(y.cpu().numpy() - ref) <= bound)
