@@ -242,6 +242,157 @@ class Job:
                     self.ev["quant"].append((q0, q1))
 
 
+DECODE_SHAPES = (("q", 4096, 4096), ("k", 4096, 4096), ("v", 4096, 4096), ("o", 4096, 4096),
+                 ("gate", 11008, 4096), ("up", 11008, 4096), ("down", 4096, 11008))
+DECODE_BLOCKS = 32
+
+
+def decode_cpu_baseline(m, bits, g, budget_s=10.0):
+    """The oracle's dequantizing product (unpack, dequantize, multiply in
+    fp64) on one matrix of each decode shape, scaled to the 224 calls of a
+    step."""
+    import numpy as np
+
+    import oracle
+    rng = np.random.default_rng(0)
+    cores = len(os.sched_getaffinity(0))
+    total, parts = 0.0, []
+    for shape in ({s[1:] for s in DECODE_SHAPES}):
+        rows, cols = shape
+        count = sum(1 for s in DECODE_SHAPES if s[1:] == shape) * DECODE_BLOCKS
+        codes = rng.integers(0, 1 << bits, size=(rows, cols))
+        packed = oracle.pack_codes(codes, bits)
+        ng = -(-cols // g)
+        sc = rng.uniform(1e-3, 2e-3, (rows, ng))
+        zr = rng.integers(0, 1 << bits, (rows, ng)).astype(np.float64)
+        x = rng.standard_normal((m, cols)).astype(np.float16)
+        t0 = time.perf_counter()
+        oracle.dequant_matmul(x, packed, bits, cols, sc, zr, g)
+        dt = time.perf_counter() - t0
+        total += dt * count
+        parts.append(f"{rows}x{cols}: {dt:.2f} s x {count}")
+    return {"value": round(total * 1e3, 1), "unit": "ms", "cores": cores, "kind": "oracle",
+            "sample": "one call per distinct shape (" + "; ".join(parts) + "), scaled by the "
+                      "number of calls of that shape in a step"}
+
+
+def decode_main(args):
+    """One decode step of W4A16 products over 32 Llama-7B-shaped blocks."""
+    import numpy as np
+    import torch
+
+    import post_weight_quantization_02_amd as gq
+
+    dev = torch.device("cuda:0")
+    m, bits, g = args.tokens, 4, 128
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1234)
+    log(f"generating {DECODE_BLOCKS} blocks of packed int{bits} g{g} weights on the device")
+    mats = []
+    alg_bytes = 0
+    for b in range(DECODE_BLOCKS):
+        for name, rows, cols in DECODE_SHAPES:
+            nw = gq.packed_words(cols, bits)
+            ng = -(-cols // g)
+            packed = torch.randint(-2 ** 31, 2 ** 31 - 1, (rows, nw), dtype=torch.int32,
+                                   device=dev, generator=gen)
+            sc = torch.rand((rows, ng), device=dev, generator=gen) * 1e-3 + 1e-3
+            zr = torch.randint(0, 1 << bits, (rows, ng), device=dev, generator=gen).float()
+            mats.append((name, rows, cols, packed, sc, zr))
+            alg_bytes += rows * nw * 4 + 2 * rows * ng * 4 + m * cols * 2 + m * rows * 4
+    xs = {c: torch.randn((m, c), device=dev, generator=gen).half() for c in (4096, 11008)}
+    ys = {r: torch.empty((m, r), dtype=torch.float32, device=dev) for r in (4096, 11008)}
+    stream = torch.cuda.current_stream(dev)
+
+    def step(events=None):
+        for i, (name, rows, cols, packed, sc, zr) in enumerate(mats):
+            if events is not None:
+                events[i][0].record(stream)
+            gq.dequant_gemm(xs[cols], packed, bits, cols, sc, zr, g, out=ys[rows])
+            if events is not None:
+                events[i][1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    # The 224 launches of a step are replayed from a HIP graph: launched one by
+    # one from Python, the host's per-call cost (about 9 us) exceeds a
+    # launch's GPU time and the GPU would wait for the host.
+    graph = None
+    if not args.no_graph:
+        side = torch.cuda.Stream(dev)
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            step()  # warm-up on the capture stream
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        torch.cuda.synchronize()
+    run = graph.replay if graph is not None else step
+    for _ in range(2):
+        run()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    ev_ms_step = e0.elapsed_time(e1) / args.steps
+    # per-launch durations (a separate eager pass with events around every call)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in mats]
+    step(ev)
+    torch.cuda.synchronize()
+    launch_ms = [a.elapsed_time(b) for a, b in ev]
+    kernel_ms = float(np.sum(launch_ms))
+    # roofline: the step's algorithmic bytes over its event-timed duration
+    # (every launch of the step, gaps between launches included)
+    achieved = alg_bytes / (ev_ms_step * 1e-3) / 1e9
+    per_shape = {}
+    for (name, rows, cols, *_), t in zip(mats, launch_ms):
+        per_shape.setdefault(f"{rows}x{cols}", []).append(t)
+    cpu = None if args.no_cpu else decode_cpu_baseline(m, bits, g)
+    line = {
+        "metric": f"ms per decode step ({DECODE_BLOCKS} Llama-7B-shaped blocks, int{bits} g{g} "
+                  f"W{bits}A16 products, {m} token{'s' if m > 1 else ''})",
+        "value": round(ms_step, 4),
+        "unit": "ms",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int4 codes, f32 dequant and accumulate, f16 activations",
+        "data": "synthetic (seeded random codes, scales and zeros generated on the device; "
+                "random fp16 activations)",
+        "config": {"workload": f"decode: {DECODE_BLOCKS} x (q,k,v,o 4096x4096; gate,up "
+                               f"11008x4096; down 4096x11008), {len(mats)} products per step, "
+                               f"{m} token(s)",
+                   "algorithmic_bytes_per_step": alg_bytes,
+                   "graph_replay": graph is not None,
+                   "event_ms_per_step": round(ev_ms_step, 4),
+                   "eager_launch_us_by_shape": {k: round(1e3 * float(np.mean(v)), 2)
+                                                for k, v in per_shape.items()},
+                   "eager_ms_per_step": round(kernel_ms, 4)},
+        "roofline": {"bound": "hbm",
+                     "kernel": "dequant_gemv_fast_kernel<4,%d> (the 224 launches of a step, "
+                               "gaps included)" % min(m, 4),
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "bytes_per_step": alg_bytes},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -258,11 +409,20 @@ def main():
     ap.add_argument("--no-peaks", action="store_true", help="skip the library peak probes")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run one device copy of this size first (counter calibration)")
+    ap.add_argument("--decode", action="store_true",
+                    help="time one decode step of packed int4 products instead of quantization")
+    ap.add_argument("--tokens", type=int, default=1, help="tokens per decode step (--decode)")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="--decode: launch the step's products one by one instead of a graph")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); how this path "
               "shards over several GPUs is a design note, not a measured run.", file=sys.stderr)
         sys.exit(2)
+
+    if args.decode:
+        decode_main(args)
+        return
 
     import numpy as np
     import torch

@@ -12,11 +12,15 @@
 // c / groupsize.
 //
 // The product is written for decode: a few tokens x (fp16, m x cols) against
-// a weight matrix streamed once from HBM per pass of up to 4 tokens.  Each
-// wave owns 4 output rows; its lanes take the packed words of those rows in
-// lane order (each load instruction reads consecutive words), dequantize in
-// fp32 and accumulate x * W_hat with fp32 FMAs; the 64 lane sums of every
-// output are added by lane shuffles.
+// a weight matrix streamed once from HBM per pass of up to 4 tokens.  The
+// general kernel (any bit width, g_idx) gives each wave 4 output rows whose
+// packed words its lanes take in lane order, dequantizes in fp32 and
+// accumulates x * W_hat with fp32 FMAs.  The fast kernel (2, 4, 8 bits, runs
+// of 4 words inside a group) stages x in LDS, reads 4 words per lane and row
+// with one 16-byte load (prefetched a batch ahead with the groups' scales and
+// zeros), sums x * code per run -- for 4 bits two codes per v_dot2_f32_f16 --
+// and applies scale and zero once per run.  The 64 lane sums of every output
+// are added by lane shuffles.
 #include "common.h"
 
 namespace gptq {
@@ -139,6 +143,250 @@ __global__ __launch_bounds__(256) void dequant_gemv_kernel(
   }
 }
 
+// Code j of a word as a float, for 2, 4 and 8 bits: the codes are spread
+// into bytes by masking (K / 4 byte lanes per mask) and each byte converted
+// with v_cvt_f32_ubyteN.
+template <int BITS>
+__device__ inline void unpack_word(uint32_t w, float (&q)[32 / BITS]) {
+  if (BITS == 8) {
+#pragma unroll
+    for (int b = 0; b < 4; ++b) q[b] = (float)((w >> (8 * b)) & 0xFFu);
+  } else {
+    constexpr int P = 8 / BITS;  // codes per byte
+    constexpr uint32_t M = (BITS == 4) ? 0x0F0F0F0Fu : 0x03030303u;
+#pragma unroll
+    for (int k = 0; k < P; ++k) {
+      const uint32_t v = (w >> (BITS * k)) & M;  // byte n holds code P*n + k
+#pragma unroll
+      for (int n = 0; n < 4; ++n) q[P * n + k] = (float)((v >> (8 * n)) & 0xFFu);
+    }
+  }
+}
+
+// Fast path for 2, 4 and 8 bits when every 4-word run of a row (4K columns)
+// lies in one group and no g_idx is given.  x (MT tokens) is staged in LDS as
+// fp16.  A lane reads 4 words of each of its R rows with one 16-byte load
+// and, per run, sums x * code and x over the run's columns; the group's scale
+// and zero then enter once per run: y += s * (sum x q - z * sum x), which
+// equals sum x (q - z) s.  Rounding: the products x * q are exact in fp32,
+// so each output's error is at most
+// (4K + ceil(runs / 64) + 8) * 2^-24 * sum_c |x_c| (|q_c| + |z_g|) s_g.
+template <int BITS, int MT, int R>
+__global__ __launch_bounds__(256) void dequant_gemv_fast_kernel(
+    const _Float16* __restrict__ x, int64_t ldx, int m, const uint32_t* __restrict__ packed,
+    int64_t nw, int64_t rows, int64_t cols, const float* __restrict__ scales,
+    const float* __restrict__ zeros, int64_t ngroups, int groupsize, float* __restrict__ y,
+    int64_t ldy, bool xvec) {
+  constexpr int K = 32 / BITS;
+  constexpr int CW = 4 * K;  // columns per 4-word run
+  // R: output rows per wave
+
+  extern __shared__ __attribute__((aligned(16))) _Float16 xs[];
+  const int64_t ldxs = nw * K;  // a multiple of CW (nw % 4 == 0)
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t r0 = ((int64_t)blockIdx.x * 4 + wave) * R;
+  // rows past the matrix read row rows - 1 and are not stored
+  int64_t rr[R];
+#pragma unroll
+  for (int i = 0; i < R; ++i) rr[i] = (r0 + i < rows) ? r0 + i : rows - 1;
+  const int64_t nv = nw / 4;  // 4-word runs per row
+  // a batch is 2 runs per lane and row; the next batch is loaded while the
+  // current one is used, and the first before x is staged
+  // The group's scale and zero of each run travel with its words, so no
+  // run waits for them after its products.
+  uint4 qv[2][R], qn[2][R];
+  float sv[2][R], zv[2][R], sn[2][R], zn[2][R];
+  auto load_batch = [&](int64_t vb, uint4 (&dst)[2][R], float (&ds)[2][R], float (&dz)[2][R]) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int64_t v = vb + 64 * u + lane;
+      const int64_t vc = (v < nv) ? v : nv - 1;
+      const int64_t g = vc * CW / groupsize;
+#pragma unroll
+      for (int i = 0; i < R; ++i) {
+        dst[u][i] = reinterpret_cast<const uint4*>(packed + rr[i] * nw)[vc];
+        ds[u][i] = scales[rr[i] * ngroups + g];
+        dz[u][i] = zeros[rr[i] * ngroups + g];
+      }
+    }
+  };
+  load_batch(0, qv, sv, zv);
+  // staging: 8 halves per 16-byte load where the row allows it (ldxs is a
+  // multiple of 8; x rows 16-byte aligned when xvec)
+  typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+#pragma unroll
+  for (int t = 0; t < MT; ++t)
+    for (int64_t c = (int64_t)threadIdx.x * 8; c < ldxs; c += 256 * 8) {
+      h8 v;
+      if (xvec && t < m && c + 8 <= cols) {
+        v = *reinterpret_cast<const h8*>(x + t * ldx + c);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          v[j] = (t < m && c + j < cols) ? x[t * ldx + c + j] : (_Float16)0.f;
+      }
+      *reinterpret_cast<h8*>(xs + t * ldxs + c) = v;
+    }
+  __syncthreads();
+  if (r0 >= rows) return;  // no barrier below
+  float acc[R][MT];
+#pragma unroll
+  for (int i = 0; i < R; ++i)
+#pragma unroll
+    for (int t = 0; t < MT; ++t) acc[i][t] = 0.f;
+  for (int64_t vb = 0; vb < nv; vb += 128) {
+    const bool more = vb + 128 < nv;
+    if (more) load_batch(vb + 128, qn, sn, zn);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int64_t v = vb + 64 * u + lane;
+      if (v >= nv) break;
+      const int64_t c0 = v * CW;
+      float sx[MT], sq[R][MT];
+#pragma unroll
+      for (int t = 0; t < MT; ++t) {
+        sx[t] = 0.f;
+#pragma unroll
+        for (int i = 0; i < R; ++i) sq[i][t] = 0.f;
+      }
+      if constexpr (BITS == 4) {
+        // Two codes per packed-fp16 operation: (w >> 4k) & 0x000F000F puts
+        // codes k and k + 4 of a word in the low bits of the two halves; OR
+        // 0x6400 makes each the fp16 number 1024 + q, and subtracting 1024
+        // leaves q exactly.  v_dot2_f32_f16 then adds x_k q_k + x_{k+4}
+        // q_{k+4} (exact products) to an fp32 sum; x is paired to match once
+        // per word for all rows.
+        typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+        typedef _Float16 h8v __attribute__((ext_vector_type(8)));
+        const h2 ones = {(_Float16)1.f, (_Float16)1.f};
+        const h2 k1024 = {(_Float16)1024.f, (_Float16)1024.f};
+#pragma unroll
+        for (int wd = 0; wd < 4; ++wd) {
+          h2 xp[MT][4];
+#pragma unroll
+          for (int t = 0; t < MT; ++t) {
+            const h8v xw = *reinterpret_cast<const h8v*>(xs + t * ldxs + c0 + wd * 8);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              xp[t][k] = h2{xw[k], xw[k + 4]};
+              sx[t] = __builtin_amdgcn_fdot2(xp[t][k], ones, sx[t], false);
+            }
+          }
+#pragma unroll
+          for (int i = 0; i < R; ++i) {
+            const uint32_t w = (wd == 0) ? qv[u][i].x : (wd == 1) ? qv[u][i].y
+                             : (wd == 2) ? qv[u][i].z : qv[u][i].w;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              const uint32_t b = ((w >> (4 * k)) & 0x000F000Fu) | 0x64006400u;
+              const h2 q = __builtin_bit_cast(h2, b) - k1024;
+#pragma unroll
+              for (int t = 0; t < MT; ++t)
+                sq[i][t] = __builtin_amdgcn_fdot2(xp[t][k], q, sq[i][t], false);
+            }
+          }
+        }
+      } else {
+#pragma unroll
+      for (int wd = 0; wd < 4; ++wd) {
+        float xv[MT][K];
+#pragma unroll
+        for (int t = 0; t < MT; ++t) {
+          // K halves at an offset that is a multiple of K (>= 4): 8-byte
+          // aligned reads of 4 halves
+          const _Float16* xp = xs + t * ldxs + c0 + wd * K;
+#pragma unroll
+          for (int j0 = 0; j0 < K; j0 += 4) {
+            typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+            const h4 hv = *reinterpret_cast<const h4*>(xp + j0);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              xv[t][j0 + j] = (float)hv[j];
+              sx[t] += xv[t][j0 + j];
+            }
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < R; ++i) {
+          const uint32_t w = (wd == 0) ? qv[u][i].x : (wd == 1) ? qv[u][i].y
+                           : (wd == 2) ? qv[u][i].z : qv[u][i].w;
+          float q[K];
+          unpack_word<BITS>(w, q);
+#pragma unroll
+          for (int j = 0; j < K; ++j)
+#pragma unroll
+            for (int t = 0; t < MT; ++t) sq[i][t] = __builtin_fmaf(xv[t][j], q[j], sq[i][t]);
+        }
+      }
+      }
+#pragma unroll
+      for (int i = 0; i < R; ++i)
+#pragma unroll
+        for (int t = 0; t < MT; ++t)
+          acc[i][t] = __builtin_fmaf(sv[u][i], __builtin_fmaf(-zv[u][i], sx[t], sq[i][t]),
+                                     acc[i][t]);
+    }
+    if (more) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int i = 0; i < R; ++i) {
+          qv[u][i] = qn[u][i];
+          sv[u][i] = sn[u][i];
+          zv[u][i] = zn[u][i];
+        }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < R; ++i)
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+      float v = acc[i][t];
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+      acc[i][t] = v;
+    }
+  if (lane == 0) {
+#pragma unroll
+    for (int i = 0; i < R; ++i)
+#pragma unroll
+      for (int t = 0; t < MT; ++t)
+        if (t < m && r0 + i < rows) y[(int64_t)t * ldy + r0 + i] = acc[i][t];
+  }
+}
+
+constexpr int64_t kGemvLds = 64 * 1024;  // x staging limit of the fast path
+
+template <int BITS, int R>
+hipError_t launch_gemv_fast(const _Float16* x, int64_t ldx, int64_t m, const uint32_t* packed,
+                            int64_t nw, int64_t rows, int64_t cols, const float* scales,
+                            const float* zeros, int64_t ngroups, int groupsize, float* y,
+                            int64_t ldy, int maxmt, hipStream_t s) {
+  const dim3 grid((unsigned)ceil_div(rows, 4 * R));
+  const int64_t row_bytes = nw * (32 / BITS) * 2;
+  const bool xvec = (ldx % 8 == 0) && ((reinterpret_cast<uintptr_t>(x) & 15) == 0);
+  for (int64_t t0 = 0; t0 < m; t0 += maxmt) {
+    const int mt = (int)((m - t0 < maxmt) ? m - t0 : maxmt);
+    const _Float16* xt = x + t0 * ldx;
+    float* yt = y + t0 * ldy;
+    if (mt == 1)
+      hipLaunchKernelGGL((dequant_gemv_fast_kernel<BITS, 1, R>), grid, dim3(256),
+                         (unsigned)row_bytes, s, xt, ldx, mt, packed, nw, rows, cols, scales,
+                         zeros, ngroups, groupsize, yt, ldy, xvec);
+    else if (mt == 2)
+      hipLaunchKernelGGL((dequant_gemv_fast_kernel<BITS, 2, R>), grid, dim3(256),
+                         (unsigned)(2 * row_bytes), s, xt, ldx, mt, packed, nw, rows, cols,
+                         scales, zeros, ngroups, groupsize, yt, ldy, xvec);
+    else
+      hipLaunchKernelGGL((dequant_gemv_fast_kernel<BITS, 4, R>), grid, dim3(256),
+                         (unsigned)(4 * row_bytes), s, xt, ldx, mt, packed, nw, rows, cols,
+                         scales, zeros, ngroups, groupsize, yt, ldy, xvec);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
 template <int BITS>
 hipError_t launch_gemv_bits(const _Float16* x, int64_t ldx, int64_t m, const uint32_t* packed,
                             int64_t nw, int64_t rows, int64_t cols, const float* scales,
@@ -182,6 +430,26 @@ hipError_t launch_dequant_gemv(const _Float16* x, int64_t ldx, int64_t m, const 
                                int64_t ldy, hipStream_t s) {
   const int64_t nw = packed_words(cols, bits);
   const int64_t ngroups = ceil_div(cols, groupsize);
+  // fast path: 2, 4 or 8 bits, whole 4-word runs inside groups, no g_idx,
+  // 16-byte aligned rows, x of at least one token fits the LDS staging
+  if ((bits == 2 || bits == 4 || bits == 8) && g_idx == nullptr && nw % 4 == 0 &&
+      groupsize % (4 * (32 / bits)) == 0 && (reinterpret_cast<uintptr_t>(packed) & 15) == 0) {
+    const int64_t row_bytes = nw * (32 / bits) * 2;
+    const int maxmt = (int)((kGemvLds / row_bytes >= 4) ? 4 : (kGemvLds / row_bytes >= 2) ? 2
+                                                                                          : 1);
+    if (row_bytes <= kGemvLds) {
+      // two rows per wave (measured against one and four: 1.78 ms per
+      // decode step against 1.86 and 1.81 at one token)
+      if (bits == 2)
+        return launch_gemv_fast<2, 2>(x, ldx, m, packed, nw, rows, cols, scales, zeros, ngroups,
+                                      groupsize, y, ldy, maxmt, s);
+      if (bits == 4)
+        return launch_gemv_fast<4, 2>(x, ldx, m, packed, nw, rows, cols, scales, zeros, ngroups,
+                                      groupsize, y, ldy, maxmt, s);
+      return launch_gemv_fast<8, 2>(x, ldx, m, packed, nw, rows, cols, scales, zeros, ngroups,
+                                    groupsize, y, ldy, maxmt, s);
+    }
+  }
   switch (bits) {
 #define GPTQ_GEMV(B) \
   case B:            \

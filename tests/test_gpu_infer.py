@@ -3,12 +3,20 @@
 Inputs come from the oracle (its round-to-nearest codes, scales and zeros,
 seeded fp16 activations) and go to both sides. Packing is integer work and
 must be bit-exact. The product is compared output by output within the
-rounding bound of its arithmetic: W_hat is formed in fp32 with one rounding
-and the products are summed in fp32 FMAs, each output as 64 lane partial
-sums added in a tree of depth 6, a lane summing the K = floor(32 / bits)
-columns of each of at most ceil(nw / 64) words (nw words per row), so
+rounding bound of its arithmetic. Two kernels compute it (K = floor(32 /
+bits) codes per word, nw words per row, 64 lanes whose partial sums are
+added in a tree of depth 6):
+  * the general one forms W_hat in fp32 (one rounding) and sums x * W_hat,
+    a lane over the K columns of each of at most ceil(nw / 64) words;
+  * the 2/4/8-bit one sums the exact products x * q and x over runs of 4K
+    columns inside one group and adds s * (sum x q - z sum x) per run, a lane
+    over at most ceil(nw / 256) runs.
+Both are within
 
-    |y_gpu - y| <= (ceil(nw / 64) * K + 8) * 2^-24 * sum_c |x_c W_hat_c|.
+    |y_gpu - y| <= F * 2^-24 * sum_c |x_c| (|q_c| + |z_c|) s_c,
+    F = max(ceil(nw / 64) K, 4K + ceil(nw / 256)) + 8,
+
+which bounds either sum since |q - z| <= |q| + |z|.
 """
 import numpy as np
 import pytest
@@ -37,10 +45,16 @@ def _layer(rows, cols, bits, g, seed):
     return r["codes"], r["scales"], r["zeros"]
 
 
-def _bound(x, W_hat, cols, bits):
+def _bound(x, codes, scales, zeros, cols, bits, g, g_idx=None):
     k = 32 // bits
     nw = -(-cols // k)
-    return (-(-nw // 64) * k + 8) * 2.0 ** -24 * oracle.abs_products(x, W_hat)
+    f = max(-(-nw // 64) * k, 4 * k + -(-nw // 256)) + 8
+    if g_idx is None:
+        gi = np.arange(cols) // (cols if g <= 0 else g)
+    else:
+        gi = np.asarray(g_idx, np.int64)
+    mag = (np.abs(codes) + np.abs(zeros[:, gi])) * np.abs(scales[:, gi])
+    return f * 2.0 ** -24 * (np.abs(np.asarray(x, np.float64)) @ mag.T)
 
 
 @pytest.mark.parametrize("bits,rows,cols", [(4, 37, 300), (3, 5, 1001), (2, 8, 17), (8, 3, 4096),
@@ -75,9 +89,8 @@ def _gemm_case(env, rows, cols, bits, g, m, seed, act_order=False):
     s32 = scales.astype(np.float32).astype(np.float64)
     z32 = zeros.astype(np.float32).astype(np.float64)
     ref = oracle.dequant_matmul(x, oracle.pack_codes(codes, bits), bits, cols, s32, z32, g, g_idx)
-    W_hat = oracle.dequant_weights(codes, s32, z32, g, g_idx)
     err = np.abs(y - ref)
-    bound = _bound(x, W_hat, cols, bits)
+    bound = _bound(x, codes, s32, z32, cols, bits, g, g_idx)
     assert np.all(err <= bound), (err.max(), bound[err > bound][:5])
     return float((err / np.maximum(bound, 1e-300)).max())
 
@@ -136,8 +149,51 @@ def test_quantize_pack_product_end_to_end(env):
     x = _cuda(env, X[:3])
     y = gq.dequant_gemm(x, gq.pack_codes(codes, 4), 4, L.x.d, scales, zeros, 128)
     torch.cuda.synchronize()
-    Wq = dequant(codes.cpu().numpy(), scales.cpu().numpy(), zeros.cpu().numpy(), 128)
+    c, sc, zr = codes.cpu().numpy(), scales.cpu().numpy(), zeros.cpu().numpy()
+    Wq = dequant(c, sc, zr, 128)
     xd = X[:3].astype(np.float64)
     ref = xd @ Wq.T
-    bound = (-(-(L.x.d // 8) // 64) * 8 + 8) * 2.0 ** -24 * (np.abs(xd) @ np.abs(Wq).T)
+    bound = _bound(xd, c.astype(np.float64), sc.astype(np.float64), zr.astype(np.float64),
+                   L.x.d, 4, 128)
     assert np.all(np.abs(y.cpu().numpy() - ref) <= bound)
+
+
+def test_dequant_gemm_graph_replay(env):
+    """The decode products captured in a HIP graph: every replay, with eager
+    work changing x in between, equals the eager result bit for bit."""
+    torch, gq = env
+    mats = []
+    for rows, cols, seed in ((96, 512, 1), (40, 1024, 2)):
+        codes, scales, zeros = _layer(rows, cols, 4, 128, seed)
+        mats.append((cols, gq.pack_codes(_cuda(env, codes.astype(np.uint8)), 4),
+                     _cuda(env, scales, np.float32), _cuda(env, zeros, np.float32),
+                     torch.empty((2, rows), dtype=torch.float32, device="cuda")))
+    xs = {c: torch.zeros((2, c), dtype=torch.float16, device="cuda") for c in (512, 1024)}
+
+    def step():
+        for cols, p, sc, zr, y in mats:
+            gq.dequant_gemm(xs[cols], p, 4, cols, sc, zr, 128, out=y)
+
+    stream = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        step()
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(9)
+    for rep in range(4):
+        for c, xt in xs.items():  # eager work between replays
+            xt.copy_(torch.from_numpy(rng.standard_normal((2, c)).astype(np.float16)).cuda())
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = [m[4].clone() for m in mats]
+        step()
+        torch.cuda.synchronize()
+        for a, m in zip(got, mats):
+            assert torch.equal(a, m[4]), rep
