@@ -48,13 +48,14 @@ constexpr int NB = kPanel;  // 64
 constexpr int PP = NB + 2;  // LDS pitch (doubles) of the 64x64 panel tiles: conflict-free
                             // MFMA operand reads (rows m = lane%16, columns k = lane/16)
 
-// 1/sqrt(p) to fp64 accuracy: hardware estimate + two Newton steps.
+// 1/sqrt(p): hardware estimate (measured 5.2e-8 relative) and one Newton
+// step (measured 4.1e-15 relative over 2^20 values from 2^-40 to 2^41; a
+// second step gives 2.4e-16).  It sits on the serial pivot chain of every
+// 64x64 diagonal factorization; 4e-15 per pivot is far below what the fp32
+// Hinv resolves.
 __device__ inline double rsqrt_f64(double p) {
-  double r = __builtin_amdgcn_rsq(p);
-  double h = 0.5 * p;
-  r = r * __builtin_fma(-h * r, r, 1.5);
-  r = r * __builtin_fma(-h * r, r, 1.5);
-  return r;
+  const double r = __builtin_amdgcn_rsq(p);
+  return r * __builtin_fma(-0.5 * p * r, r, 1.5);
 }
 constexpr int GT = 64;      // GEMM tile edge
 constexpr int GK = 16;      // GEMM K chunk
