@@ -36,6 +36,7 @@
 //     1-based index; the host reads it once at the end.
 #include <limits.h>
 
+#include <atomic>
 #include <utility>
 
 #include "common.h"
@@ -1060,18 +1061,19 @@ __global__ __launch_bounds__(256) void store_upper_kernel(const double* __restri
   }
 }
 
-// Compute units of the current device (cached per device id).
+// Compute units of the current device (cached per device id; concurrent
+// callers may both query and store the same value).
 int device_cus() {
-  static int cus[64] = {0};
+  static std::atomic<int> cus[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cus[dev] <= 0) {
-    int n = 0;
+  int n = cus[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
       n = 256;
-    cus[dev] = n;
+    cus[dev].store(n, std::memory_order_relaxed);
   }
-  return cus[dev];
+  return n;
 }
 
 }  // namespace
