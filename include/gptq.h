@@ -305,10 +305,12 @@ gptq_status gptq_pack_codes(const uint8_t* codes, int64_t rows, int64_t cols, in
  *   zeros      groupsize >= cols: one group).
  *   g_idx      cols int32 or NULL; entries are clamped to the group range.
  *   y          m x rows fp32 out, row t at y + t*ldy (ldy >= rows).
- *   W_hat is formed in fp32 (one rounding) and the products are summed with
- *   fp32 FMAs: each output adds 64 lane partial sums in a tree of depth 6, a
- *   lane summing the K codes of each of at most ceil(words / 64) words, so
- *   the error is at most (ceil(words / 64) * K + 8) * 2^-24 * sum |x W_hat|.
+ *   Arithmetic is fp32.  For 2, 4 and 8 bits without g_idx, when runs of 4
+ *   words lie inside groups, each run's exact products x * code and the sum
+ *   of x are added up and the run contributes s * (sum x q - z * sum x);
+ *   otherwise W_hat is formed in fp32 and x * W_hat summed.  Every output's
+ *   error is at most F * 2^-24 * sum_c |x_c| (|q_c| + |z|) s with
+ *   F = max(ceil(words / 64) * K, 4K + ceil(words / 256)) + 8.
  *   Asynchronous.
  */
 gptq_status gptq_dequant_gemm(const void* x, int64_t m, int64_t cols, int64_t ldx,
