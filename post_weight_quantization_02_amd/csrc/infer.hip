@@ -31,8 +31,8 @@ namespace {
 __global__ __launch_bounds__(256) void pack_codes_kernel(const uint8_t* __restrict__ codes,
                                                          int64_t rows, int64_t cols, int bits,
                                                          int64_t nw, uint32_t* __restrict__ out) {
-  const int64_t r = blockIdx.y;
-  const int64_t w = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t r = blockIdx.x;
+  const int64_t w = (int64_t)blockIdx.y * 256 + threadIdx.x;
   if (w >= nw) return;
   const int k = 32 / bits;
   const uint32_t mask = (1u << bits) - 1u;
@@ -419,7 +419,8 @@ int64_t packed_words(int64_t cols, int bits) { return ceil_div(cols, 32 / bits);
 hipError_t launch_pack_codes(const uint8_t* codes, int64_t rows, int64_t cols, int bits,
                              uint32_t* packed, hipStream_t s) {
   const int64_t nw = packed_words(cols, bits);
-  hipLaunchKernelGGL(pack_codes_kernel, dim3((unsigned)ceil_div(nw, 256), (unsigned)rows),
+  // rows in x (up to 2^31 workgroups), words in y (at most 2^20 / 4 / 256)
+  hipLaunchKernelGGL(pack_codes_kernel, dim3((unsigned)rows, (unsigned)ceil_div(nw, 256)),
                      dim3(256), 0, s, codes, rows, cols, bits, nw, packed);
   return hipGetLastError();
 }
