@@ -171,7 +171,7 @@ __device__ inline void unpack_word(uint32_t w, float (&q)[32 / BITS]) {
 // equals sum x (q - z) s.  Rounding: the products x * q are exact in fp32,
 // so each output's error is at most
 // (4K + ceil(runs / 64) + 8) * 2^-24 * sum_c |x_c| (|q_c| + |z_g|) s_g.
-template <int BITS, int MT, int R>
+template <int BITS, int MT, int R, bool XD>
 __global__ __launch_bounds__(256) void dequant_gemv_fast_kernel(
     const _Float16* __restrict__ x, int64_t ldx, int m, const uint32_t* __restrict__ packed,
     int64_t nw, int64_t rows, int64_t cols, const float* __restrict__ scales,
@@ -179,7 +179,10 @@ __global__ __launch_bounds__(256) void dequant_gemv_fast_kernel(
     int64_t ldy, bool xvec) {
   constexpr int K = 32 / BITS;
   constexpr int CW = 4 * K;  // columns per 4-word run
-  // R: output rows per wave
+  // R: output rows per wave.  XD (4 bits, one token, cols a multiple of 32,
+  // x rows 16-byte aligned): each lane loads its runs' x directly with the
+  // packed words instead of the workgroup staging x in LDS (no barrier).
+  static_assert(!XD || (BITS == 4 && MT == 1), "direct x: 4 bits, one token");
 
   extern __shared__ __attribute__((aligned(16))) _Float16 xs[];
   const int64_t ldxs = nw * K;  // a multiple of CW (nw % 4 == 0)
@@ -196,7 +199,9 @@ __global__ __launch_bounds__(256) void dequant_gemv_fast_kernel(
   // run waits for them after its products.
   uint4 qv[2][R], qn[2][R];
   float sv[2][R], zv[2][R], sn[2][R], zn[2][R];
-  auto load_batch = [&](int64_t vb, uint4 (&dst)[2][R], float (&ds)[2][R], float (&dz)[2][R]) {
+  uint4 xb[2][XD ? 4 : 1], xn[2][XD ? 4 : 1];
+  auto load_batch = [&](int64_t vb, uint4 (&dst)[2][R], float (&ds)[2][R], float (&dz)[2][R],
+                        uint4 (&dx)[2][XD ? 4 : 1]) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int64_t v = vb + 64 * u + lane;
@@ -208,12 +213,18 @@ __global__ __launch_bounds__(256) void dequant_gemv_fast_kernel(
         ds[u][i] = scales[rr[i] * ngroups + g];
         dz[u][i] = zeros[rr[i] * ngroups + g];
       }
+      if constexpr (XD) {
+#pragma unroll
+        for (int wd = 0; wd < 4; ++wd)
+          dx[u][wd] = *reinterpret_cast<const uint4*>(x + vc * CW + 8 * wd);
+      }
     }
   };
-  load_batch(0, qv, sv, zv);
+  load_batch(0, qv, sv, zv, xb);
   // staging: 8 halves per 16-byte load where the row allows it (ldxs is a
   // multiple of 8; x rows 16-byte aligned when xvec)
   typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+  if constexpr (!XD) {
 #pragma unroll
   for (int t = 0; t < MT; ++t)
     for (int64_t c = (int64_t)threadIdx.x * 8; c < ldxs; c += 256 * 8) {
@@ -228,6 +239,7 @@ __global__ __launch_bounds__(256) void dequant_gemv_fast_kernel(
       *reinterpret_cast<h8*>(xs + t * ldxs + c) = v;
     }
   __syncthreads();
+  }
   if (r0 >= rows) return;  // no barrier below
   float acc[R][MT];
 #pragma unroll
@@ -236,7 +248,7 @@ __global__ __launch_bounds__(256) void dequant_gemv_fast_kernel(
     for (int t = 0; t < MT; ++t) acc[i][t] = 0.f;
   for (int64_t vb = 0; vb < nv; vb += 128) {
     const bool more = vb + 128 < nv;
-    if (more) load_batch(vb + 128, qn, sn, zn);
+    if (more) load_batch(vb + 128, qn, sn, zn, xn);
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int64_t v = vb + 64 * u + lane;
@@ -265,7 +277,11 @@ __global__ __launch_bounds__(256) void dequant_gemv_fast_kernel(
           h2 xp[MT][4];
 #pragma unroll
           for (int t = 0; t < MT; ++t) {
-            const h8v xw = *reinterpret_cast<const h8v*>(xs + t * ldxs + c0 + wd * 8);
+            h8v xw;
+            if constexpr (XD)
+              xw = __builtin_bit_cast(h8v, xb[u][wd]);
+            else
+              xw = *reinterpret_cast<const h8v*>(xs + t * ldxs + c0 + wd * 8);
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
               xp[t][k] = h2{xw[k], xw[k + 4]};
@@ -335,6 +351,12 @@ __global__ __launch_bounds__(256) void dequant_gemv_fast_kernel(
           sv[u][i] = sn[u][i];
           zv[u][i] = zn[u][i];
         }
+      if constexpr (XD) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int wd = 0; wd < 4; ++wd) xb[u][wd] = xn[u][wd];
+      }
     }
   }
 #pragma unroll
@@ -358,6 +380,22 @@ __global__ __launch_bounds__(256) void dequant_gemv_fast_kernel(
 constexpr int64_t kGemvLds = 64 * 1024;  // x staging limit of the fast path
 
 template <int BITS, int R>
+hipError_t launch_gemv_fast_direct(const _Float16* x, int64_t ldx, int64_t m,
+                                   const uint32_t* packed, int64_t nw, int64_t rows, int64_t cols,
+                                   const float* scales, const float* zeros, int64_t ngroups,
+                                   int groupsize, float* y, int64_t ldy, hipStream_t s) {
+  const dim3 grid((unsigned)ceil_div(rows, 4 * R));
+  for (int64_t t0 = 0; t0 < m; ++t0) {
+    hipLaunchKernelGGL((dequant_gemv_fast_kernel<BITS, 1, R, true>), grid, dim3(256), 0, s,
+                       x + t0 * ldx, ldx, 1, packed, nw, rows, cols, scales, zeros, ngroups,
+                       groupsize, y + t0 * ldy, ldy, true);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+template <int BITS, int R>
 hipError_t launch_gemv_fast(const _Float16* x, int64_t ldx, int64_t m, const uint32_t* packed,
                             int64_t nw, int64_t rows, int64_t cols, const float* scales,
                             const float* zeros, int64_t ngroups, int groupsize, float* y,
@@ -370,15 +408,15 @@ hipError_t launch_gemv_fast(const _Float16* x, int64_t ldx, int64_t m, const uin
     const _Float16* xt = x + t0 * ldx;
     float* yt = y + t0 * ldy;
     if (mt == 1)
-      hipLaunchKernelGGL((dequant_gemv_fast_kernel<BITS, 1, R>), grid, dim3(256),
+      hipLaunchKernelGGL((dequant_gemv_fast_kernel<BITS, 1, R, false>), grid, dim3(256),
                          (unsigned)row_bytes, s, xt, ldx, mt, packed, nw, rows, cols, scales,
                          zeros, ngroups, groupsize, yt, ldy, xvec);
     else if (mt == 2)
-      hipLaunchKernelGGL((dequant_gemv_fast_kernel<BITS, 2, R>), grid, dim3(256),
+      hipLaunchKernelGGL((dequant_gemv_fast_kernel<BITS, 2, R, false>), grid, dim3(256),
                          (unsigned)(2 * row_bytes), s, xt, ldx, mt, packed, nw, rows, cols,
                          scales, zeros, ngroups, groupsize, yt, ldy, xvec);
     else
-      hipLaunchKernelGGL((dequant_gemv_fast_kernel<BITS, 4, R>), grid, dim3(256),
+      hipLaunchKernelGGL((dequant_gemv_fast_kernel<BITS, 4, R, false>), grid, dim3(256),
                          (unsigned)(4 * row_bytes), s, xt, ldx, mt, packed, nw, rows, cols,
                          scales, zeros, ngroups, groupsize, yt, ldy, xvec);
     const hipError_t e = hipGetLastError();
@@ -444,6 +482,10 @@ hipError_t launch_dequant_gemv(const _Float16* x, int64_t ldx, int64_t m, const 
       if (bits == 2)
         return launch_gemv_fast<2, 2>(x, ldx, m, packed, nw, rows, cols, scales, zeros, ngroups,
                                       groupsize, y, ldy, maxmt, s);
+      // one token, whole 32-column runs, aligned x rows: x loaded directly
+      if (bits == 4 && m == 1 && cols % 32 == 0 && (reinterpret_cast<uintptr_t>(x) & 15) == 0)
+        return launch_gemv_fast_direct<4, 2>(x, ldx, m, packed, nw, rows, cols, scales, zeros,
+                                             ngroups, groupsize, y, ldy, s);
       if (bits == 4)
         return launch_gemv_fast<4, 2>(x, ldx, m, packed, nw, rows, cols, scales, zeros, ngroups,
                                       groupsize, y, ldy, maxmt, s);
