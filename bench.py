@@ -244,6 +244,9 @@ class Job:
 
 DECODE_SHAPES = (("q", 4096, 4096), ("k", 4096, 4096), ("v", 4096, 4096), ("o", 4096, 4096),
                  ("gate", 11008, 4096), ("up", 11008, 4096), ("down", 4096, 11008))
+# q|k|v and gate|up stored as one matrix each (the same bytes in 4 products)
+DECODE_SHAPES_FUSED = (("qkv", 12288, 4096), ("o", 4096, 4096), ("gate_up", 22016, 4096),
+                       ("down", 4096, 11008))
 DECODE_BLOCKS = 32
 
 
@@ -288,10 +291,11 @@ def decode_main(args):
     gen = torch.Generator(device=dev)
     gen.manual_seed(1234)
     log(f"generating {DECODE_BLOCKS} blocks of packed int{bits} g{g} weights on the device")
+    shapes = DECODE_SHAPES_FUSED if args.fused else DECODE_SHAPES
     mats = []
     alg_bytes = 0
     for b in range(DECODE_BLOCKS):
-        for name, rows, cols in DECODE_SHAPES:
+        for name, rows, cols in shapes:
             nw = gq.packed_words(cols, bits)
             ng = -(-cols // g)
             packed = torch.randint(-2 ** 31, 2 ** 31 - 1, (rows, nw), dtype=torch.int32,
@@ -301,7 +305,8 @@ def decode_main(args):
             mats.append((name, rows, cols, packed, sc, zr))
             alg_bytes += rows * nw * 4 + 2 * rows * ng * 4 + m * cols * 2 + m * rows * 4
     xs = {c: torch.randn((m, c), device=dev, generator=gen).half() for c in (4096, 11008)}
-    ys = {r: torch.empty((m, r), dtype=torch.float32, device=dev) for r in (4096, 11008)}
+    ys = {r: torch.empty((m, r), dtype=torch.float32, device=dev)
+          for r in {rows for _, rows, _ in shapes}}
     stream = torch.cuda.current_stream(dev)
 
     def step(events=None):
@@ -360,7 +365,8 @@ def decode_main(args):
     cpu = None if args.no_cpu else decode_cpu_baseline(m, bits, g)
     line = {
         "metric": f"ms per decode step ({DECODE_BLOCKS} Llama-7B-shaped blocks, int{bits} g{g} "
-                  f"W{bits}A16 products, {m} token{'s' if m > 1 else ''})",
+                  f"W{bits}A16 products{', fused qkv and gate_up' if args.fused else ''}, "
+                  f"{m} token{'s' if m > 1 else ''})",
         "value": round(ms_step, 4),
         "unit": "ms",
         "n_gpus": 1,
@@ -374,8 +380,9 @@ def decode_main(args):
         "data": "synthetic (seeded random codes, scales and zeros generated on the device; "
                 "random fp16 activations)",
         "config": {"workload": f"decode: {DECODE_BLOCKS} x (q,k,v,o 4096x4096; gate,up "
-                               f"11008x4096; down 4096x11008), {len(mats)} products per step, "
-                               f"{m} token(s)",
+                               f"11008x4096; down 4096x11008)"
+                               + (", q|k|v and gate|up stored fused" if args.fused else "")
+                               + f", {len(mats)} products per step, {m} token(s)",
                    "algorithmic_bytes_per_step": alg_bytes,
                    "graph_replay": graph is not None,
                    "event_ms_per_step": round(ev_ms_step, 4),
@@ -383,8 +390,8 @@ def decode_main(args):
                                                 for k, v in per_shape.items()},
                    "eager_ms_per_step": round(kernel_ms, 4)},
         "roofline": {"bound": "hbm",
-                     "kernel": "dequant_gemv_fast_kernel<4,%d> (the 224 launches of a step, "
-                               "gaps included)" % min(m, 4),
+                     "kernel": "dequant_gemv_fast_kernel (the %d launches of a step, gaps "
+                               "included)" % len(mats),
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
                      "bytes_per_step": alg_bytes},
@@ -412,6 +419,8 @@ def main():
     ap.add_argument("--decode", action="store_true",
                     help="time one decode step of packed int4 products instead of quantization")
     ap.add_argument("--tokens", type=int, default=1, help="tokens per decode step (--decode)")
+    ap.add_argument("--fused", action="store_true",
+                    help="--decode: q|k|v and gate|up stored as one matrix each")
     ap.add_argument("--no-graph", action="store_true",
                     help="--decode: launch the step's products one by one instead of a graph")
     args = ap.parse_args()
