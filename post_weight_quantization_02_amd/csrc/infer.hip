@@ -254,12 +254,12 @@ __global__ __launch_bounds__(256) void dequant_gemv_fast_kernel(
       const int64_t v = vb + 64 * u + lane;
       if (v >= nv) break;
       const int64_t c0 = v * CW;
-      float sx[MT], sq[R][MT];
+      float sx[MT], sq[R][MT], so[R][MT];
 #pragma unroll
       for (int t = 0; t < MT; ++t) {
         sx[t] = 0.f;
 #pragma unroll
-        for (int i = 0; i < R; ++i) sq[i][t] = 0.f;
+        for (int i = 0; i < R; ++i) sq[i][t] = so[i][t] = 0.f;
       }
       if constexpr (BITS == 4) {
         // Two codes per packed-fp16 operation: (w >> 4k) & 0x000F000F puts
@@ -292,13 +292,19 @@ __global__ __launch_bounds__(256) void dequant_gemv_fast_kernel(
           for (int i = 0; i < R; ++i) {
             const uint32_t w = (wd == 0) ? qv[u][i].x : (wd == 1) ? qv[u][i].y
                              : (wd == 2) ? qv[u][i].z : qv[u][i].w;
+            // codes 2j, 2j+4 from (w >> 8j) & 0x000F000F; codes 2j+1, 2j+5
+            // in place from (w >> 8j) & 0x00F000F0 as 16 q (exact in fp16),
+            // summed apart and scaled by 1/16 (exact) when the run is applied
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-              const uint32_t b = ((w >> (4 * k)) & 0x000F000Fu) | 0x64006400u;
-              const h2 q = __builtin_bit_cast(h2, b) - k1024;
+            for (int j = 0; j < 2; ++j) {
+              const uint32_t wj = w >> (8 * j);
+              const h2 qe = __builtin_bit_cast(h2, (wj & 0x000F000Fu) | 0x64006400u) - k1024;
+              const h2 qo = __builtin_bit_cast(h2, (wj & 0x00F000F0u) | 0x64006400u) - k1024;
 #pragma unroll
-              for (int t = 0; t < MT; ++t)
-                sq[i][t] = __builtin_amdgcn_fdot2(xp[t][k], q, sq[i][t], false);
+              for (int t = 0; t < MT; ++t) {
+                sq[i][t] = __builtin_amdgcn_fdot2(xp[t][2 * j], qe, sq[i][t], false);
+                so[i][t] = __builtin_amdgcn_fdot2(xp[t][2 * j + 1], qo, so[i][t], false);
+              }
             }
           }
         }
@@ -338,9 +344,10 @@ __global__ __launch_bounds__(256) void dequant_gemv_fast_kernel(
 #pragma unroll
       for (int i = 0; i < R; ++i)
 #pragma unroll
-        for (int t = 0; t < MT; ++t)
-          acc[i][t] = __builtin_fmaf(sv[u][i], __builtin_fmaf(-zv[u][i], sx[t], sq[i][t]),
-                                     acc[i][t]);
+        for (int t = 0; t < MT; ++t) {
+          const float q = __builtin_fmaf(so[i][t], 0.0625f, sq[i][t]);  // so is 0 below 4 bits
+          acc[i][t] = __builtin_fmaf(sv[u][i], __builtin_fmaf(-zv[u][i], sx[t], q), acc[i][t]);
+        }
     }
     if (more) {
 #pragma unroll
