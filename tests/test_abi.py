@@ -159,3 +159,38 @@ def test_act_order_entry_points_validation():
     assert lib.gptq_quantize_layer_perm(*args, FAKE, q, None) == WS
     assert lib.gptq_quantize_layer_perm(*args[:5], FAKE + 2, *args[6:], FAKE, qp, None) == E
     assert lib.gptq_quantize_layer_perm(*args[:14], FAKE + 2, FAKE, qp, None) == E  # g_idx
+
+
+def test_pack_and_product_validation():
+    """Host-side checks of gptq_pack_codes and gptq_dequant_gemm (no launch)."""
+    E = gq.GPTQ_ERR_INVALID_ARG
+    assert gq.packed_words(4096, 4) == 512
+    assert gq.packed_words(4097, 4) == 513
+    assert gq.packed_words(100, 3) == 10
+    assert gq.packed_words(17, 2) == 2
+    assert gq.packed_words(0, 4) == 0 and gq.packed_words(10, 1) == 0 and gq.packed_words(10, 9) == 0
+    pk = lib.gptq_pack_codes
+    assert pk(None, 4, 8, 4, FAKE, None) == E
+    assert pk(FAKE, 4, 8, 4, None, None) == E
+    assert pk(FAKE, 0, 8, 4, FAKE, None) == E
+    assert pk(FAKE, 4, 8, 1, FAKE, None) == E
+    assert pk(FAKE, 4, 8, 9, FAKE, None) == E
+    assert pk(FAKE, 4, 8, 4, FAKE + 2, None) == E          # packed must be 4-byte aligned
+
+    def dq(x=FAKE, m=1, cols=256, ldx=256, packed=FAKE, bits=4, rows=8, sc=FAKE, zr=FAKE, g=128,
+           gidx=None, y=FAKE, ldy=8):
+        return lib.gptq_dequant_gemm(x, m, cols, ldx, packed, bits, rows, sc, zr, g, gidx, y, ldy,
+                                     None)
+    assert dq(m=-1) == E
+    assert dq(rows=0) == E and dq(cols=0) == E
+    assert dq(bits=1) == E and dq(bits=9) == E
+    assert dq(g=0) == E
+    assert dq(ldy=7) == E
+    assert dq(ldx=255) == E
+    assert dq(x=None) == E and dq(y=None) == E
+    assert dq(packed=None) == E and dq(sc=None) == E and dq(zr=None) == E
+    assert dq(x=FAKE + 1) == E                              # fp16 x: 2-byte aligned
+    assert dq(packed=FAKE + 2) == E and dq(sc=FAKE + 2) == E and dq(y=FAKE + 2) == E
+    assert dq(gidx=FAKE + 2) == E
+    # m = 0 is a no-op: nothing is read, so null x and y are accepted
+    assert dq(m=0, x=None, y=None, ldx=0) == gq.GPTQ_OK
