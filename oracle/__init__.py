@@ -31,3 +31,9 @@ from .infer64 import (  # noqa: F401
     dequant_matmul,
     abs_products,
 )
+from .pipeline64 import (  # noqa: F401
+    quantize_one_layer,
+    relu_to_f16,
+    quantized_layer_output,
+    two_layer_block,
+)
