@@ -318,6 +318,38 @@ gptq_status gptq_dequant_gemm(const void* x, int64_t m, int64_t cols, int64_t ld
                               const float* zeros, int groupsize, const int32_t* g_idx, float* y,
                               int64_t ldy, void* stream);
 
+/*
+ * gptq_linear_forward -- the layer's forward product from its stored form
+ * for many tokens, y = act(x W_hat^T) in fp16, with W_hat as for
+ * gptq_dequant_gemm.  Quantizing layer by layer, each layer's calibration
+ * inputs are recorded from the model as it stands, so a later layer's inputs
+ * are this product of the layers already quantized ("GPTQ: fixing errors as
+ * you go", "The algorithm, in words").
+ *
+ *   x          m x cols fp16, row t at x + t*ldx (ldx >= cols, ldx % 8 == 0,
+ *              ldx < 2^23, x 16-byte aligned); m >= 0 (0 is a no-op, and x
+ *              and y may then be NULL).
+ *   packed     rows x gptq_packed_words(cols, 4) uint32 from gptq_pack_codes
+ *              with bits = 4, 16-byte aligned.
+ *   scales,    rows x ceil(cols / groupsize) fp32, the quantizer's outputs
+ *   zeros      (groupsize >= cols: one group); zeros must be integers in
+ *              [0, 15], as the quantizer writes them.
+ *   groupsize  a multiple of 128, or >= cols.  cols must be a multiple of
+ *              128.  Other shapes and bit widths: GPTQ_ERR_UNSUPPORTED.
+ *   relu       0: y = x W_hat^T; 1: y = max(x W_hat^T, 0).
+ *   y          m x rows fp16 out, row t at y + t*ldy (ldy >= rows).
+ *   Arithmetic: the products x * (code - zero) are exact in fp32, each
+ *   group's sum is an fp32 sum of at most groupsize of them, and the groups
+ *   are added as acc += scale * sum, so before the one rounding to fp16
+ *   (half to even) every output is within
+ *   (groupsize + ngroups + 2) * 2^-24 * sum_c |x_c| |code_c - zero| scale
+ *   of the exact product.  Asynchronous.
+ */
+gptq_status gptq_linear_forward(const void* x, int64_t m, int64_t cols, int64_t ldx,
+                                const uint32_t* packed, int bits, int64_t rows,
+                                const float* scales, const float* zeros, int groupsize, int relu,
+                                void* y, int64_t ldy, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

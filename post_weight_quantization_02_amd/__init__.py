@@ -23,6 +23,7 @@ from ._lib import (  # noqa: F401
     dequant_gemm,
     hessian_accumulate,
     lib,
+    linear_forward,
     pack_codes,
     packed_words,
     prepare_hinv,

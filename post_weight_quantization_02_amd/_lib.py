@@ -71,6 +71,9 @@ lib.gptq_pack_codes.argtypes = [_p, _i64, _i64, _int, _p, _p]
 lib.gptq_dequant_gemm.restype = _int
 lib.gptq_dequant_gemm.argtypes = [_p, _i64, _i64, _i64, _p, _int, _i64, _p, _p, _int, _p, _p,
                                   _i64, _p]
+lib.gptq_linear_forward.restype = _int
+lib.gptq_linear_forward.argtypes = [_p, _i64, _i64, _i64, _p, _int, _i64, _p, _p, _int, _int, _p,
+                                    _i64, _p]
 lib.gptq_quantize_layer_perm.restype = _int
 lib.gptq_quantize_layer_perm.argtypes = [_p, _int, _i64, _i64, _i64, _p, _p, _int, _int, _int,
                                          _p, _p, _p, _p, _p, _p, _sz, _p]
@@ -348,4 +351,37 @@ def dequant_gemm(x, packed, bits: int, cols: int, scales, zeros, groupsize: int,
                                g_idx.data_ptr() if g_idx is not None else None, out.data_ptr(),
                                out.stride(0) if m > 1 else rows, _stream_ptr(stream, x.device))
     _check(st, "gptq_dequant_gemm")
+    return out
+
+
+def linear_forward(x, packed, bits: int, cols: int, scales, zeros, groupsize: int,
+                   relu: bool = False, out=None, stream=None):
+    """y = x W_hat^T, or max(x W_hat^T, 0) with relu, as m x rows fp16, for
+    fp16 x (m x cols) and the 4-bit packed codes with their scales and zeros
+    (gptq_linear_forward: the product for many tokens on MFMA)."""
+    torch = _torch()
+    if x.dtype != torch.float16 or not x.is_cuda or x.dim() != 2 or x.stride(1) != 1 or \
+            x.shape[1] != cols:
+        raise ValueError("x must be an m x cols fp16 CUDA tensor with unit column stride")
+    rows = packed.shape[0]
+    if packed.dtype != torch.int32 or not packed.is_contiguous() or \
+            packed.shape[1] != packed_words(cols, bits):
+        raise ValueError("packed must come from pack_codes for these cols and bits")
+    if groupsize <= 0:
+        groupsize = cols
+    ng = (cols + groupsize - 1) // groupsize
+    for t in (scales, zeros):
+        if t.dtype != torch.float32 or t.shape != (rows, ng) or not t.is_contiguous():
+            raise ValueError("scales and zeros must be contiguous rows x ngroups fp32")
+    m = x.shape[0]
+    if out is None:
+        out = torch.empty((m, rows), dtype=torch.float16, device=x.device)
+    elif out.dtype != torch.float16 or out.shape != (m, rows) or out.stride(1) != 1:
+        raise ValueError("out must be an m x rows fp16 tensor with unit column stride")
+    ldx = x.stride(0) if m > 1 else cols
+    st = lib.gptq_linear_forward(x.data_ptr(), m, cols, ldx, packed.data_ptr(), bits, rows,
+                                 scales.data_ptr(), zeros.data_ptr(), groupsize, 1 if relu else 0,
+                                 out.data_ptr(), out.stride(0) if m > 1 else rows,
+                                 _stream_ptr(stream, x.device))
+    _check(st, "gptq_linear_forward")
     return out

@@ -382,4 +382,28 @@ gptq_status gptq_dequant_gemm(const void* x, int64_t m, int64_t cols, int64_t ld
   return GPTQ_OK;
 }
 
+gptq_status gptq_linear_forward(const void* x, int64_t m, int64_t cols, int64_t ldx,
+                                const uint32_t* packed, int bits, int64_t rows,
+                                const float* scales, const float* zeros, int groupsize, int relu,
+                                void* y, int64_t ldy, void* stream) {
+  if (m < 0 || rows < 1 || cols < 1 || rows > kMaxDim || cols > kMaxDim) return GPTQ_ERR_INVALID_ARG;
+  if (bits < 2 || bits > 8 || groupsize < 1 || ldy < rows || (m > 0 && ldx < cols) ||
+      (relu != 0 && relu != 1))
+    return GPTQ_ERR_INVALID_ARG;
+  if (m > kMaxElems / (ldx > ldy ? ldx : ldy)) return GPTQ_ERR_INVALID_ARG;
+  if (packed == nullptr || scales == nullptr || zeros == nullptr) return GPTQ_ERR_INVALID_ARG;
+  if (m > 0 && (x == nullptr || y == nullptr)) return GPTQ_ERR_INVALID_ARG;  // m = 0: never read
+  if (!aligned(x, 2) || !aligned(packed, 4) || !aligned(scales, 4) || !aligned(zeros, 4) ||
+      !aligned(y, 2))
+    return GPTQ_ERR_INVALID_ARG;
+  if (bits != 4 || !linear_int4_supported(cols, groupsize, x, m > 0 ? ldx : 8, packed))
+    return GPTQ_ERR_UNSUPPORTED;
+  if (m == 0) return GPTQ_OK;
+  if (launch_linear_int4(reinterpret_cast<const _Float16*>(x), ldx, m, packed, rows, cols, scales,
+                         zeros, groupsize, relu == 1, reinterpret_cast<_Float16*>(y), ldy,
+                         reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
+    return GPTQ_ERR_HIP;
+  return GPTQ_OK;
+}
+
 }  // extern "C"

@@ -194,3 +194,32 @@ def test_pack_and_product_validation():
     assert dq(gidx=FAKE + 2) == E
     # m = 0 is a no-op: nothing is read, so null x and y are accepted
     assert dq(m=0, x=None, y=None, ldx=0) == gq.GPTQ_OK
+
+
+def test_linear_forward_validation():
+    """Host-side checks of gptq_linear_forward (no launch): invalid arguments,
+    then the shapes the MFMA kernel does not take."""
+    E, U = gq.GPTQ_ERR_INVALID_ARG, gq.GPTQ_ERR_UNSUPPORTED
+
+    def lf(x=FAKE, m=1, cols=256, ldx=256, packed=FAKE, bits=4, rows=8, sc=FAKE, zr=FAKE, g=128,
+           relu=0, y=FAKE, ldy=8):
+        return lib.gptq_linear_forward(x, m, cols, ldx, packed, bits, rows, sc, zr, g, relu, y, ldy,
+                                       None)
+    assert lf(m=-1) == E
+    assert lf(rows=0) == E and lf(cols=0) == E
+    assert lf(bits=1) == E and lf(bits=9) == E
+    assert lf(g=0) == E and lf(relu=2) == E and lf(relu=-1) == E
+    assert lf(ldy=7) == E and lf(ldx=255) == E
+    assert lf(x=None) == E and lf(y=None) == E
+    assert lf(packed=None) == E and lf(sc=None) == E and lf(zr=None) == E
+    assert lf(x=FAKE + 1) == E and lf(y=FAKE + 1) == E
+    assert lf(packed=FAKE + 2) == E and lf(sc=FAKE + 2) == E
+    # valid arguments the 4-bit MFMA kernel does not take
+    assert lf(bits=3) == U and lf(bits=8) == U
+    assert lf(cols=200, ldx=200) == U                       # cols not a multiple of 128
+    assert lf(g=64) == U                                    # groups inside a 128-column stage
+    assert lf(ldx=260) == U                                 # rows not 16-byte aligned
+    assert lf(x=FAKE + 8) == U and lf(packed=FAKE + 4) == U
+    assert lf(ldx=1 << 23, cols=256) == U                   # lane offsets would pass 32 bits
+    # m = 0 is a no-op: nothing is read, so null x and y are accepted
+    assert lf(m=0, x=None, y=None, ldx=0) == gq.GPTQ_OK

@@ -1,0 +1,117 @@
+"""The 4-bit layer's forward product for many tokens (MFMA, fp16 out) against
+the oracle.
+
+Codes, scales and zeros come from the oracle's round-to-nearest quantizer and
+are packed by the oracle; x is seeded fp16. The GPU sums the exact products
+x * (code - zero) of each group in fp32 and adds scale * group sum, so before
+its one rounding to fp16 every output is within
+
+    B = (g + ngroups + 2) * 2^-24 * sum_c |x_c| |code_c - zero| scale
+
+of the exact product; the oracle rounds its fp64 product to fp16 once. Both
+roundings are to nearest, so the two fp16 results differ by at most
+B + ulp16(|y| + B), ulp16 the fp16 spacing at that magnitude.
+"""
+import numpy as np
+import pytest
+
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def env():
+    import torch
+    import post_weight_quantization_02_amd as gq
+    return torch, gq
+
+
+def _cuda(env, a, dtype=None):
+    torch, _ = env
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=dtype)).cuda()
+
+
+def ulp16(v):
+    """fp16 spacing at magnitude v (subnormal spacing 2^-24 below 2^-14)."""
+    _, e = np.frexp(np.maximum(np.abs(v), 2.0 ** -30))
+    return np.ldexp(1.0, np.maximum(e - 1, -14) - 10)
+
+
+def _quantized(rows, cols, g, seed):
+    W = np.random.default_rng(seed).standard_normal((rows, cols)) * 0.02
+    r = oracle.rtn(W, 4, g, precision="f32")
+    return r["codes"], r["scales"].astype(np.float32), r["zeros"].astype(np.float32)
+
+
+def _check(y_gpu, x, codes, s32, z32, g, relu):
+    cols = codes.shape[1]
+    gg = cols if g <= 0 or g >= cols else g
+    ng = -(-cols // gg)
+    gi = np.arange(cols) // gg
+    ref = oracle.quantized_layer_output(x, codes, s32.astype(np.float64), z32.astype(np.float64), gg)
+    y_ref = oracle.relu_to_f16(ref) if relu else ref.astype(np.float16)
+    mag = np.abs(codes - z32.astype(np.float64)[:, gi]) * s32.astype(np.float64)[:, gi]
+    B = (gg + ng + 2) * 2.0 ** -24 * (np.abs(x.astype(np.float64)) @ mag.T)
+    tol = B + ulp16(np.abs(ref) + B)
+    err = np.abs(y_gpu.astype(np.float64) - y_ref.astype(np.float64))
+    assert np.all(err <= tol), (float(err.max()), int((err > tol).sum()))
+    return float(np.mean(y_gpu == y_ref))
+
+
+def _case(env, m, rows, cols, g, relu, seed):
+    torch, gq = env
+    codes, s32, z32 = _quantized(rows, cols, g, seed)
+    x = np.random.default_rng(seed + 1).standard_normal((m, cols)).astype(np.float16)
+    packed = _cuda(env, oracle.pack_codes(codes, 4).view(np.int32))
+    y = gq.linear_forward(_cuda(env, x), packed, 4, cols, _cuda(env, s32), _cuda(env, z32), g,
+                          relu=relu)
+    torch.cuda.synchronize()
+    return _check(y.cpu().numpy(), x, codes, s32, z32, g, relu)
+
+
+@pytest.mark.parametrize("m,rows,cols,g,relu", [
+    (1, 1, 128, 128, False),        # one token, one output, one group
+    (300, 600, 512, 128, True),     # ragged token and output tiles, 3 x 3 tiles
+    (129, 257, 256, 128, False),    # one past a tile in both directions
+    (200, 96, 384, 0, True),        # per-channel: one group over 384 columns
+    (64, 300, 640, 256, False),     # groups of 256 and a short last group of 128
+    (1000, 512, 1024, 128, True),   # eight stages through the 3-stage ring
+])
+def test_linear_forward_matches_oracle(env, m, rows, cols, g, relu):
+    same = _case(env, m, rows, cols, g, relu, seed=m + rows + cols)
+    print("identical fp16 outputs", same)
+    assert same >= 0.99
+
+
+def test_linear_forward_full_width(env):
+    """The MLP up projection's shape, 11008 x 4096, on 4096 tokens: every
+    output compared."""
+    same = _case(env, 4096, 11008, 4096, 128, True, seed=7)
+    assert same >= 0.99
+
+
+def test_linear_forward_zero_tokens_and_unsupported_shapes(env):
+    torch, gq = env
+    codes, s32, z32 = _quantized(8, 256, 128, 3)
+    packed = _cuda(env, oracle.pack_codes(codes, 4).view(np.int32))
+    y = gq.linear_forward(torch.empty((0, 256), dtype=torch.float16, device="cuda"), packed, 4, 256,
+                          _cuda(env, s32), _cuda(env, z32), 128)
+    assert y.shape == (0, 8)
+    x = torch.zeros((4, 256), dtype=torch.float16, device="cuda")
+    # groups of 64 are not a multiple of the 128-column stage
+    c64, s64, z64 = _quantized(8, 256, 64, 3)
+    with pytest.raises(gq.GPTQError, match="UNSUPPORTED"):
+        gq.linear_forward(x, _cuda(env, oracle.pack_codes(c64, 4).view(np.int32)), 4, 256,
+                          _cuda(env, s64), _cuda(env, z64), 64)
+    # 3-bit codes
+    r3 = oracle.rtn(np.random.default_rng(4).standard_normal((8, 256)) * 0.02, 3, 128)
+    with pytest.raises(gq.GPTQError, match="UNSUPPORTED"):
+        gq.linear_forward(x, _cuda(env, oracle.pack_codes(r3["codes"], 3).view(np.int32)), 3, 256,
+                          _cuda(env, r3["scales"], np.float32), _cuda(env, r3["zeros"], np.float32),
+                          128)
+    # x rows not 16-byte aligned
+    xb = torch.zeros((4, 264), dtype=torch.float16, device="cuda")[:, 4:260]
+    with pytest.raises(gq.GPTQError, match="UNSUPPORTED"):
+        gq.linear_forward(xb, packed, 4, 256, _cuda(env, s32), _cuda(env, z32), 128)
+    torch.cuda.synchronize()
