@@ -400,6 +400,164 @@ def decode_main(args):
     print(json.dumps(line), flush=True)
 
 
+def pipeline_cpu_baseline(x, W1, W2, budget_s=4.0):
+    """The fp64 oracle's layer-by-layer block on a bounded sample, each phase
+    timed on a slice and scaled to the full block: H1 and H2 on 4096-token
+    chunks until about budget_s, the two Hinv preparations at full size
+    (d = 4096) and at half size scaled by 8 (d = 11008, cubic), the two sweeps
+    on 512 rows, the forward product on 2048 tokens."""
+    import numpy as np
+
+    import oracle
+    from oracle.pipeline64 import relu_to_f16
+    n, d = x.shape
+    m, dout = W1.shape[0], W2.shape[0]
+    cores = len(os.sched_getaffinity(0))
+
+    def hess(X, dd):
+        t0, toks, H = time.perf_counter(), 0, np.zeros((dd, dd))
+        while toks < X.shape[0] and time.perf_counter() - t0 < budget_s:
+            H += oracle.hessian([X[toks:toks + 4096]], dd)
+            toks = min(toks + 4096, X.shape[0])
+        return (time.perf_counter() - t0) * X.shape[0] / toks, H * (X.shape[0] / toks), toks
+
+    t_h1, H1, tok1 = hess(x, d)
+    t0 = time.perf_counter()
+    U1, _ = oracle.hinv_upper(H1, 0.01)
+    t_p1 = time.perf_counter() - t0
+    r1 = min(512, m)
+    t0 = time.perf_counter()
+    q1 = oracle.gptq(W1[:r1], U1, 4, 128, 128, precision="f32")
+    t_s1 = (time.perf_counter() - t0) * m / r1
+    nf = min(2048, n)
+    t0 = time.perf_counter()
+    y = relu_to_f16(oracle.quantized_layer_output(x[:nf], q1["codes"], q1["scales"], q1["zeros"],
+                                                  128))
+    t_f = (time.perf_counter() - t0) * (n / nf) * (m / r1)
+    y1 = np.tile(y, (1, -(-m // r1)))[:, :m]  # inputs of the right shape for timing H2
+    t0, toks, H2 = time.perf_counter(), 0, np.zeros((m, m))
+    while toks < nf and time.perf_counter() - t0 < budget_s:
+        H2 += oracle.hessian([y1[toks:toks + 1024]], m)
+        toks += 1024
+    t_h2 = (time.perf_counter() - t0) * n / toks
+    h = m // 2
+    Hh = H2[:h, :h] + np.eye(h) * np.mean(np.diag(H2))
+    t0 = time.perf_counter()
+    U2h, _ = oracle.hinv_upper(Hh, 0.01)
+    t_p2 = (time.perf_counter() - t0) * (m / h) ** 3
+    r2 = min(256, dout)
+    U2 = np.kron(np.eye(2), U2h)  # a 2h x 2h factor: the sweep's cost does not depend on values
+    t0 = time.perf_counter()
+    oracle.gptq(W2[:r2, :U2.shape[0]], U2, 4, 128, 128, precision="f32")
+    t_s2 = (time.perf_counter() - t0) * dout / r2
+    est = t_h1 + t_p1 + t_s1 + t_f + t_h2 + t_p2 + t_s2
+    return {
+        "value": round(est * 1e3, 1), "unit": "ms", "cores": cores, "kind": "oracle",
+        "sample": (f"H1 on {tok1} of {n} tokens, prep at d={d}, sweep 1 on {r1} of {m} rows, "
+                   f"forward on {nf} tokens x {r1} outputs, H2 on {toks} tokens, prep at "
+                   f"d={h} (x{(m / h) ** 3:.0f}), sweep 2 on {r2} of {dout} rows; each scaled "
+                   f"to the full block; s: H1 {t_h1:.1f}, prep1 {t_p1:.1f}, sweep1 {t_s1:.1f}, "
+                   f"forward {t_f:.1f}, H2 {t_h2:.1f}, prep2 {t_p2:.1f}, sweep2 {t_s2:.1f}"),
+    }
+
+
+def pipeline_main(args):
+    """Layer-by-layer quantization of the Llama-7B-shaped MLP up -> ReLU ->
+    down pair: the down projection's H is recorded from the quantized up
+    projection's outputs."""
+    import contextlib
+
+    import numpy as np
+    import torch
+
+    import post_weight_quantization_02_amd as gq
+    import synth
+
+    dev = torch.device("cuda:0")
+    up = [L for L in synth.BLOCK if L.name == "up"][0]
+    down = [L for L in synth.BLOCK if L.name == "down"][0]
+    n, d, m, dout = up.x.n, up.x.d, up.w.rows, down.w.rows
+    log(f"generating x {n}x{d} fp16, W_up {m}x{d}, W_down {dout}x{m}")
+    x = synth.activations(up.x, threads=min(16, len(os.sched_getaffinity(0))))
+    W1, W2 = synth.weights(up.w), synth.weights(down.w)
+    xd, W1d, W2d = (torch.from_numpy(a).to(dev) for a in (x, W1, W2))
+    stream = torch.cuda.current_stream(dev)
+    ev = {}
+
+    def timer(name):
+        @contextlib.contextmanager
+        def cm():
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            yield
+            b.record(stream)
+            ev.setdefault(name, []).append((a, b))
+        return cm()
+
+    for _ in range(args.warmup):
+        out = gq.quantize_relu_block(xd, W1d, W2d)
+        del out
+    torch.cuda.synchronize()
+    ev.clear()
+    log(f"timing {args.steps} steps")
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        out = gq.quantize_relu_block(xd, W1d, W2d, timer=timer)
+        del out
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    ph = {k: float(np.mean([a.elapsed_time(b) for a, b in v])) for k, v in ev.items()}
+    log("phase ms:", {k: round(v, 3) for k, v in ph.items()})
+    w1 = algorithmic_work(m, d, n)
+    w2 = algorithmic_work(dout, m, n)
+    fwd_flops = 2.0 * n * d * m
+    work = w1["syrk"] + w1["prep"] + w1["lazy"] + w1["sweep"] + fwd_flops + \
+        w2["syrk"] + w2["prep"] + w2["lazy"] + w2["sweep"]
+    # roofline of the dominant single kernel: the larger of the forward product
+    # (one launch) and the second H accumulation (one SYRK call)
+    cand = {"forward1": ("linear_int4_kernel (the up projection's forward product)", fwd_flops),
+            "acc2": ("hessian accumulate call at d=%d: syrk_fast_kernel + syrk_reduce_kernel" % m,
+                     w2["syrk"])}
+    dom = max(cand, key=lambda k: ph[k])
+    rf = {}
+    for k, (name, flops) in cand.items():
+        ach = flops / (ph[k] * 1e-3) / 1e12
+        rf[k] = {"bound": "mfma", "kernel": name, "achieved": round(ach, 2),
+                 "peak": FP16_MFMA_TFLOPS, "unit": "TFLOP/s",
+                 "frac": round(ach / FP16_MFMA_TFLOPS, 4), "traffic": None,
+                 "per_launch_ms": round(ph[k], 4), "flops_per_launch": flops}
+    cpu = None
+    if not args.no_cpu:
+        log("cpu baseline (oracle on a bounded sample)")
+        cpu = pipeline_cpu_baseline(x, W1, W2)
+        log("  ", cpu)
+    line = {
+        "metric": "ms per layer-by-layer quantized MLP pair (up 11008x4096 -> ReLU -> down "
+                  "4096x11008, int4 g128; down's H from the quantized up's outputs)",
+        "value": round(ms_step, 4),
+        "unit": "ms",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16-in/f32-acc SYRK and forward product, f64 Hinv, f32 sweep",
+        "data": "synthetic (seeded low-rank-plus-noise activations, Gaussian weights)",
+        "config": {"workload": f"MLP pair: x {n}x{d} fp16 (128x2048 tokens), W_up {m}x{d} fp16, "
+                               f"W_down {dout}x{m} fp16, int4 g128 B128 percdamp 0.01; "
+                               "y1 = fp16(relu(x W_up_hat^T)) recorded for the down projection",
+                   "phase_ms": {k: round(v, 4) for k, v in ph.items()},
+                   "effective_tflops": round(work / (ms_step * 1e-3) / 1e12, 2),
+                   "roofline_other": rf["acc2" if dom == "forward1" else "forward1"]},
+        "roofline": rf[dom],
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -421,6 +579,8 @@ def main():
     ap.add_argument("--tokens", type=int, default=1, help="tokens per decode step (--decode)")
     ap.add_argument("--fused", action="store_true",
                     help="--decode: q|k|v and gate|up stored as one matrix each")
+    ap.add_argument("--pipeline", action="store_true",
+                    help="layer-by-layer quantization of the MLP up -> ReLU -> down pair")
     ap.add_argument("--no-graph", action="store_true",
                     help="--decode: launch the step's products one by one instead of a graph")
     args = ap.parse_args()
@@ -431,6 +591,9 @@ def main():
 
     if args.decode:
         decode_main(args)
+        return
+    if args.pipeline:
+        pipeline_main(args)
         return
 
     import numpy as np

@@ -34,3 +34,4 @@ from ._lib import (  # noqa: F401
     version,
     workspace_bytes,
 )
+from .pipeline import quantize_relu_block  # noqa: F401,E402
