@@ -400,6 +400,20 @@ def decode_main(args):
     print(json.dumps(line), flush=True)
 
 
+def copy_probe(torch, dev, mib):
+    """One plain device copy of known size: the reference the HBM counters
+    (FETCH_SIZE, WRITE_SIZE) are scaled by."""
+    if not mib:
+        return
+    nb = mib << 20
+    src = torch.ones(nb // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"copy probe: {nb} bytes read, {nb} bytes written")
+    del src, dst
+
+
 def pipeline_cpu_baseline(x, W1, W2, budget_s=4.0):
     """The fp64 oracle's layer-by-layer block on a bounded sample, each phase
     timed on a slice and scaled to the full block: H1 and H2 on 4096-token
@@ -474,6 +488,7 @@ def pipeline_main(args):
     import synth
 
     dev = torch.device("cuda:0")
+    copy_probe(torch, dev, args.copy_probe_mib)
     up = [L for L in synth.BLOCK if L.name == "up"][0]
     down = [L for L in synth.BLOCK if L.name == "down"][0]
     n, d, m, dout = up.x.n, up.x.d, up.w.rows, down.w.rows
@@ -603,14 +618,7 @@ def main():
     import synth
 
     dev = torch.device("cuda:0")
-    if args.copy_probe_mib:
-        nb = args.copy_probe_mib << 20
-        src = torch.ones(nb // 4, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        log(f"copy probe: {nb} bytes read, {nb} bytes written")
-        del src, dst
+    copy_probe(torch, dev, args.copy_probe_mib)
 
     if args.layer == "block":
         groups = []

@@ -28,8 +28,8 @@
 //     over a group's 128 columns, lane group k (lanes 16k..16k+15) takes
 //     columns 32k..32k+31, so the words of a lane's four K steps are one
 //     16-byte piece of the packed row.
-//   * XCD-aware order: all output tiles of a token tile go to one XCD, so the
-//     x tile is fetched into that XCD's L2 once.
+//   * XCD-aware order: an XCD works on groups of 4 token tiles x all output
+//     tiles, 4 x 8 tiles at a time, so its L2 serves both operands.
 #include "common.h"
 
 namespace gptq {
@@ -46,6 +46,7 @@ constexpr int STAGE = X_BYTES + B_BYTES + 2 * S_BYTES;  // 50 KB
 constexpr int NWAVE = 8;
 constexpr int LOADS_PER_STAGE = (X_BYTES / 1024 + B_BYTES / 1024) / NWAVE + 1;  // per wave: 7
 constexpr int kXcds = 8;
+constexpr int kGroupM = 4;  // token tiles per XCD-local group
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void;
@@ -70,14 +71,17 @@ __device__ inline void lds_barrier() {
 
 // (q - z) for the 8 codes of one word, in column order, as an MFMA operand.
 // Byte p of the word holds codes 2p (low nibble) and 2p + 1 (high nibble).
-__device__ inline half8 codes_minus_zero(uint32_t w, half2_t mul, half2_t off) {
+__device__ inline half8 codes_minus_zero(uint32_t w, half2_t mul, half2_t off, uint32_t magic) {
   half8 r;
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
     // 0x00bb00bb with byte p of w in both halves (selector 12 gives 0x00)
     const uint32_t b = __builtin_amdgcn_perm(w, w, (12u << 24) | ((uint32_t)p << 16) | (12u << 8) | p);
-    // low half 0x6400 | q_lo = 1024 + q_lo, high half 0x6400 | 16 q_hi = 1024 + 16 q_hi
-    const uint32_t m = (b & 0x00F0000Fu) | 0x64006400u;
+    // low half 0x6400 | q_lo = 1024 + q_lo, high half 0x6400 | 16 q_hi = 1024 + 16 q_hi, in
+    // one v_and_or_b32 (a VOP3 op takes no literal here: the mask goes in an SGPR,
+    // the magic number in a VGPR)
+    uint32_t m;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(m) : "v"(b), "s"(0x00F0000Fu), "v"(magic));
     const half2_t h = __builtin_bit_cast(half2_t, m) * mul + off;  // exact: (q_lo - z, q_hi - z)
     r[2 * p] = h[0];
     r[2 * p + 1] = h[1];
@@ -119,10 +123,11 @@ __device__ inline DmaOffsets dma_offsets(int64_t ldx, int64_t t0, int64_t m, int
 
 // Issue one stage's direct loads (input columns c0..c0+127) into `st`.
 __device__ inline void issue_stage(const char* xb, const char* wbase, const char* szb,
-                                   const DmaOffsets& d, int64_t c0, int g, char* st, int wave) {
+                                   const DmaOffsets& d, int k, int grp, char* st, int wave) {
+  const uint32_t c0 = (uint32_t)k * KG;
   // the column offset goes into the 32-bit lane offset (at most 2^21 more),
   // which keeps each address a scalar base plus one VGPR inside the loop
-  const uint32_t cx = (uint32_t)(c0 * 2), cw = (uint32_t)(c0 / 2), cs = (uint32_t)((c0 / g) * 4);
+  const uint32_t cx = c0 * 2, cw = c0 / 2, cs = (uint32_t)grp * 4;
 #pragma unroll
   for (int u = 0; u < 4; ++u)
     __builtin_amdgcn_global_load_lds((const void*)(xb + (d.x[u] + cx)),
@@ -136,6 +141,19 @@ __device__ inline void issue_stage(const char* xb, const char* wbase, const char
       (const void*)(szb + (d.sz + cs)),
       (lds_void*)(st + X_BYTES + B_BYTES + (wave >> 2) * S_BYTES + 256 * (wave & 3)), 4, 0, 0);
 }
+
+// Position of a stage inside its scale group (groups are gk stages long);
+// kept as running counters so the loop does no division.
+struct GroupCursor {
+  int in = 0;   // stage index inside the group
+  int grp = 0;  // group index
+  __device__ void advance(int gk) {
+    if (++in == gk) {
+      in = 0;
+      ++grp;
+    }
+  }
+};
 
 // One stage of the main loop: wait for stage k (held in `cur`), publish it
 // with a barrier, start the loads of stage k + 2 into `nxt` (the stage read
@@ -153,10 +171,10 @@ struct LaneOffsets {
   int sz;     // scale / zero of b-tile 0 (b-tile b adds 64 b)
 };
 
-__device__ inline void stage_step(int64_t k, int64_t nk, const char* cur, char* nxt,
-                                  const char* xb, const char* wbase, const char* szb,
-                                  const DmaOffsets& dm, int g, int wave, const LaneOffsets& lo,
-                                  f32x4 (&acc)[4][4], f32x4 (&part)[4][4]) {
+__device__ inline void stage_step(int k, int nk, const char* cur, char* nxt, const char* xb,
+                                  const char* wbase, const char* szb, const DmaOffsets& dm,
+                                  int gk, GroupCursor& use, GroupCursor& iss, int wave,
+                                  const LaneOffsets& lo, f32x4 (&acc)[4][4], f32x4 (&part)[4][4]) {
   // stage k has landed for this wave; stage k + 1 may still be in flight
   if (k + 1 < nk) wait_vm<LOADS_PER_STAGE>();
   else wait_vm<0>();
@@ -174,12 +192,22 @@ __device__ inline void stage_step(int64_t k, int64_t nk, const char* cur, char* 
     const float z = *reinterpret_cast<const float*>(reinterpret_cast<const char*>(sz) + lo.sz + 64 * b);
     off[b] = half2_t{(_Float16)(-1024.0f - z), (_Float16)(-64.0f - z)};
   }
-  if (k + 2 < nk) issue_stage(xb, wbase, szb, dm, (k + 2) * KG, g, nxt, wave);
+  // a lane's four words of the stage, one 16-byte read per b-tile (the word
+  // swizzle keeps these reads free of bank conflicts; 4-byte reads of the
+  // same layout would not be)
+  uint4 wb[4];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) wb[b] = *reinterpret_cast<const uint4*>(sb + lo.w + 1024 * b);
+  if (k + 2 < nk) {
+    issue_stage(xb, wbase, szb, dm, k + 2, iss.grp, nxt, wave);
+    iss.advance(gk);
+  }
 
-  const int64_t c0 = k * KG;
-  const bool gstart = (c0 % g) == 0;
-  const bool gend = ((c0 + KG) % g) == 0 || k + 1 == nk;
+  const bool gstart = use.in == 0;
+  const bool gend = use.in == gk - 1 || k + 1 == nk;
+  use.advance(gk);
   const half2_t mul = {(_Float16)1.0f, (_Float16)0.0625f};
+  const uint32_t magic = 0x64006400u;
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
     half8 af[4];
@@ -189,8 +217,8 @@ __device__ inline void stage_step(int64_t k, int64_t nk, const char* cur, char* 
     half8 bf[4];
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
-      const uint32_t w = *reinterpret_cast<const uint32_t*>(sb + lo.w + 1024 * b + 4 * s);
-      bf[b] = codes_minus_zero(w, mul, off[b]);
+      const uint32_t w = s == 0 ? wb[b].x : s == 1 ? wb[b].y : s == 2 ? wb[b].z : wb[b].w;
+      bf[b] = codes_minus_zero(w, mul, off[b], magic);
     }
     if (s == 0 && gstart) {
 #pragma unroll
@@ -223,18 +251,22 @@ template <bool RELU>
 __global__ __launch_bounds__(512, 1) void linear_int4_kernel(
     const _Float16* __restrict__ x, int64_t ldx, int64_t m, const uint32_t* __restrict__ packed,
     int64_t nw, int64_t rows, int64_t cols, const float* __restrict__ scales,
-    const float* __restrict__ zeros, int64_t ngroups, int g, int64_t ntn, int64_t ntm,
+    const float* __restrict__ zeros, int64_t ngroups, int gk, int64_t ntn, int64_t ntm,
     _Float16* __restrict__ y, int64_t ldy) {
   __shared__ __attribute__((aligned(1024))) char st0[STAGE];
   __shared__ __attribute__((aligned(1024))) char st1[STAGE];
   __shared__ __attribute__((aligned(1024))) char st2[STAGE];
 
-  // XCD-aware tile: workgroup b runs on XCD b % 8; its local index walks the
-  // output tiles of token tiles xcd, xcd + 8, ...
+  // XCD-aware tile order.  Workgroup b runs on XCD b % 8, which takes token
+  // tiles xcd, xcd + 8, ...; its local index walks them in groups of kGroupM
+  // token tiles, and within a group output tile by output tile, so the ~32
+  // workgroups an XCD runs at once share 4 x tiles and 8 weight tiles in its
+  // L2 (32 KB and 16 KB per stage: the split that minimises its misses).
   const int64_t bid = blockIdx.x;
   const int64_t xcd = bid % kXcds, local = bid / kXcds;
-  const int64_t tm = (local / ntn) * kXcds + xcd;
-  const int64_t tn = local % ntn;
+  const int64_t grp = local / (kGroupM * ntn), idx = local % (kGroupM * ntn);
+  const int64_t tm = (grp * kGroupM + idx % kGroupM) * kXcds + xcd;
+  const int64_t tn = idx / kGroupM;
   if (tm >= ntm) return;
   const int64_t t0 = tm * TM, n0 = tn * TN;
 
@@ -243,7 +275,7 @@ __global__ __launch_bounds__(512, 1) void linear_int4_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar bases
   const int wm = wave >> 2, wn = wave & 3;
   const int li = lane & 15, kg = lane >> 4;
-  const int64_t nk = cols / KG;
+  const int nk = (int)(cols / KG);
   LaneOffsets lo;
 #pragma unroll
   for (int s = 0; s < 4; ++s) lo.x[s] = 256 * (64 * wm + li) + 16 * x_piece(li, 4 * kg + s);
@@ -261,12 +293,19 @@ __global__ __launch_bounds__(512, 1) void linear_int4_kernel(
   const char* wbase = reinterpret_cast<const char*>(packed + n0 * nw);
   const char* szb = reinterpret_cast<const char*>((wave < 4 ? scales : zeros) + n0 * ngroups);
 
-  issue_stage(xb, wbase, szb, dm, 0, g, st0, wave);
-  if (nk > 1) issue_stage(xb, wbase, szb, dm, KG, g, st1, wave);
-  for (int64_t k = 0; k < nk; k += NSTAGE) {
-    stage_step(k, nk, st0, st2, xb, wbase, szb, dm, g, wave, lo, acc, part);
-    if (k + 1 < nk) stage_step(k + 1, nk, st1, st0, xb, wbase, szb, dm, g, wave, lo, acc, part);
-    if (k + 2 < nk) stage_step(k + 2, nk, st2, st1, xb, wbase, szb, dm, g, wave, lo, acc, part);
+  GroupCursor use, iss;
+  issue_stage(xb, wbase, szb, dm, 0, iss.grp, st0, wave);
+  iss.advance(gk);
+  if (nk > 1) {
+    issue_stage(xb, wbase, szb, dm, 1, iss.grp, st1, wave);
+    iss.advance(gk);
+  }
+  for (int k = 0; k < nk; k += NSTAGE) {
+    stage_step(k, nk, st0, st2, xb, wbase, szb, dm, gk, use, iss, wave, lo, acc, part);
+    if (k + 1 < nk)
+      stage_step(k + 1, nk, st1, st0, xb, wbase, szb, dm, gk, use, iss, wave, lo, acc, part);
+    if (k + 2 < nk)
+      stage_step(k + 2, nk, st2, st1, xb, wbase, szb, dm, gk, use, iss, wave, lo, acc, part);
   }
 
   // lane holds rows 4 * kg + i of each 16 x 16 tile, column li
@@ -303,15 +342,17 @@ hipError_t launch_linear_int4(const _Float16* x, int64_t ldx, int64_t m, const u
                               int groupsize, bool relu, _Float16* y, int64_t ldy, hipStream_t s) {
   const int g = groupsize >= cols ? (int)cols : groupsize;
   const int64_t ngroups = ceil_div(cols, g);
+  const int gk = (int)ceil_div(g, KG);  // stages per group (a short last group ends at cols)
   const int64_t nw = cols / 8;
   const int64_t ntm = ceil_div(m, TM), ntn = ceil_div(rows, TN);
-  const int64_t blocks = round_up(ntm, kXcds) * ntn;
+  // every XCD gets the same whole number of kGroupM-token-tile groups
+  const int64_t blocks = kXcds * round_up(ceil_div(ntm, kXcds), kGroupM) * ntn;
   if (relu)
     hipLaunchKernelGGL(linear_int4_kernel<true>, dim3((unsigned)blocks), dim3(512), 0, s, x, ldx, m,
-                       packed, nw, rows, cols, scales, zeros, ngroups, g, ntn, ntm, y, ldy);
+                       packed, nw, rows, cols, scales, zeros, ngroups, gk, ntn, ntm, y, ldy);
   else
     hipLaunchKernelGGL(linear_int4_kernel<false>, dim3((unsigned)blocks), dim3(512), 0, s, x, ldx,
-                       m, packed, nw, rows, cols, scales, zeros, ngroups, g, ntn, ntm, y, ldy);
+                       m, packed, nw, rows, cols, scales, zeros, ngroups, gk, ntn, ntm, y, ldy);
   return hipGetLastError();
 }
 
