@@ -41,6 +41,8 @@ FP64_MFMA_TFLOPS = 78.6
 
 SYRK_SOURCE = os.path.join(ROOT, "post_weight_quantization_02_amd", "csrc", "syrk_f16.hip")
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "hessian_accumulate_attn_traffic.md")
+LINEAR_SOURCE = os.path.join(ROOT, "post_weight_quantization_02_amd", "csrc", "linear_mfma.hip")
+LINEAR_TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "mlp_pair_pipeline_kernels.md")
 
 
 def log(*a):
@@ -64,17 +66,19 @@ def source_digest(path):
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def recorded_traffic():
-    """HBM bytes per accumulate call from the committed counter summary, or
-    None when there is none or the SYRK source has changed since it was
-    taken."""
+def recorded_traffic(summary=None, source=None, key="syrk_source_sha256_16"):
+    """HBM bytes per call of a kernel from its committed counter summary, or
+    None when there is none or the kernel's source has changed since the
+    counters were taken (default: the accumulate call's SYRK)."""
+    summary = summary or TRAFFIC_SUMMARY
+    source = source or SYRK_SOURCE
     try:
-        text = open(TRAFFIC_SUMMARY).read()
+        text = open(summary).read()
     except OSError:
         return None
     m_b = re.search(r"^traffic_bytes_per_call:\s*([0-9.eE+]+)\s*$", text, re.M)
-    m_h = re.search(r"^syrk_source_sha256_16:\s*([0-9a-f]+)\s*$", text, re.M)
-    if not (m_b and m_h) or m_h.group(1) != source_digest(SYRK_SOURCE):
+    m_h = re.search(r"^" + key + r":\s*([0-9a-f]+)\s*$", text, re.M)
+    if not (m_b and m_h) or m_h.group(1) != source_digest(source):
         return None
     return float(m_b.group(1))
 
@@ -538,9 +542,12 @@ def pipeline_main(args):
     rf = {}
     for k, (name, flops) in cand.items():
         ach = flops / (ph[k] * 1e-3) / 1e12
+        tr = None
+        if k == "forward1":
+            tr = recorded_traffic(LINEAR_TRAFFIC_SUMMARY, LINEAR_SOURCE, "linear_source_sha256_16")
         rf[k] = {"bound": "mfma", "kernel": name, "achieved": round(ach, 2),
                  "peak": FP16_MFMA_TFLOPS, "unit": "TFLOP/s",
-                 "frac": round(ach / FP16_MFMA_TFLOPS, 4), "traffic": None,
+                 "frac": round(ach / FP16_MFMA_TFLOPS, 4), "traffic": tr,
                  "per_launch_ms": round(ph[k], 4), "flops_per_launch": flops}
     cpu = None
     if not args.no_cpu:
