@@ -10,9 +10,9 @@
 //
 // gfx950 design (a dense contraction, so MFMA):
 //   * 128 tokens x 256 outputs per workgroup, eight waves (two per SIMD) of
-//     64 x 64, each as 4 x 4 tiles of v_mfma_f32_16x16x32_f16: a lane holds
+//     128 x 32, each as 8 x 2 tiles of v_mfma_f32_16x16x32_f16: a lane holds
 //     64 running sums and 64 group partials, so two waves fit one SIMD's
-//     registers.
+//     registers, and no two waves convert the same packed words.
 //   * Per 128 input columns one ring stage (3 stages, 50 KB each) receives,
 //     by direct global->LDS loads, the 128 x 128 fp16 tile of x, the 256 x 64
 //     bytes of packed words and the 256 scales and zeros of the group.  Every
@@ -44,6 +44,13 @@ constexpr int B_BYTES = TN * (KG / 2);      // 16 KB (4-bit codes)
 constexpr int S_BYTES = TN * 4;             // 1 KB
 constexpr int STAGE = X_BYTES + B_BYTES + 2 * S_BYTES;  // 50 KB
 constexpr int NWAVE = 8;
+// Wave layout: WAVES_M x WAVES_N waves, each WTM tokens x WTN outputs as AT x BT
+// MFMA tiles.  1 x 8: each wave owns distinct outputs, so every packed word is
+// turned into fp16 operands once per workgroup (2 x 4 would do it twice),
+// at the price of twice the x fragment reads from LDS.
+constexpr int WAVES_M = 1, WAVES_N = NWAVE / WAVES_M;
+constexpr int WTM = TM / WAVES_M, WTN = TN / WAVES_N;
+constexpr int AT = WTM / 16, BT = WTN / 16;
 constexpr int LOADS_PER_STAGE = (X_BYTES / 1024 + B_BYTES / 1024) / NWAVE + 1;  // per wave: 7
 constexpr int kXcds = 8;
 constexpr int kGroupM = 4;  // token tiles per XCD-local group
@@ -161,8 +168,8 @@ struct GroupCursor {
 // The stages are three distinct LDS arrays named at compile time, so the
 // compiler can tell that reading `cur` does not touch the direct loads still
 // landing in the other two and adds no wait for them.
-// Per-lane LDS byte offsets inside a stage.  With row = 64 wm + 16 a + li the
-// x swizzle (p ^ (row & 15)) depends on li only, and with row = 64 wn + 16 b
+// Per-lane LDS byte offsets inside a stage.  With row = WTM wm + 16 a + li the
+// x swizzle (p ^ (row & 15)) depends on li only, and with row = WTN wn + 16 b
 // + li so does the word swizzle, so every read is one of these offsets plus
 // a compile-time constant.
 struct LaneOffsets {
@@ -174,7 +181,7 @@ struct LaneOffsets {
 __device__ inline void stage_step(int k, int nk, const char* cur, char* nxt, const char* xb,
                                   const char* wbase, const char* szb, const DmaOffsets& dm,
                                   int gk, GroupCursor& use, GroupCursor& iss, int wave,
-                                  const LaneOffsets& lo, f32x4 (&acc)[4][4], f32x4 (&part)[4][4]) {
+                                  const LaneOffsets& lo, f32x4 (&acc)[AT][BT], f32x4 (&part)[AT][BT]) {
   // stage k has landed for this wave; stage k + 1 may still be in flight
   if (k + 1 < nk) wait_vm<LOADS_PER_STAGE>();
   else wait_vm<0>();
@@ -186,18 +193,18 @@ __device__ inline void stage_step(int k, int nk, const char* cur, char* nxt, con
   // the compiler cannot rule out that this read overlaps loads still in
   // flight (after the loop's back edge) it waits for them, and at this point
   // that is only stage k + 1, issued a whole stage earlier.
-  half2_t off[4];
+  half2_t off[BT];
 #pragma unroll
-  for (int b = 0; b < 4; ++b) {
+  for (int b = 0; b < BT; ++b) {
     const float z = *reinterpret_cast<const float*>(reinterpret_cast<const char*>(sz) + lo.sz + 64 * b);
     off[b] = half2_t{(_Float16)(-1024.0f - z), (_Float16)(-64.0f - z)};
   }
   // a lane's four words of the stage, one 16-byte read per b-tile (the word
   // swizzle keeps these reads free of bank conflicts; 4-byte reads of the
   // same layout would not be)
-  uint4 wb[4];
+  uint4 wb[BT];
 #pragma unroll
-  for (int b = 0; b < 4; ++b) wb[b] = *reinterpret_cast<const uint4*>(sb + lo.w + 1024 * b);
+  for (int b = 0; b < BT; ++b) wb[b] = *reinterpret_cast<const uint4*>(sb + lo.w + 1024 * b);
   if (k + 2 < nk) {
     issue_stage(xb, wbase, szb, dm, k + 2, iss.grp, nxt, wave);
     iss.advance(gk);
@@ -210,37 +217,37 @@ __device__ inline void stage_step(int k, int nk, const char* cur, char* nxt, con
   const uint32_t magic = 0x64006400u;
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
-    half8 af[4];
+    half8 af[AT];
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+    for (int a = 0; a < AT; ++a)
       af[a] = *reinterpret_cast<const half8*>(cur + lo.x[s] + 4096 * a);
-    half8 bf[4];
+    half8 bf[BT];
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
+    for (int b = 0; b < BT; ++b) {
       const uint32_t w = s == 0 ? wb[b].x : s == 1 ? wb[b].y : s == 2 ? wb[b].z : wb[b].w;
       bf[b] = codes_minus_zero(w, mul, off[b], magic);
     }
     if (s == 0 && gstart) {
 #pragma unroll
-      for (int a = 0; a < 4; ++a)
+      for (int a = 0; a < AT; ++a)
 #pragma unroll
-        for (int b = 0; b < 4; ++b)
+        for (int b = 0; b < BT; ++b)
           part[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[a], bf[b],
                                                               f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
     } else {
 #pragma unroll
-      for (int a = 0; a < 4; ++a)
+      for (int a = 0; a < AT; ++a)
 #pragma unroll
-        for (int b = 0; b < 4; ++b)
+        for (int b = 0; b < BT; ++b)
           part[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[a], bf[b], part[a][b], 0, 0, 0);
     }
   }
   if (gend) {
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
+    for (int b = 0; b < BT; ++b) {
       const float sc = *reinterpret_cast<const float*>(reinterpret_cast<const char*>(ss) + lo.sz + 64 * b);
 #pragma unroll
-      for (int a = 0; a < 4; ++a)
+      for (int a = 0; a < AT; ++a)
 #pragma unroll
         for (int i = 0; i < 4; ++i) acc[a][b][i] = __builtin_fmaf(sc, part[a][b][i], acc[a][b][i]);
     }
@@ -273,20 +280,20 @@ __global__ __launch_bounds__(512, 1) void linear_int4_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar bases
-  const int wm = wave >> 2, wn = wave & 3;
+  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
   const int li = lane & 15, kg = lane >> 4;
   const int nk = (int)(cols / KG);
   LaneOffsets lo;
 #pragma unroll
-  for (int s = 0; s < 4; ++s) lo.x[s] = 256 * (64 * wm + li) + 16 * x_piece(li, 4 * kg + s);
-  lo.w = 64 * (64 * wn + li) + 16 * b_piece(li, kg);
-  lo.sz = 4 * (64 * wn + li);
+  for (int s = 0; s < 4; ++s) lo.x[s] = 256 * (WTM * wm + li) + 16 * x_piece(li, 4 * kg + s);
+  lo.w = 64 * (WTN * wn + li) + 16 * b_piece(li, kg);
+  lo.sz = 4 * (WTN * wn + li);
 
-  f32x4 acc[4][4], part[4][4];
+  f32x4 acc[AT][BT], part[AT][BT];
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+  for (int a = 0; a < AT; ++a)
 #pragma unroll
-    for (int b = 0; b < 4; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int b = 0; b < BT; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const DmaOffsets dm = dma_offsets(ldx, t0, m, nw, ngroups, n0, rows, wave, lane);
   const char* xb = reinterpret_cast<const char*>(x + t0 * ldx);
@@ -310,14 +317,14 @@ __global__ __launch_bounds__(512, 1) void linear_int4_kernel(
 
   // lane holds rows 4 * kg + i of each 16 x 16 tile, column li
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+  for (int a = 0; a < AT; ++a)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int64_t t = t0 + 64 * wm + 16 * a + 4 * kg + i;
+      const int64_t t = t0 + WTM * wm + 16 * a + 4 * kg + i;
       if (t >= m) continue;
 #pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const int64_t r = n0 + 64 * wn + 16 * b + li;
+      for (int b = 0; b < BT; ++b) {
+        const int64_t r = n0 + WTN * wn + 16 * b + li;
         if (r >= rows) continue;
         float v = acc[a][b][i];
         if (RELU) v = v > 0.f ? v : 0.f;
