@@ -335,7 +335,8 @@ gptq_status gptq_dequant_gemm(const void* x, int64_t m, int64_t cols, int64_t ld
  *   zeros      (groupsize >= cols: one group); zeros must be integers in
  *              [0, 15], as the quantizer writes them.
  *   groupsize  a multiple of 128, or >= cols.  cols must be a multiple of
- *              128.  Other shapes and bit widths: GPTQ_ERR_UNSUPPORTED.
+ *              128, and about m * rows / 64 < 2^32 (the launch grid).  Other
+ *              shapes and bit widths: GPTQ_ERR_UNSUPPORTED.
  *   relu       0: y = x W_hat^T; 1: y = max(x W_hat^T, 0).
  *   y          m x rows fp16 out, row t at y + t*ldy (ldy >= rows).
  *   Arithmetic: the products x * (code - zero) are exact in fp32, each

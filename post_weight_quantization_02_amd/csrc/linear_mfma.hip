@@ -335,13 +335,22 @@ __global__ __launch_bounds__(512, 1) void linear_int4_kernel(
 
 }  // namespace
 
-bool linear_int4_supported(int64_t cols, int groupsize, const void* x, int64_t ldx,
-                           const void* packed) {
-  // ldx < 2^23: a token tile's lane offsets (< 128 rows of 2 ldx bytes) fit 32 bits
+namespace {
+int64_t linear_blocks(int64_t m, int64_t rows) {
+  // every XCD gets the same whole number of kGroupM-token-tile groups
+  return kXcds * round_up(ceil_div(ceil_div(m, TM), kXcds), kGroupM) * ceil_div(rows, TN);
+}
+}  // namespace
+
+bool linear_int4_supported(int64_t m, int64_t rows, int64_t cols, int groupsize, const void* x,
+                           int64_t ldx, const void* packed) {
+  // ldx < 2^23: a token tile's lane offsets (< 128 rows of 2 ldx bytes) fit 32 bits;
+  // the grid's work-items must fit 32 bits
   return cols % KG == 0 && (groupsize % KG == 0 || groupsize >= cols) && ldx % 8 == 0 &&
          ldx < ((int64_t)1 << 23) &&
          (reinterpret_cast<uintptr_t>(x) & 15) == 0 &&
-         (reinterpret_cast<uintptr_t>(packed) & 15) == 0;
+         (reinterpret_cast<uintptr_t>(packed) & 15) == 0 &&
+         linear_blocks(m, rows) * 64 * NWAVE <= (int64_t)UINT32_MAX;
 }
 
 hipError_t launch_linear_int4(const _Float16* x, int64_t ldx, int64_t m, const uint32_t* packed,
@@ -352,8 +361,7 @@ hipError_t launch_linear_int4(const _Float16* x, int64_t ldx, int64_t m, const u
   const int gk = (int)ceil_div(g, KG);  // stages per group (a short last group ends at cols)
   const int64_t nw = cols / 8;
   const int64_t ntm = ceil_div(m, TM), ntn = ceil_div(rows, TN);
-  // every XCD gets the same whole number of kGroupM-token-tile groups
-  const int64_t blocks = kXcds * round_up(ceil_div(ntm, kXcds), kGroupM) * ntn;
+  const int64_t blocks = linear_blocks(m, rows);
   if (relu)
     hipLaunchKernelGGL(linear_int4_kernel<true>, dim3((unsigned)blocks), dim3(512), 0, s, x, ldx, m,
                        packed, nw, rows, cols, scales, zeros, ngroups, gk, ntn, ntm, y, ldy);

@@ -13,6 +13,8 @@ intermediate buffers.
 """
 from __future__ import annotations
 
+import contextlib
+
 from . import _lib
 
 
@@ -33,10 +35,7 @@ def quantize_relu_block(x, W1, W2, bits: int = 4, groupsize: int = 128, blocksiz
         raise ValueError("shapes: x n x d, W1 m x d, W2 d_out x m")
 
     def phase(name):
-        if timer is None:
-            import contextlib
-            return contextlib.nullcontext()
-        return timer(name)
+        return contextlib.nullcontext() if timer is None else timer(name)
 
     out = {}
     with phase("acc1"):

@@ -221,5 +221,6 @@ def test_linear_forward_validation():
     assert lf(ldx=260) == U                                 # rows not 16-byte aligned
     assert lf(x=FAKE + 8) == U and lf(packed=FAKE + 4) == U
     assert lf(ldx=1 << 23, cols=256) == U                   # lane offsets would pass 32 bits
+    assert lf(m=1 << 20, rows=1 << 20, ldy=1 << 20) == U    # launch grid would pass 2^32 items
     # m = 0 is a no-op: nothing is read, so null x and y are accepted
     assert lf(m=0, x=None, y=None, ldx=0) == gq.GPTQ_OK
