@@ -178,10 +178,22 @@ struct LaneOffsets {
   int sz;     // scale / zero of b-tile 0 (b-tile b adds 64 b)
 };
 
+// acc += scale * partial for every output of the lane (the group's last stage)
+__device__ inline void fold_group(f32x4 (&acc)[AT][BT], const f32x4 (&part)[AT][BT],
+                                  const float (&fsc)[BT]) {
+#pragma unroll
+  for (int b = 0; b < BT; ++b)
+#pragma unroll
+    for (int a = 0; a < AT; ++a)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[a][b][i] = __builtin_fmaf(fsc[b], part[a][b][i], acc[a][b][i]);
+}
+
 __device__ inline void stage_step(int k, int nk, const char* cur, char* nxt, const char* xb,
                                   const char* wbase, const char* szb, const DmaOffsets& dm,
                                   int gk, GroupCursor& use, GroupCursor& iss, int wave,
-                                  const LaneOffsets& lo, f32x4 (&acc)[AT][BT], f32x4 (&part)[AT][BT]) {
+                                  const LaneOffsets& lo, f32x4 (&acc)[AT][BT], f32x4 (&part)[AT][BT],
+                                  bool& fold, float (&fsc)[BT]) {
   // stage k has landed for this wave; stage k + 1 may still be in flight
   if (k + 1 < nk) wait_vm<LOADS_PER_STAGE>();
   else wait_vm<0>();
@@ -208,6 +220,13 @@ __device__ inline void stage_step(int k, int nk, const char* cur, char* nxt, con
   if (k + 2 < nk) {
     issue_stage(xb, wbase, szb, dm, k + 2, iss.grp, nxt, wave);
     iss.advance(gk);
+  }
+  // The previous group's partial sums enter the running sums here, after the
+  // barrier, where these FMAs fill the wait for this stage's first LDS reads
+  // instead of delaying the barrier.
+  if (fold) {
+    fold_group(acc, part, fsc);
+    fold = false;
   }
 
   const bool gstart = use.in == 0;
@@ -242,15 +261,11 @@ __device__ inline void stage_step(int k, int nk, const char* cur, char* nxt, con
           part[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[a], bf[b], part[a][b], 0, 0, 0);
     }
   }
-  if (gend) {
+  if (gend) {  // the group's scales now; its fold at the next stage (or after the loop)
 #pragma unroll
-    for (int b = 0; b < BT; ++b) {
-      const float sc = *reinterpret_cast<const float*>(reinterpret_cast<const char*>(ss) + lo.sz + 64 * b);
-#pragma unroll
-      for (int a = 0; a < AT; ++a)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[a][b][i] = __builtin_fmaf(sc, part[a][b][i], acc[a][b][i]);
-    }
+    for (int b = 0; b < BT; ++b)
+      fsc[b] = *reinterpret_cast<const float*>(reinterpret_cast<const char*>(ss) + lo.sz + 64 * b);
+    fold = true;
   }
 }
 
@@ -307,13 +322,18 @@ __global__ __launch_bounds__(512, 1) void linear_int4_kernel(
     issue_stage(xb, wbase, szb, dm, 1, iss.grp, st1, wave);
     iss.advance(gk);
   }
+  bool fold = false;
+  float fsc[BT];
   for (int k = 0; k < nk; k += NSTAGE) {
-    stage_step(k, nk, st0, st2, xb, wbase, szb, dm, gk, use, iss, wave, lo, acc, part);
+    stage_step(k, nk, st0, st2, xb, wbase, szb, dm, gk, use, iss, wave, lo, acc, part, fold, fsc);
     if (k + 1 < nk)
-      stage_step(k + 1, nk, st1, st0, xb, wbase, szb, dm, gk, use, iss, wave, lo, acc, part);
+      stage_step(k + 1, nk, st1, st0, xb, wbase, szb, dm, gk, use, iss, wave, lo, acc, part, fold,
+                 fsc);
     if (k + 2 < nk)
-      stage_step(k + 2, nk, st2, st1, xb, wbase, szb, dm, gk, use, iss, wave, lo, acc, part);
+      stage_step(k + 2, nk, st2, st1, xb, wbase, szb, dm, gk, use, iss, wave, lo, acc, part, fold,
+                 fsc);
   }
+  fold_group(acc, part, fsc);  // the last stage always ends a group
 
   // lane holds rows 4 * kg + i of each 16 x 16 tile, column li
 #pragma unroll
