@@ -54,33 +54,39 @@ def _layer_check(W, got, ref, H, g=128):
     return rep
 
 
-@pytest.mark.parametrize("n,d,m,dout", [(4096, 256, 512, 256), (16384, 1024, 2048, 1024)])
-def test_relu_block_matches_oracle(env, n, d, m, dout):
+@pytest.mark.parametrize("n,d,m,dout,g", [
+    (4096, 256, 512, 256, 128),
+    (16384, 1024, 2048, 1024, 128),
+    (4096, 384, 640, 256, 0),        # per-channel scales in both layers
+    (4096, 512, 768, 384, 256),      # groups of 256: one fold per two stages
+])
+def test_relu_block_matches_oracle(env, n, d, m, dout, g):
     torch, gq = env
     x, W1, W2 = _inputs(n, d, m, dout)
     out = gq.quantize_relu_block(torch.from_numpy(x).cuda(), torch.from_numpy(W1).cuda(),
-                                 torch.from_numpy(W2).cuda())
+                                 torch.from_numpy(W2).cuda(), groupsize=g)
     torch.cuda.synchronize()
     got = {k: {a: (b.cpu().numpy() if hasattr(b, "cpu") else b) for a, b in v.items()}
            for k, v in out.items() if k != "y1"}
     y1 = out["y1"].cpu().numpy()
-    ref = oracle.two_layer_block(x, W1, W2, 4, 128, 128, 0.01, "f32", tie_distance=True)
+    ref = oracle.two_layer_block(x, W1, W2, 4, g, 128, 0.01, "f32", tie_distance=True)
+    g1 = d if g <= 0 else g  # the first layer's group width
 
     assert h_rel_error(got["first"]["H"], ref["first"]["H"]) <= 1e-4
-    r1 = _layer_check(W1, got["first"], ref["first"], ref["first"]["H"])
+    r1 = _layer_check(W1, got["first"], ref["first"], ref["first"]["H"], g)
 
     # recorded inputs of the second layer, on channels whose first-layer codes agree
     c1, s1, z1 = got["first"]["codes"], got["first"]["scales"], got["first"]["zeros"]
     same_rows = np.all(c1 == ref["first"]["codes"], axis=1)
     assert same_rows.mean() >= 0.99, same_rows.mean()
-    gi = np.arange(d) // 128
+    gi = np.arange(d) // g1
     rs = ref["first"]["scales"]
     rel_s = np.max(np.abs(s1[same_rows].astype(np.float64) - rs[same_rows]) / rs[same_rows])
     assert rel_s <= 1e-5
     mag = np.abs(ref["first"]["codes"] - ref["first"]["zeros"][:, gi]) * rs[:, gi]
-    pre = oracle.quantized_layer_output(x, ref["first"]["codes"], rs, ref["first"]["zeros"], 128)
+    pre = oracle.quantized_layer_output(x, ref["first"]["codes"], rs, ref["first"]["zeros"], g1)
     S = np.abs(x.astype(np.float64)) @ mag.T
-    B = (128 + d // 128 + 2) * 2.0 ** -24 * S + rel_s * S
+    B = (g1 + -(-d // g1) + 2) * 2.0 ** -24 * S + rel_s * S
     tol = B + ulp16(np.abs(pre) + B)
     err = np.abs(y1.astype(np.float64) - ref["y1"].astype(np.float64))
     sel = err[:, same_rows] <= tol[:, same_rows]
@@ -90,7 +96,7 @@ def test_relu_block_matches_oracle(env, n, d, m, dout):
     H2g, H2o = got["second"]["H"], ref["second"]["H"]
     if same_rows.all():
         assert h_rel_error(H2g, H2o) <= 1e-4
-        r2 = _layer_check(W2, got["second"], ref["second"], H2o)
+        r2 = _layer_check(W2, got["second"], ref["second"], H2o, g)
     else:
         # A channel whose first-layer codes took a legitimate near-tie flip
         # records different (equally valid) inputs, so H2 differs in its row
@@ -99,9 +105,9 @@ def test_relu_block_matches_oracle(env, n, d, m, dout):
         k = np.nonzero(same_rows)[0]
         assert h_rel_error(H2g[np.ix_(k, k)], H2o[np.ix_(k, k)]) <= 1e-4
         g2 = got["second"]
-        Wg = dequant(g2["codes"], g2["scales"], g2["zeros"], 128)
+        Wg = dequant(g2["codes"], g2["scales"], g2["zeros"], g)
         Wo = oracle.dequantize(ref["second"]["codes"], ref["second"]["scales"],
-                               ref["second"]["zeros"], 128)
+                               ref["second"]["zeros"], g)
         e_gpu, e_ref = output_error(W2, Wg, H2o), oracle.output_error(W2, Wo, H2o)
         assert abs(e_gpu - e_ref) <= 0.01 * e_ref, (e_gpu, e_ref)
         r2 = dict(e_gpu=e_gpu, e_ref=e_ref, h2_rel=h_rel_error(H2g, H2o),
