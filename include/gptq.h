@@ -329,14 +329,15 @@ gptq_status gptq_dequant_gemm(const void* x, int64_t m, int64_t cols, int64_t ld
  *   x          m x cols fp16, row t at x + t*ldx (ldx >= cols, ldx % 8 == 0,
  *              ldx < 2^23, x 16-byte aligned); m >= 0 (0 is a no-op, and x
  *              and y may then be NULL).
- *   packed     rows x gptq_packed_words(cols, 4) uint32 from gptq_pack_codes
- *              with bits = 4, 16-byte aligned.
+ *   packed     rows x gptq_packed_words(cols, bits) uint32 from
+ *              gptq_pack_codes, bits = 4 or 8, 16-byte aligned.
  *   scales,    rows x ceil(cols / groupsize) fp32, the quantizer's outputs
  *   zeros      (groupsize >= cols: one group); zeros must be integers in
- *              [0, 15], as the quantizer writes them.
+ *              [0, 2^bits - 1], as the quantizer writes them.
  *   groupsize  a multiple of 128, or >= cols.  cols must be a multiple of
- *              128, and about m * rows / 64 < 2^32 (the launch grid).  Other
- *              shapes and bit widths: GPTQ_ERR_UNSUPPORTED.
+ *              128, and the launch grid, about m * rows * bits / 256
+ *              work-items, must stay below 2^32.  Other shapes and bit
+ *              widths: GPTQ_ERR_UNSUPPORTED.
  *   relu       0: y = x W_hat^T; 1: y = max(x W_hat^T, 0).
  *   y          m x rows fp16 out, row t at y + t*ldy (ldy >= rows).
  *   Arithmetic: the products x * (code - zero) are exact in fp32, each

@@ -357,8 +357,8 @@ def dequant_gemm(x, packed, bits: int, cols: int, scales, zeros, groupsize: int,
 def linear_forward(x, packed, bits: int, cols: int, scales, zeros, groupsize: int,
                    relu: bool = False, out=None, stream=None):
     """y = x W_hat^T, or max(x W_hat^T, 0) with relu, as m x rows fp16, for
-    fp16 x (m x cols) and the 4-bit packed codes with their scales and zeros
-    (gptq_linear_forward: the product for many tokens on MFMA)."""
+    fp16 x (m x cols) and the 4- or 8-bit packed codes with their scales and
+    zeros (gptq_linear_forward: the product for many tokens on MFMA)."""
     torch = _torch()
     if x.dtype != torch.float16 or not x.is_cuda or x.dim() != 2 or x.stride(1) != 1 or \
             x.shape[1] != cols:

@@ -93,12 +93,13 @@ hipError_t launch_dequant_gemv(const _Float16* x, int64_t ldx, int64_t m, const 
                                int bits, int64_t rows, int64_t cols, const float* scales,
                                const float* zeros, int groupsize, const int* g_idx, float* y,
                                int64_t ldy, hipStream_t s);
-// the forward product of a 4-bit layer for many tokens (MFMA), fp16 out
-bool linear_int4_supported(int64_t m, int64_t rows, int64_t cols, int groupsize, const void* x,
-                           int64_t ldx, const void* packed);
-hipError_t launch_linear_int4(const _Float16* x, int64_t ldx, int64_t m, const uint32_t* packed,
-                              int64_t rows, int64_t cols, const float* scales, const float* zeros,
-                              int groupsize, bool relu, _Float16* y, int64_t ldy, hipStream_t s);
+// the forward product of a 4- or 8-bit layer for many tokens (MFMA), fp16 out
+bool linear_forward_supported(int bits, int64_t m, int64_t rows, int64_t cols, int groupsize,
+                              const void* x, int64_t ldx, const void* packed);
+hipError_t launch_linear_forward(int bits, const _Float16* x, int64_t ldx, int64_t m,
+                                 const uint32_t* packed, int64_t rows, int64_t cols,
+                                 const float* scales, const float* zeros, int groupsize, bool relu,
+                                 _Float16* y, int64_t ldy, hipStream_t s);
 constexpr int kSweepRows = 16;  // rows per sweep workgroup
 constexpr int kBlock = 128;     // columns per block
 constexpr int kSuperBlock = 512;  // columns per superblock of the two-level lazy update

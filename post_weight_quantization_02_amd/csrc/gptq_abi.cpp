@@ -396,12 +396,12 @@ gptq_status gptq_linear_forward(const void* x, int64_t m, int64_t cols, int64_t 
   if (!aligned(x, 2) || !aligned(packed, 4) || !aligned(scales, 4) || !aligned(zeros, 4) ||
       !aligned(y, 2))
     return GPTQ_ERR_INVALID_ARG;
-  if (bits != 4 || !linear_int4_supported(m, rows, cols, groupsize, x, m > 0 ? ldx : 8, packed))
+  if (!linear_forward_supported(bits, m, rows, cols, groupsize, x, m > 0 ? ldx : 8, packed))
     return GPTQ_ERR_UNSUPPORTED;
   if (m == 0) return GPTQ_OK;
-  if (launch_linear_int4(reinterpret_cast<const _Float16*>(x), ldx, m, packed, rows, cols, scales,
-                         zeros, groupsize, relu == 1, reinterpret_cast<_Float16*>(y), ldy,
-                         reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
+  if (launch_linear_forward(bits, reinterpret_cast<const _Float16*>(x), ldx, m, packed, rows, cols,
+                            scales, zeros, groupsize, relu == 1, reinterpret_cast<_Float16*>(y),
+                            ldy, reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
     return GPTQ_ERR_HIP;
   return GPTQ_OK;
 }

@@ -28,8 +28,8 @@ def quantize_relu_block(x, W1, W2, bits: int = 4, groupsize: int = 128, blocksiz
     ``timer``, if given, is a context-manager factory ``timer(name)`` wrapped
     around each phase (the benchmark's event pairs)."""
     torch = _lib._torch()
-    if bits != 4:
-        raise ValueError("the block's forward product takes 4-bit codes")
+    if bits not in (4, 8):
+        raise ValueError("the block's forward product takes 4- or 8-bit codes")
     d, m = x.shape[1], W1.shape[0]
     if W1.shape[1] != d or W2.shape[1] != m:
         raise ValueError("shapes: x n x d, W1 m x d, W2 d_out x m")

@@ -198,7 +198,8 @@ def test_pack_and_product_validation():
 
 def test_linear_forward_validation():
     """Host-side checks of gptq_linear_forward (no launch): invalid arguments,
-    then the shapes the MFMA kernel does not take."""
+    then the shapes the MFMA kernel does not take. Every call fails before a
+    launch (the pointers are fake)."""
     E, U = gq.GPTQ_ERR_INVALID_ARG, gq.GPTQ_ERR_UNSUPPORTED
 
     def lf(x=FAKE, m=1, cols=256, ldx=256, packed=FAKE, bits=4, rows=8, sc=FAKE, zr=FAKE, g=128,
@@ -215,8 +216,9 @@ def test_linear_forward_validation():
     assert lf(x=FAKE + 1) == E and lf(y=FAKE + 1) == E
     assert lf(packed=FAKE + 2) == E and lf(sc=FAKE + 2) == E
     # valid arguments the 4-bit MFMA kernel does not take
-    assert lf(bits=3) == U and lf(bits=8) == U
+    assert lf(bits=3) == U and lf(bits=2) == U and lf(bits=5) == U
     assert lf(cols=200, ldx=200) == U                       # cols not a multiple of 128
+    assert lf(bits=8, cols=200, ldx=200) == U and lf(bits=8, g=64) == U
     assert lf(g=64) == U                                    # groups inside a 128-column stage
     assert lf(ldx=260) == U                                 # rows not 16-byte aligned
     assert lf(x=FAKE + 8) == U and lf(packed=FAKE + 4) == U

@@ -1,5 +1,5 @@
-"""The 4-bit layer's forward product for many tokens (MFMA, fp16 out) against
-the oracle.
+"""The forward product of a 4- or 8-bit layer for many tokens (MFMA, fp16 out)
+against the oracle.
 
 Codes, scales and zeros come from the oracle's round-to-nearest quantizer and
 are packed by the oracle; x is seeded fp16. The GPU sums the exact products
@@ -38,9 +38,9 @@ def ulp16(v):
     return np.ldexp(1.0, np.maximum(e - 1, -14) - 10)
 
 
-def _quantized(rows, cols, g, seed):
+def _quantized(rows, cols, g, seed, bits=4):
     W = np.random.default_rng(seed).standard_normal((rows, cols)) * 0.02
-    r = oracle.rtn(W, 4, g, precision="f32")
+    r = oracle.rtn(W, bits, g, precision="f32")
     return r["codes"], r["scales"].astype(np.float32), r["zeros"].astype(np.float32)
 
 
@@ -59,12 +59,12 @@ def _check(y_gpu, x, codes, s32, z32, g, relu):
     return float(np.mean(y_gpu == y_ref))
 
 
-def _case(env, m, rows, cols, g, relu, seed):
+def _case(env, m, rows, cols, g, relu, seed, bits=4):
     torch, gq = env
-    codes, s32, z32 = _quantized(rows, cols, g, seed)
+    codes, s32, z32 = _quantized(rows, cols, g, seed, bits)
     x = np.random.default_rng(seed + 1).standard_normal((m, cols)).astype(np.float16)
-    packed = _cuda(env, oracle.pack_codes(codes, 4).view(np.int32))
-    y = gq.linear_forward(_cuda(env, x), packed, 4, cols, _cuda(env, s32), _cuda(env, z32), g,
+    packed = _cuda(env, oracle.pack_codes(codes, bits).view(np.int32))
+    y = gq.linear_forward(_cuda(env, x), packed, bits, cols, _cuda(env, s32), _cuda(env, z32), g,
                           relu=relu)
     torch.cuda.synchronize()
     return _check(y.cpu().numpy(), x, codes, s32, z32, g, relu)
@@ -80,6 +80,19 @@ def _case(env, m, rows, cols, g, relu, seed):
 ])
 def test_linear_forward_matches_oracle(env, m, rows, cols, g, relu):
     same = _case(env, m, rows, cols, g, relu, seed=m + rows + cols)
+    print("identical fp16 outputs", same)
+    assert same >= 0.99
+
+
+@pytest.mark.parametrize("m,rows,cols,g,relu", [
+    (1, 1, 128, 128, False),
+    (300, 300, 512, 128, True),     # ragged token and output tiles (128 outputs per tile)
+    (200, 96, 384, 0, False),       # per-channel
+    (64, 130, 640, 256, True),      # groups of 256 and a short last group
+    (1000, 256, 1024, 128, False),  # eight stages through the ring
+])
+def test_linear_forward_8bit_matches_oracle(env, m, rows, cols, g, relu):
+    same = _case(env, m, rows, cols, g, relu, seed=m + 3 * rows + cols, bits=8)
     print("identical fp16 outputs", same)
     assert same >= 0.99
 

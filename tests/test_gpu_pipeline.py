@@ -54,22 +54,23 @@ def _layer_check(W, got, ref, H, g=128):
     return rep
 
 
-@pytest.mark.parametrize("n,d,m,dout,g", [
-    (4096, 256, 512, 256, 128),
-    (16384, 1024, 2048, 1024, 128),
-    (4096, 384, 640, 256, 0),        # per-channel scales in both layers
-    (4096, 512, 768, 384, 256),      # groups of 256: one fold per two stages
+@pytest.mark.parametrize("n,d,m,dout,g,bits", [
+    (4096, 256, 512, 256, 128, 4),
+    (16384, 1024, 2048, 1024, 128, 4),
+    (4096, 384, 640, 256, 0, 4),        # per-channel scales in both layers
+    (4096, 512, 768, 384, 256, 4),      # groups of 256: one fold per two stages
+    (4096, 256, 384, 256, 128, 8),      # 8-bit codes in both layers
 ])
-def test_relu_block_matches_oracle(env, n, d, m, dout, g):
+def test_relu_block_matches_oracle(env, n, d, m, dout, g, bits):
     torch, gq = env
     x, W1, W2 = _inputs(n, d, m, dout)
     out = gq.quantize_relu_block(torch.from_numpy(x).cuda(), torch.from_numpy(W1).cuda(),
-                                 torch.from_numpy(W2).cuda(), groupsize=g)
+                                 torch.from_numpy(W2).cuda(), bits=bits, groupsize=g)
     torch.cuda.synchronize()
     got = {k: {a: (b.cpu().numpy() if hasattr(b, "cpu") else b) for a, b in v.items()}
            for k, v in out.items() if k != "y1"}
     y1 = out["y1"].cpu().numpy()
-    ref = oracle.two_layer_block(x, W1, W2, 4, g, 128, 0.01, "f32", tie_distance=True)
+    ref = oracle.two_layer_block(x, W1, W2, bits, g, 128, 0.01, "f32", tie_distance=True)
     g1 = d if g <= 0 else g  # the first layer's group width
 
     assert h_rel_error(got["first"]["H"], ref["first"]["H"]) <= 1e-4
