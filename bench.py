@@ -418,7 +418,7 @@ def copy_probe(torch, dev, mib):
     del src, dst
 
 
-def pipeline_cpu_baseline(x, W1, W2, budget_s=4.0):
+def pipeline_cpu_baseline(x, W1, W2, bits=4, budget_s=4.0):
     """The fp64 oracle's layer-by-layer block on a bounded sample, each phase
     timed on a slice and scaled to the full block: H1 and H2 on 4096-token
     chunks until about budget_s, the two Hinv preparations at full size
@@ -445,7 +445,7 @@ def pipeline_cpu_baseline(x, W1, W2, budget_s=4.0):
     t_p1 = time.perf_counter() - t0
     r1 = min(512, m)
     t0 = time.perf_counter()
-    q1 = oracle.gptq(W1[:r1], U1, 4, 128, 128, precision="f32")
+    q1 = oracle.gptq(W1[:r1], U1, bits, 128, 128, precision="f32")
     t_s1 = (time.perf_counter() - t0) * m / r1
     nf = min(2048, n)
     t0 = time.perf_counter()
@@ -466,7 +466,7 @@ def pipeline_cpu_baseline(x, W1, W2, budget_s=4.0):
     r2 = min(256, dout)
     U2 = np.kron(np.eye(2), U2h)  # a 2h x 2h factor: the sweep's cost does not depend on values
     t0 = time.perf_counter()
-    oracle.gptq(W2[:r2, :U2.shape[0]], U2, 4, 128, 128, precision="f32")
+    oracle.gptq(W2[:r2, :U2.shape[0]], U2, bits, 128, 128, precision="f32")
     t_s2 = (time.perf_counter() - t0) * dout / r2
     est = t_h1 + t_p1 + t_s1 + t_f + t_h2 + t_p2 + t_s2
     return {
@@ -496,6 +496,7 @@ def pipeline_main(args):
     up = [L for L in synth.BLOCK if L.name == "up"][0]
     down = [L for L in synth.BLOCK if L.name == "down"][0]
     n, d, m, dout = up.x.n, up.x.d, up.w.rows, down.w.rows
+    bits = 4 if args.bits is None else args.bits
     log(f"generating x {n}x{d} fp16, W_up {m}x{d}, W_down {dout}x{m}")
     x = synth.activations(up.x, threads=min(16, len(os.sched_getaffinity(0))))
     W1, W2 = synth.weights(up.w), synth.weights(down.w)
@@ -515,14 +516,14 @@ def pipeline_main(args):
         return cm()
 
     for _ in range(args.warmup):
-        out = gq.quantize_relu_block(xd, W1d, W2d)
+        out = gq.quantize_relu_block(xd, W1d, W2d, bits=bits)
         del out
     torch.cuda.synchronize()
     ev.clear()
     log(f"timing {args.steps} steps")
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        out = gq.quantize_relu_block(xd, W1d, W2d, timer=timer)
+        out = gq.quantize_relu_block(xd, W1d, W2d, bits=bits, timer=timer)
         del out
     torch.cuda.synchronize()
     ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
@@ -535,7 +536,8 @@ def pipeline_main(args):
         w2["syrk"] + w2["prep"] + w2["lazy"] + w2["sweep"]
     # roofline of the dominant single kernel: the larger of the forward product
     # (one launch) and the second H accumulation (one SYRK call)
-    cand = {"forward1": ("linear_int4_kernel (the up projection's forward product)", fwd_flops),
+    cand = {"forward1": ("linear_kernel<%d, true> (the up projection's forward product)" % bits,
+                         fwd_flops),
             "acc2": ("hessian accumulate call at d=%d: syrk_fast_kernel + syrk_reduce_kernel" % m,
                      w2["syrk"])}
     dom = max(cand, key=lambda k: ph[k])
@@ -552,11 +554,11 @@ def pipeline_main(args):
     cpu = None
     if not args.no_cpu:
         log("cpu baseline (oracle on a bounded sample)")
-        cpu = pipeline_cpu_baseline(x, W1, W2)
+        cpu = pipeline_cpu_baseline(x, W1, W2, bits)
         log("  ", cpu)
     line = {
         "metric": "ms per layer-by-layer quantized MLP pair (up 11008x4096 -> ReLU -> down "
-                  "4096x11008, int4 g128; down's H from the quantized up's outputs)",
+                  f"4096x11008, int{bits} g128; down's H from the quantized up's outputs)",
         "value": round(ms_step, 4),
         "unit": "ms",
         "n_gpus": 1,
@@ -569,7 +571,7 @@ def pipeline_main(args):
         "dtype": "f16-in/f32-acc SYRK and forward product, f64 Hinv, f32 sweep",
         "data": "synthetic (seeded low-rank-plus-noise activations, Gaussian weights)",
         "config": {"workload": f"MLP pair: x {n}x{d} fp16 (128x2048 tokens), W_up {m}x{d} fp16, "
-                               f"W_down {dout}x{m} fp16, int4 g128 B128 percdamp 0.01; "
+                               f"W_down {dout}x{m} fp16, int{bits} g128 B128 percdamp 0.01; "
                                "y1 = fp16(relu(x W_up_hat^T)) recorded for the down projection",
                    "phase_ms": {k: round(v, 4) for k, v in ph.items()},
                    "effective_tflops": round(work / (ms_step * 1e-3) / 1e12, 2),

@@ -104,6 +104,31 @@ def test_linear_forward_full_width(env):
     assert same >= 0.99
 
 
+def test_linear_forward_bench_shape_sampled(env):
+    """The MLP pair's forward product as the benchmark launches it: all 262144
+    tokens of the seeded MLP-input stream x 4096 -> 11008 outputs, int4 g128,
+    ReLU; 48 tokens (the ends, token-tile edges and random ones) compared in
+    full against the oracle."""
+    torch, gq = env
+    import synth
+    up = [L for L in synth.BLOCK if L.name == "up"][0]
+    x = synth.activations(up.x)
+    r = oracle.rtn(synth.weights(up.w), 4, 128, precision="f32")
+    codes, s32, z32 = r["codes"], r["scales"].astype(np.float32), r["zeros"].astype(np.float32)
+    n, cols = x.shape
+    xd = torch.from_numpy(x).cuda()
+    y = gq.linear_forward(xd, _cuda(env, oracle.pack_codes(codes, 4).view(np.int32)), 4, cols,
+                          _cuda(env, s32), _cuda(env, z32), 128, relu=True)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(11)
+    edges = [0, 127, 128, n // 2 - 1, n // 2, n - 129, n - 128, n - 1]
+    toks = np.unique(np.concatenate([edges, rng.integers(0, n, 40)]))
+    yt = y[torch.from_numpy(toks).cuda()].cpu().numpy()
+    del y, xd
+    torch.cuda.empty_cache()
+    assert _check(yt, x[toks], codes, s32, z32, 128, True) >= 0.99
+
+
 def test_linear_forward_zero_tokens_and_unsupported_shapes(env):
     torch, gq = env
     codes, s32, z32 = _quantized(8, 256, 128, 3)
