@@ -104,6 +104,30 @@ def test_linear_forward_full_width(env):
     assert same >= 0.99
 
 
+@pytest.mark.parametrize("bits", [4, 8])
+def test_linear_forward_strided_operands(env, bits):
+    """x a row-strided view (ldx > cols, rows still 16-byte aligned) and y
+    written into the left part of a wider buffer (ldy > rows): outputs equal
+    the contiguous call's, and the rest of the buffer is untouched."""
+    torch, gq = env
+    m, rows, cols, g = 200, 300, 512, 128
+    codes, s32, z32 = _quantized(rows, cols, g, 21, bits)
+    x = np.random.default_rng(22).standard_normal((m, cols)).astype(np.float16)
+    packed = _cuda(env, oracle.pack_codes(codes, bits).view(np.int32))
+    sc, zr = _cuda(env, s32), _cuda(env, z32)
+    big = torch.zeros((m, cols + 64), dtype=torch.float16, device="cuda")
+    big[:, :cols] = torch.from_numpy(x).cuda()
+    xv = big[:, :cols]                                  # ldx = cols + 64
+    ybuf = torch.full((m, rows + 40), 7.0, dtype=torch.float16, device="cuda")
+    yv = ybuf[:, :rows]                                 # ldy = rows + 40
+    gq.linear_forward(xv, packed, bits, cols, sc, zr, g, relu=True, out=yv)
+    y0 = gq.linear_forward(_cuda(env, x), packed, bits, cols, sc, zr, g, relu=True)
+    torch.cuda.synchronize()
+    assert torch.equal(yv, y0)
+    assert bool((ybuf[:, rows:] == 7.0).all())
+    _check(yv.cpu().numpy(), x, codes, s32, z32, g, True)
+
+
 def test_linear_forward_bench_shape_sampled(env):
     """The MLP pair's forward product as the benchmark launches it: all 262144
     tokens of the seeded MLP-input stream x 4096 -> 11008 outputs, int4 g128,
