@@ -226,3 +226,17 @@ def test_linear_forward_validation():
     assert lf(m=1 << 20, rows=1 << 20, ldy=1 << 20) == U    # launch grid would pass 2^32 items
     # m = 0 is a no-op: nothing is read, so null x and y are accepted
     assert lf(m=0, x=None, y=None, ldx=0) == gq.GPTQ_OK
+
+
+def test_relu_block_rejects_unsupported_bits_and_shapes():
+    """The layer-by-layer driver checks its arguments before any device work."""
+    torch = pytest.importorskip("torch")
+    x = torch.zeros((4, 128), dtype=torch.float16)
+    W1, W2 = torch.zeros((8, 128)), torch.zeros((4, 8))
+    for bits in (2, 3, 5):
+        with pytest.raises(ValueError, match="4- or 8-bit"):
+            gq.quantize_relu_block(x, W1, W2, bits=bits)
+    with pytest.raises(ValueError, match="shapes"):
+        gq.quantize_relu_block(x, torch.zeros((8, 64)), W2)
+    with pytest.raises(ValueError, match="shapes"):
+        gq.quantize_relu_block(x, W1, torch.zeros((4, 9)))
