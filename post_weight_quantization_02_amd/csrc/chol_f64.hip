@@ -1026,11 +1026,11 @@ __global__ __launch_bounds__(256, 2) void gemm128_f64_kernel(GemmDesc g) {
 // a dense 4096^3 product, and the finer tiles balance triangular K ranges
 // and small updates better.
 template <bool AK, bool BN, bool CN>
-hipError_t gemm_f64(const GemmDesc& g, int batches, hipStream_t s) {
+hipError_t gemm_f64(const GemmDesc& g, int batches, hipStream_t s, int64_t min_big_tiles = 4096) {
   if (g.M <= 0 || g.N <= 0 || batches <= 0) return hipSuccess;
   const int64_t tm = ceil_div(g.M, GT2), tn = ceil_div(g.N, GT2);
   const int64_t tiles = (g.tri ? tm * (tm + 1) / 2 : tm * tn) * batches;
-  const bool big = g.M > GT && g.N > GT && tiles >= 4096;
+  const bool big = g.M > GT && g.N > GT && tiles >= min_big_tiles;
   if (!big) return gemm64<AK, BN, CN>(g, batches, s);
   hipLaunchKernelGGL((gemm128_f64_kernel<AK, BN, CN>), dim3((unsigned)(tiles / batches), batches),
                      dim3(256), 0, s, g);
@@ -1193,7 +1193,9 @@ hipError_t launch_lauum(const double* X, int ldx, double* S, int lds, int d, hip
   g.M = g.N = g.K = d;
   g.alpha = 1.0; g.beta = 0.0; g.tri = 1; g.kmode = 3;
   g.trA = 2; g.trB = 1;
-  return gemm_f64<false, true, true>(g, 1, s);
+  // one large triangular product: from about d = 8192 on (2048 tiles of
+  // 128x128) the coarser tiles win
+  return gemm_f64<false, true, true>(g, 1, s, 2048);
 }
 
 hipError_t launch_store_upper_f32(const double* L2, int ld2, float* Hinv, int d, hipStream_t s) {
