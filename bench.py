@@ -43,6 +43,8 @@ SYRK_SOURCE = os.path.join(ROOT, "post_weight_quantization_02_amd", "csrc", "syr
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "hessian_accumulate_attn_traffic.md")
 LINEAR_SOURCE = os.path.join(ROOT, "post_weight_quantization_02_amd", "csrc", "linear_mfma.hip")
 LINEAR_TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "mlp_pair_pipeline_kernels.md")
+INFER_SOURCE = os.path.join(ROOT, "post_weight_quantization_02_amd", "csrc", "infer.hip")
+DECODE_TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "decode_step_traffic.md")
 
 
 def log(*a):
@@ -291,6 +293,7 @@ def decode_main(args):
     import post_weight_quantization_02_amd as gq
 
     dev = torch.device("cuda:0")
+    copy_probe(torch, dev, args.copy_probe_mib)
     m, bits, g = args.tokens, 4, 128
     gen = torch.Generator(device=dev)
     gen.manual_seed(1234)
@@ -397,7 +400,10 @@ def decode_main(args):
                      "kernel": "dequant_gemv_fast_kernel (the %d launches of a step, gaps "
                                "included)" % len(mats),
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": (recorded_traffic(DECODE_TRAFFIC_SUMMARY, INFER_SOURCE,
+                                                  "infer_source_sha256_16")
+                                 if m == 1 and not args.fused else None),
                      "bytes_per_step": alg_bytes},
         "cpu_baseline": cpu,
     }
