@@ -44,6 +44,8 @@ TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "hessian_accumulate_attn_traffi
 LINEAR_SOURCE = os.path.join(ROOT, "post_weight_quantization_02_amd", "csrc", "linear_mfma.hip")
 LINEAR_TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "mlp_pair_pipeline_kernels.md")
 INFER_SOURCE = os.path.join(ROOT, "post_weight_quantization_02_amd", "csrc", "infer.hip")
+# the same SYRK launch (262144 x 11008 fp16 inputs): the mlp_down layer and the pipeline's second H
+TRAFFIC_SUMMARY_11008 = os.path.join(ROOT, "profiles", "hessian_accumulate_mlp_down_traffic.md")
 DECODE_TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "decode_step_traffic.md")
 
 
@@ -550,9 +552,10 @@ def pipeline_main(args):
     rf = {}
     for k, (name, flops) in cand.items():
         ach = flops / (ph[k] * 1e-3) / 1e12
-        tr = None
         if k == "forward1":
             tr = recorded_traffic(LINEAR_TRAFFIC_SUMMARY, LINEAR_SOURCE, "linear_source_sha256_16")
+        else:
+            tr = recorded_traffic(TRAFFIC_SUMMARY_11008) if m == 11008 else None
         rf[k] = {"bound": "mfma", "kernel": name, "achieved": round(ach, 2),
                  "peak": FP16_MFMA_TFLOPS, "unit": "TFLOP/s",
                  "frac": round(ach / FP16_MFMA_TFLOPS, 4), "traffic": tr,
@@ -713,7 +716,11 @@ def main():
     acc_ms = float(np.mean(acc_calls))
     syrk_flops_call = work["syrk"] / len(job.groups)
     syrk_tflops = syrk_flops_call / (acc_ms * 1e-3) / 1e12
-    traffic = recorded_traffic() if args.layer == "attn" and not args.act_order else None
+    traffic = None
+    if args.layer == "attn" and not args.act_order:
+        traffic = recorded_traffic()
+    elif args.layer == "mlp_down" and not args.act_order:
+        traffic = recorded_traffic(TRAFFIC_SUMMARY_11008)
 
     cpu = None
     if not args.no_cpu and args.layer != "block":
