@@ -259,9 +259,10 @@ gptq_status quantize_impl(const void* W, int w_dtype, int64_t rows, int64_t cols
   // errors reach the rest of the superblock before those columns are swept;
   // the columns after the superblock receive all of its errors in one GEMM
   // with K = SB.  Every column still gets every update before its block is
-  // swept (and before its group's statistics are taken, since SB is a
-  // multiple of the group size when groups span blocks), so the result
-  // equals per-block lazy updates in exact arithmetic.  When groups lie
+  // swept (and before its group's statistics are taken: when groups span
+  // blocks SB is a multiple of the group size, so every group lies inside
+  // one superblock and its later columns receive each block's errors right
+  // away), so the result equals per-block lazy updates in exact arithmetic.  When groups lie
   // inside blocks, the sweep kernel applies a block's pending errors from the
   // earlier blocks of its superblock itself (to its own rows, just before
   // sweeping them); when groups span blocks, a group's statistics read
@@ -270,7 +271,7 @@ gptq_status quantize_impl(const void* W, int w_dtype, int64_t rows, int64_t cols
   // (A single per-channel group takes its statistics before any update, so
   // it puts no constraint on the superblock.)
   const int64_t SB = (groupsize > kBlock && !per_channel)
-                         ? (groupsize > kSuperBlock ? groupsize : kSuperBlock)
+                         ? groupsize * ceil_div(kSuperBlock, groupsize)
                          : kSuperBlock;
   const bool fused_near = groupsize <= kBlock;
   for (int64_t s0 = 0; s0 < cols; s0 += SB) {

@@ -46,6 +46,9 @@ def _gpu_quant(env, W, U32, bits, g):
     (33, 320, 4, 64, "f32"),
     (20, 512, 8, 16, "f32"),
     (24, 640, 4, 256, "f16"),     # groups spanning two blocks, short last group
+    (40, 1152, 4, 384, "f32"),    # groups of three blocks: the group at 384 ends past
+                                  # column 512, so superblocks must hold whole groups
+    (20, 1300, 3, 640, "f16"),    # groups of five blocks, short last group
     (5, 130, 4, 128, "f32"),      # 2-column last block
     (1, 64, 4, 128, "f32"),       # a single row, a single short block
     (50, 1100, 4, 128, "f16"),    # three superblocks, the last one a ragged block
@@ -59,8 +62,9 @@ def _gpu_quant(env, W, U32, bits, g):
 def test_sweep_matches_oracle_given_hinv(env, rows, cols, bits, g, wdt):
     W, H, U32 = _case(rows, cols, 4 * cols, wdtype=wdt)
     codes, scales, zeros, losses = _gpu_quant(env, W, U32, bits, g)
-    ref = oracle.gptq(W, U32.astype(np.float64), bits, g, 128, precision="f32", tie_distance=True)
-    rep = assert_sweep_parity(codes, scales, zeros, ref, g)
+    U = U32.astype(np.float64)
+    ref = oracle.gptq(W, U, bits, g, 128, precision="f32", tie_distance=True)
+    rep = assert_sweep_parity(codes, scales, zeros, ref, g, W=W, U=U, bits=bits)
     assert codes.max() <= (1 << bits) - 1
     # first group of every row sees unmodified weights: bit-exact scale and zero
     assert np.array_equal(scales[:, 0], ref["scales"][:, 0].astype(np.float32))
