@@ -132,22 +132,34 @@ def hinv_upper(H: np.ndarray, percdamp: float):
 # --------------------------------------------------------------------------
 # Quantizer ([RTN] listing: asymmetric min/max grid per row and group)
 # --------------------------------------------------------------------------
-def group_params(G: np.ndarray, bits: int, precision: str = "f64"):
-    """Per-row scale and zero point from the current values G (rows x g)."""
+def group_params(G: np.ndarray, bits: int, precision: str = "f64", position: bool = False):
+    """Per-row scale and zero point from the current values G (rows x g).
+    With ``position`` also the unrounded zero position -min/s."""
     qmax = (1 << bits) - 1
     if precision == "f64":
         G = np.asarray(G, dtype=np.float64)
         mn, mx = G.min(axis=1), G.max(axis=1)
         s = np.maximum((mx - mn) / qmax, 1e-8)
-        z = np.clip(np.rint(-mn / s), 0, qmax)
-        return s, z
-    if precision == "f32":
+        tz = -mn / s
+    elif precision == "f32":
         G = np.asarray(G, dtype=np.float64).astype(np.float32)
         mn, mx = G.min(axis=1), G.max(axis=1)
         s = np.maximum((mx - mn) / np.float32(qmax), np.float32(1e-8))
-        z = np.clip(np.rint(-mn / s), 0, qmax)
-        return s.astype(np.float64), z.astype(np.float64)
-    raise ValueError(precision)
+        tz = -mn / s
+    else:
+        raise ValueError(precision)
+    z = np.clip(np.rint(tz), 0, qmax)
+    s, z, tz = s.astype(np.float64), z.astype(np.float64), tz.astype(np.float64)
+    return (s, z, tz) if position else (s, z)
+
+
+def _near_tie_alternative(given, own, t, tie_tol):
+    """True where the integer decision `given` differs from this sweep's own
+    rounding `own` of the unrounded value t by one level and t lies within
+    tie_tol levels of the rounding boundary between the two: a perturbation
+    of t of that size decides for either neighbour."""
+    lo = np.minimum(given, own)
+    return (np.abs(given - own) == 1) & (np.abs(t - (lo + 0.5)) <= tie_tol)
 
 
 def grid_position(w: np.ndarray, s: np.ndarray, z: np.ndarray,
@@ -180,7 +192,8 @@ def quantize(w: np.ndarray, s: np.ndarray, z: np.ndarray, bits: int,
 # --------------------------------------------------------------------------
 def gptq(W: np.ndarray, U: np.ndarray, bits: int = 4, groupsize: int = 128,
          blocksize: int = 128, precision: str = "f64", trace: bool = False,
-         tie_distance: bool = False):
+         tie_distance: bool = False, follow: Optional[dict] = None,
+         tie_tol: float = 2e-3):
     """Returns dict(codes, scales, zeros, losses[, trace][, tie_distance]).
 
     codes  rows x cols (int64 in [0, 2^bits-1])
@@ -191,6 +204,25 @@ def gptq(W: np.ndarray, U: np.ndarray, bits: int = 4, groupsize: int = 128,
            rounding tie (k + 1/2) when the code was decided; 0 means an exact
            tie, so a small value marks a decision that a tiny perturbation of
            the inputs can flip to the neighbouring level
+
+    follow (optional) dict(codes=rows x cols, zeros=rows x ngroups): another
+           result whose integer decisions are to be checked against this
+           sweep. Every decision rounds an unrounded value (w/s + z for a
+           code, -min/s for a zero point); where such a value lies within
+           ``tie_tol`` levels of a rounding boundary, either neighbour is a
+           correct outcome under a perturbation of the inputs that small,
+           and everything after it depends on which was taken. So at each
+           decision the given one is taken when it equals this sweep's own
+           rounding or is the other neighbour of a near tie; otherwise this
+           sweep keeps its own and counts a violation. The sweep then
+           continues from the decision taken, so every later decision is
+           checked from the state the given result was in. Extra outputs:
+             own_codes   rows x cols, this sweep's own rounding at each step
+             alternatives rows x cols bool, near-tie neighbours taken
+             zero_alternatives rows x ngroups bool, likewise for zero points
+             violations  rows x cols bool, code decisions that were neither
+             zero_violations rows x ngroups bool, likewise for zero points
+           With follow, codes and zeros are the decisions taken.
     """
     W = np.asarray(W, dtype=np.float64)
     rows, cols = W.shape
@@ -205,18 +237,40 @@ def gptq(W: np.ndarray, U: np.ndarray, bits: int = 4, groupsize: int = 128,
     losses = np.zeros(cols)
     states = [] if trace else None
     ties = np.zeros((rows, cols)) if tie_distance else None
+    if follow is not None:
+        f_codes = np.asarray(follow["codes"], dtype=np.float64)
+        f_zeros = np.asarray(follow["zeros"], dtype=np.float64)
+        assert f_codes.shape == (rows, cols) and f_zeros.shape == (rows, ngroups)
+        own_codes = np.zeros((rows, cols), dtype=np.int64)
+        alts = np.zeros((rows, cols), dtype=bool)
+        viol = np.zeros((rows, cols), dtype=bool)
+        zalts = np.zeros((rows, ngroups), dtype=bool)
+        zviol = np.zeros((rows, ngroups), dtype=bool)
     s = z = None
     for i1 in range(0, cols, B):
         i2 = min(i1 + B, cols)
         Err1 = np.zeros((rows, i2 - i1))
         for j in range(i1, i2):
             if j % g == 0:
-                s, z = group_params(Wk[:, j:min(j + g, cols)], bits, precision)
+                s, z, tz = group_params(Wk[:, j:min(j + g, cols)], bits, precision, position=True)
+                if follow is not None:
+                    gz = f_zeros[:, j // g]
+                    ok = (gz == z) | _near_tie_alternative(gz, z, tz, tie_tol)
+                    zalts[:, j // g] = ok & (gz != z)
+                    zviol[:, j // g] = ~ok
+                    z = np.where(ok, gz, z)
                 scales[:, j // g] = s
                 zeros[:, j // g] = z
             w = Wk[:, j].copy()
             t = grid_position(w, s, z, precision)
             q = np.clip(np.rint(t), 0, (1 << bits) - 1)
+            if follow is not None:
+                own_codes[:, j] = q.astype(np.int64)
+                gq = f_codes[:, j]
+                ok = (gq == q) | _near_tie_alternative(gq, q, t, tie_tol)
+                alts[:, j] = ok & (gq != q)
+                viol[:, j] = ~ok
+                q = np.where(ok, gq, q)
             if tie_distance:
                 ties[:, j] = np.abs(np.abs(t - np.floor(t)) - 0.5)
             w_hat = (q - z) * s
@@ -237,6 +291,9 @@ def gptq(W: np.ndarray, U: np.ndarray, bits: int = 4, groupsize: int = 128,
         out["trace"] = states
     if tie_distance:
         out["tie_distance"] = ties
+    if follow is not None:
+        out.update(own_codes=own_codes, alternatives=alts, violations=viol,
+                   zero_alternatives=zalts, zero_violations=zviol)
     return out
 
 
