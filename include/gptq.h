@@ -100,9 +100,11 @@ size_t gptq_workspace_bytes(int op, int64_t rows, int64_t cols, int64_t n);
  *   n      tokens in this chunk, >= 0 (0 is a no-op).
  *   ldx    row stride of X in elements, >= d.
  *   alpha  scale applied to X^T X (2.0 for H = 2XX^T).
- *   Products of fp16 values are exact in fp32; sums are accumulated in fp32
- *   in an order that depends only on (d, n), so results are bitwise
- *   reproducible.
+ *   Products of fp16 values are exact in fp32.  The tokens are cut into
+ *   splits of at most 4096; each split's sums are accumulated in fp32, the
+ *   split sums are added in fp64 in split order, and each entry is rounded
+ *   once to fp32 when alpha times that sum is added into H.  The order
+ *   depends only on (d, n), so results are bitwise reproducible.
  */
 gptq_status gptq_hessian_accumulate(float* H, int64_t d, const void* X, int64_t n,
                                     int64_t ldx, float alpha, void* workspace,

@@ -24,7 +24,7 @@
 //     General path (ragged d or n, unaligned X): register-staged, double-
 //     buffered LDS with padded rows.
 //   * The token range is split so the grid fills every CU for several rounds
-//     (at most 8192 tokens per split: a split sums in fp32); each split
+//     (at most 4096 tokens per split: a split sums in fp32); each split
 //     writes its own fp32 partial tile and a second kernel sums the partials
 //     in a fixed order in fp64 (bitwise reproducible, no float atomics).
 //   * fp16 products are exact in fp32; accumulation is fp32.
@@ -417,14 +417,19 @@ int syrk_splits(int64_t d, int64_t n) {
   // One 256x256 workgroup runs per CU at a time.  Pick the split count that
   // minimises (rounds of 256 workgroups) x (time of one split) plus the time
   // to write and re-read the fp32 partial tiles, with at most kMaxSplitChunks
-  // chunks (8192 tokens) per split: a partial sums its products in fp32, and
-  // shorter runs keep H within about 1e-7 of the exact sum.
+  // chunks (4096 tokens) per split.  A partial sums its products in fp32, so
+  // H's error grows with the tokens per split: at 262144 tokens of the
+  // attention stream, 8192-token splits leave H 1.0e-7 from the exact sum
+  // (Frobenius, relative) and Hinv 3.1e-6, 4096-token splits 6.6e-8 and
+  // 1.8e-6.  The larger error moves late group scales of an 11008-row
+  // layer up to 1.4e-5 (relative) from the exact-arithmetic result, past
+  // the 1e-5 the quantizer's outputs are held to; the smaller one 8.0e-6.
   const int64_t nb = ceil_div(d, T);
   const int64_t tiles = nb * (nb + 1) / 2;
   const int64_t chunks = ceil_div(n, KC);
   const double t_tile = 2.0 * T * T * (double)(chunks * KC) / (4.0 * 1024.0 * 2.4e9);
   const double t_part = (double)T * T * 4.0 * 2.0 / 6.0e12;
-  constexpr int64_t kMaxSplitChunks = 256;
+  constexpr int64_t kMaxSplitChunks = 128;
   constexpr int64_t kMaxSplits = 128;
   int64_t lo = ceil_div(chunks, kMaxSplitChunks);
   if (lo < 1) lo = 1;
