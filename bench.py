@@ -174,17 +174,17 @@ def cpu_baseline(layer, X, W, budget_s=8.0, act_order=False):
 
 
 class Job:
-    """Device buffers and the per-step call sequence of one workload.
-
-    ``hs``: list of (XSpec, layers sharing its H); every layer of a group
-    shares one Hinv.  One workspace of the largest size serves every call.
-    """
+    """Device buffers of one workload and its per-step call sequence
+    (post_weight_quantization_02_amd.block.quantize_streams: one H and one
+    Hinv per activation stream, shared by that stream's layers, and one
+    workspace of the largest size for every call)."""
 
     def __init__(self, torch, gq, synth, groups, dev, act_order=False):
-        self.torch, self.gq = torch, gq
+        from post_weight_quantization_02_amd import block
+        self.torch, self.gq, self.block = torch, gq, block
         self.act_order = act_order
         self.groups = []
-        ws_bytes = 0
+        self.streams = []
         threads = min(16, len(os.sched_getaffinity(0)))
         for xs, layers in groups:
             log(f"generating X {xs.n}x{xs.d} fp16")
@@ -196,19 +196,16 @@ class Job:
             ls = []
             for L in layers:
                 W = synth.weights(L.w)
-                ng = (L.w.cols + L.groupsize - 1) // L.groupsize
-                outs = (torch.empty((L.w.rows, L.w.cols), dtype=torch.uint8, device=dev),
-                        torch.empty((L.w.rows, ng), dtype=torch.float32, device=dev),
-                        torch.empty((L.w.rows, ng), dtype=torch.float32, device=dev),
-                        torch.empty((L.w.cols,), dtype=torch.float32, device=dev))
-                if act_order:
-                    outs = outs + (torch.empty((L.w.cols,), dtype=torch.int32, device=dev),)
-                ls.append((L, W, torch.from_numpy(W).to(dev), outs))
-                op = gq.OP_QUANTIZE_PERM if act_order else gq.OP_QUANTIZE
-                ws_bytes = max(ws_bytes, gq.workspace_bytes(op, L.w.rows, xs.d, 0))
-            ws_bytes = max(ws_bytes, gq.workspace_bytes(gq.OP_ACCUMULATE, 0, xs.d, xs.n),
-                           gq.workspace_bytes(gq.OP_PREPARE, 0, xs.d, 0))
+                Wd = torch.from_numpy(W).to(dev)
+                outs = block.allocate_outputs(torch, Wd, L.groupsize, act_order)
+                ls.append((L, W, Wd, outs))
             self.groups.append((xs, X, Xd, H, U, perm, ls))
+            self.streams.append(block.BlockStream(
+                X=Xd, H=H, U=U, perm=perm, percdamp=layers[0].percdamp,
+                layers=[block.BlockLayer(W=Wd, bits=L.bits, groupsize=L.groupsize,
+                                         blocksize=L.blocksize, out=outs)
+                        for L, _, Wd, outs in ls]))
+        ws_bytes = block.workspace_bytes(self.streams, act_order)
         raw = torch.empty(ws_bytes + 256, dtype=torch.uint8, device=dev)
         off = (-raw.data_ptr()) % 256
         self.ws = raw[off:off + ws_bytes]
@@ -216,38 +213,19 @@ class Job:
         self.ev = {k: [] for k in ("acc", "prep", "quant")}
 
     def step(self, record):
-        torch, gq = self.torch, self.gq
-        for xs, X, Xd, H, U, perm, ls in self.groups:
-            H.zero_()
-            e = [torch.cuda.Event(enable_timing=True) for _ in range(3)] if record else None
-            if record:
-                e[0].record(self.stream)
-            gq.hessian_accumulate(H, Xd, 2.0, workspace=self.ws)
-            if record:
-                e[1].record(self.stream)
-            if self.act_order:
-                gq.act_order(H, out=perm)
-                gq.prepare_hinv_perm(H, perm, ls[0][0].percdamp, out=U, workspace=self.ws)
+        torch = self.torch
+        open_ev = {}
+
+        def mark(phase, begin):
+            e = torch.cuda.Event(enable_timing=True)
+            e.record(self.stream)
+            if begin:
+                open_ev[phase] = e
             else:
-                gq.prepare_hinv(H, ls[0][0].percdamp, out=U, workspace=self.ws)
-            if record:
-                e[2].record(self.stream)
-                self.ev["acc"].append((e[0], e[1]))
-                self.ev["prep"].append((e[1], e[2]))
-            for L, W, Wd, outs in ls:
-                if record:
-                    q0 = torch.cuda.Event(enable_timing=True)
-                    q1 = torch.cuda.Event(enable_timing=True)
-                    q0.record(self.stream)
-                if self.act_order:
-                    gq.quantize_layer_perm(Wd, perm, U, L.bits, L.groupsize, L.blocksize,
-                                           out=outs, workspace=self.ws)
-                else:
-                    gq.quantize_layer(Wd, U, L.bits, L.groupsize, L.blocksize, out=outs,
-                                      workspace=self.ws)
-                if record:
-                    q1.record(self.stream)
-                    self.ev["quant"].append((q0, q1))
+                self.ev[phase].append((open_ev.pop(phase), e))
+
+        self.block.quantize_streams(self.streams, self.ws, self.act_order,
+                                    mark=mark if record else None)
 
 
 DECODE_SHAPES = (("q", 4096, 4096), ("k", 4096, 4096), ("v", 4096, 4096), ("o", 4096, 4096),

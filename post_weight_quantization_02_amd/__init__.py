@@ -35,3 +35,4 @@ from ._lib import (  # noqa: F401
     workspace_bytes,
 )
 from .pipeline import quantize_relu_block  # noqa: F401,E402
+from .block import BlockLayer, BlockStream, quantize_streams  # noqa: F401,E402

@@ -154,9 +154,10 @@ def test_sweep_perm_matches_oracle_given_hinv(env, rows, cols, bits, g, wdt):
     W, H, perm, U32 = _perm_case(rows, cols, 4 * cols, wdt)
     codes, scales, zeros, losses, g_idx = _gpu_quant_perm(env, W, perm, U32, bits, g)
     # the oracle's sweep in processing order, with the same fp32 Hinv
-    ref = oracle.gptq(W[:, perm], U32.astype(np.float64), bits, g, 128, precision="f32",
-                      tie_distance=True)
-    rep = assert_sweep_parity(codes[:, perm], scales, zeros, ref, g)
+    U = U32.astype(np.float64)
+    ref = oracle.gptq(W[:, perm], U, bits, g, 128, precision="f32", tie_distance=True)
+    rep = assert_sweep_parity(codes[:, perm], scales, zeros, ref, g, W=W[:, perm], U=U,
+                              bits=bits)
     gi = np.empty(cols, np.int64)
     gi[perm] = np.arange(cols) // g
     assert np.array_equal(g_idx, gi)
@@ -216,16 +217,17 @@ def check_gpu_order(perm, H_gpu, Href, tol=1e-5):
     return int(np.sum(perm != oracle.act_order_perm(np.diag(Href))))
 
 
-def check_act_order_result(W, out, ref, g, Href, rows=None):
+def check_act_order_result(W, out, ref, g, Href, bits, rows=None):
     """Element parity in processing order (the GPU ran the oracle's order)
-    and the layer output error within 1% of the oracle's."""
+    and the layer output error within 1% of the oracle's. `ref` is the
+    oracle's act-order result for W's rows `rows` (all rows if None)."""
     perm = ref["perm"]
     sel = (lambda a: a) if rows is None else (lambda a: a[rows])
     Wr = sel(W)
     refp = dict(codes=ref["codes"][:, perm], scales=ref["scales"], zeros=ref["zeros"],
                 tie_distance=ref["tie_distance"][:, perm])
     rep = assert_sweep_parity(sel(out["codes"])[:, perm], sel(out["scales"]),
-                              sel(out["zeros"]), refp, g)
+                              sel(out["zeros"]), refp, g, W=Wr[:, perm], U=ref["U"], bits=bits)
     assert np.array_equal(out["g_idx"], ref["g_idx"])
     Wg = dequant(sel(out["codes"]), sel(out["scales"]), sel(out["zeros"]), g_idx=out["g_idx"])
     Wo = oracle.dequantize_gidx(ref["codes"], ref["scales"], ref["zeros"], ref["g_idx"])
@@ -252,7 +254,7 @@ def test_act_order_layer_end_to_end(env, name, rows, cols, n):
     Href = oracle.hessian([X], cols)
     ref = oracle.gptq_act_order(W, Href, 0.01, L.bits, 128, precision="f32", tie_distance=True)
     out = _gpu_act_order_layer(env, W, X, L.bits, 128, perm=ref["perm"], chunk=5000)
-    rep = check_act_order_result(W, out, ref, 128, Href)
+    rep = check_act_order_result(W, out, ref, 128, Href, L.bits)
     own = _gpu_act_order_layer(env, W, X, L.bits, 128, chunk=5000)
     moved = check_gpu_order(own["perm"], own["H"], Href)
     Wg = dequant(own["codes"], own["scales"], own["zeros"], g_idx=own["g_idx"])

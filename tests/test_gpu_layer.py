@@ -1,5 +1,10 @@
 """The whole path on the GPU (accumulate -> prepare -> quantize) against the
-oracle run end to end on the same fp16 inputs."""
+oracle run end to end on the same fp16 inputs.
+
+Every full-size test runs the GPU path in the launch configuration the
+benchmark times and prints, per layer: the fraction of identical codes, the
+rows that took a near-tie decision the other way, the largest raw code
+difference, and the followed comparison (tests/parity.py)."""
 import numpy as np
 import pytest
 
@@ -35,25 +40,37 @@ def _gpu_layer(env, W, X, bits, g, percdamp=0.01, chunk=None):
                 losses=losses.cpu().numpy())
 
 
-def _check(W, X, out, bits, g, Href=None, rows=None):
-    d = X.shape[1]
-    if Href is None:
-        Href = oracle.hessian([X], d)
-    assert h_rel_error(out["H"], Href) <= 1e-4
-    U, lam = oracle.hinv_upper(Href, 0.01)
+def _hessian(X, d):
+    return oracle.hessian((X[t:t + 8192] for t in range(0, X.shape[0], 8192)), d)
+
+
+def _check_layer(W, out, bits, g, Href, U=None, rows=None, h_tol=1e-4):
+    """H within h_tol (Frobenius, relative) when the GPU's H is given; the
+    sweep of the given rows (all if None) under the parity definition; the
+    output error under the oracle's H within 1% of the oracle's."""
+    if out.get("H") is not None:
+        assert h_rel_error(out["H"], Href) <= h_tol
+    if U is None:
+        U, _ = oracle.hinv_upper(Href, 0.01)
     Wr = W if rows is None else W[rows]
-    ref = oracle.gptq(Wr, U, bits, g, 128, precision="f32", tie_distance=True)
     sel = (lambda a: a) if rows is None else (lambda a: a[rows])
-    rep = assert_sweep_parity(sel(out["codes"]), sel(out["scales"]), sel(out["zeros"]), ref, g)
+    ref = oracle.gptq(Wr, U, bits, g, 128, precision="f32", tie_distance=True)
+    rep = assert_sweep_parity(sel(out["codes"]), sel(out["scales"]), sel(out["zeros"]), ref, g,
+                              W=Wr, U=U, bits=bits)
     Wg = dequant(sel(out["codes"]), sel(out["scales"]), sel(out["zeros"]), g)
     Wo = oracle.dequantize(ref["codes"], ref["scales"], ref["zeros"], g)
     e_gpu = output_error(Wr, Wg, Href)
     e_ref = oracle.output_error(Wr, Wo, Href)
     assert abs(e_gpu - e_ref) <= 0.01 * e_ref, (e_gpu, e_ref)
-    rt = oracle.rtn(Wr, bits, g, precision="f32")
-    e_rtn = oracle.output_error(Wr, oracle.dequantize(rt["codes"], rt["scales"], rt["zeros"], g), Href)
-    rep.update(e_gpu=e_gpu, e_ref=e_ref, e_rtn=e_rtn)
+    rep.update(e_gpu=e_gpu, e_ref=e_ref)
     return rep
+
+
+def _summary(name, rep):
+    keys = ("rows", "same", "rows_diverged", "raw_max_dcode", "raw_codes_over_1",
+            "followed_same", "near_tie_codes", "near_tie_zeros", "violations",
+            "followed_max_dcode", "followed_max_rel_scale", "e_gpu", "e_ref")
+    print(name, {k: rep[k] for k in keys if k in rep}, flush=True)
 
 
 def test_tiny_layer(env):
@@ -61,7 +78,7 @@ def test_tiny_layer(env):
     X = synth.activations(L.x)
     W = synth.weights(L.w)
     out = _gpu_layer(env, W, X, 4, 128)
-    rep = _check(W, X, out, 4, 128)
+    rep = _check_layer(W, out, 4, 128, oracle.hessian([X], L.x.d))
     assert rep["same"] == 1.0, rep
 
 
@@ -75,89 +92,84 @@ def test_reduced_layers(env, name, rows, cols, n):
     X = synth.activations(L.x)
     W = synth.weights(L.w)
     out = _gpu_layer(env, W, X, L.bits, 128, chunk=5000)
-    rep = _check(W, X, out, L.bits, 128)
-    print(name, rep)
+    _summary(name, _check_layer(W, out, L.bits, 128, oracle.hessian([X], L.x.d)))
 
 
 @pytest.fixture(scope="module")
 def attn_inputs():
-    """X of the attention workload (262144 x 4096 fp16) and its fp64 H."""
+    """X of the attention workload (262144 x 4096 fp16), its fp64 H and the
+    oracle's Hinv."""
     L = synth.LAYERS["attn"]
     X = synth.activations(L.x, threads=16)
-    Href = oracle.hessian((X[t:t + 8192] for t in range(0, X.shape[0], 8192)), L.x.d)
-    return X, Href
+    Href = _hessian(X, L.x.d)
+    U, _ = oracle.hinv_upper(Href, 0.01)
+    return X, Href, U
 
 
-def test_full_attention_layer_sampled_rows(env, attn_inputs):
+def test_full_attention_layer_all_rows(env, attn_inputs):
     """4096x4096 int4 g128 at 262144 tokens, the benchmark configuration (one
-    accumulate call over all tokens, as the benchmark times it). The GPU
-    quantizes every row; the oracle has H in fp64 over all tokens, its own
-    Hinv, and the sweep for 96 sampled rows (rows are independent)."""
+    accumulate call over all tokens, as the benchmark times it); all 4096 rows
+    compared with the oracle's fp64 run."""
     L = synth.LAYERS["attn"]
-    X, Href = attn_inputs
+    X, Href, U = attn_inputs
     W = synth.weights(L.w)
     out = _gpu_layer(env, W, X, 4, 128)
-    rows = np.sort(np.random.default_rng(0).choice(4096, 96, replace=False))
-    rep = _check(W, X, out, 4, 128, Href=Href, rows=rows)
-    print("attn full", rep)
+    _summary("attn full", _check_layer(W, out, 4, 128, Href, U=U))
 
 
-def test_full_attention_layer_act_order(env, attn_inputs):
+def test_full_attention_layer_act_order_all_rows(env, attn_inputs):
     """The benchmark's act-order configuration: 4096x4096 int4 g128 at
     262144 tokens, columns in decreasing order of diag(H). Run once with the
-    oracle's order passed in (96 sampled rows compared element by element in
+    oracle's order passed in (all rows compared element by element in
     processing order) and once with the GPU's own order from its own H
     (checked by its properties; near-equal diagonal entries may swap within
     the fp32 accumulation error), both scored by the layer output error."""
     from test_gpu_act_order import _gpu_act_order_layer, check_act_order_result, check_gpu_order
     L = synth.LAYERS["attn"]
-    X, Href = attn_inputs
+    X, Href, _ = attn_inputs
     W = synth.weights(L.w)
-    rows = np.sort(np.random.default_rng(3).choice(4096, 96, replace=False))
-    ref = oracle.gptq_act_order(W[rows], Href, 0.01, 4, 128, precision="f32", tie_distance=True)
+    ref = oracle.gptq_act_order(W, Href, 0.01, 4, 128, precision="f32", tie_distance=True)
     out = _gpu_act_order_layer(env, W, X, 4, 128, perm=ref["perm"])
-    rep = check_act_order_result(W, out, ref, 128, Href, rows=rows)
+    rep = check_act_order_result(W, out, ref, 128, Href, 4)
     own = _gpu_act_order_layer(env, W, X, 4, 128)
     moved = check_gpu_order(own["perm"], own["H"], Href)
-    Wg = dequant(own["codes"][rows], own["scales"][rows], own["zeros"][rows], g_idx=own["g_idx"])
-    e_own = output_error(W[rows], Wg, Href)
+    Wg = dequant(own["codes"], own["scales"], own["zeros"], g_idx=own["g_idx"])
+    e_own = output_error(W, Wg, Href)
     assert abs(e_own - rep["e_ref"]) <= 0.01 * rep["e_ref"], (e_own, rep["e_ref"])
-    print("attn full act-order", rep, "own order: positions differing", moved, "e_own", e_own)
+    _summary("attn full act-order", rep)
+    print("  own order: positions differing", moved, "e_own", e_own)
 
 
-def test_full_mlp_up_layer_sampled_rows(env, attn_inputs):
+def test_full_mlp_up_layer_all_rows(env, attn_inputs):
     """11008x4096 int3 g128 on the attention activations (the MLP input has the
-    same generator), full size; 96 sampled rows against the oracle."""
+    same generator), full size; all 11008 rows against the oracle."""
     L = synth.LAYERS["mlp_up"]
-    X, Href = attn_inputs
+    X, Href, U = attn_inputs
     W = synth.weights(L.w)
     out = _gpu_layer(env, W, X, L.bits, 128)
-    rows = np.sort(np.random.default_rng(1).choice(L.w.rows, 96, replace=False))
-    rep = _check(W, X, out, L.bits, 128, Href=Href, rows=rows)
-    print("mlp_up full", rep)
+    _summary("mlp_up full", _check_layer(W, out, L.bits, 128, Href, U=U))
 
 
-def test_full_mlp_down_layer_sampled(env):
-    """4096x11008 int4 g128 at 262144 tokens with 60% zeros and 220 dead
-    channels (H singular before damping), full size. A full fp64 H is 6e13
-    flops on the host, so:
-      * the GPU path runs as the benchmark runs it (one accumulate call over
-        all tokens, the preparation, the sweep), and its H is compared on 3000
-        sampled entries, each an fp64 dot product over all tokens (diagonal
-        entries of dead channels included);
-      * the preparation and the sweep are compared at full size on an H the
-        oracle forms itself, from the first 65536 tokens (rounded to fp32 for
-        both sides; the launch configuration of both depends only on the
-        shapes): Hinv against the oracle's, and the sweep of every row with
-        the oracle's Hinv against the oracle's sweep on 128 sampled rows,
-        scored by the output error under that H."""
+@pytest.fixture(scope="module")
+def down_inputs():
+    L = synth.LAYERS["mlp_down"]
+    return synth.activations(L.x, threads=16)
+
+
+def test_full_mlp_down_hessian_sampled_entries(env, down_inputs):
+    """4096x11008 at 262144 tokens with 60% zeros and 220 dead channels (H
+    singular before damping), one accumulate call over all tokens as the
+    benchmark makes it: 3000 sampled entries of H, each an fp64 dot product
+    over all tokens (diagonal entries of dead channels included)."""
     torch, gq = env
     L = synth.LAYERS["mlp_down"]
-    X = synth.activations(L.x, threads=16)
-    W = synth.weights(L.w)
-    out = _gpu_layer(env, W, X, 4, 128)
+    X = down_inputs
     d = L.x.d
-    Hg = out["H"]
+    H = torch.zeros((d, d), dtype=torch.float32, device="cuda")
+    gq.hessian_accumulate(H, torch.from_numpy(X).cuda(), 2.0)
+    torch.cuda.synchronize()
+    Hg = H.cpu().numpy()
+    del H
     rng = np.random.default_rng(2)
     dead = synth.dead_channels(L.x)
     ii = np.concatenate([rng.integers(0, d, 2900), dead[:50], rng.integers(0, d, 50)])
@@ -171,29 +183,155 @@ def test_full_mlp_down_layer_sampled(env):
     scale = np.abs(np.diag(Hg)).max()
     assert np.abs(hgpu - href).max() <= 1e-4 * scale
     assert np.all(hgpu[2900:2950] == 0.0)  # dead channel diagonal entries
-    del out, Hg
-    # the oracle's H on a token subset, its Hinv, and both stages on the GPU
-    Hs = oracle.hessian((X[t:t + 16384] for t in range(0, 65536, 16384)), d).astype(np.float32)
-    U, lam = oracle.hinv_upper(Hs.astype(np.float64), 0.01)
-    Ug = gq.prepare_hinv(torch.from_numpy(Hs).cuda(), 0.01)
+
+
+def test_full_mlp_down_chain_gpu_h_hinv_codes(env, down_inputs):
+    """The GPU's own chain at d = 11008: H accumulated on the GPU from the
+    first 131072 tokens of the mlp_down stream in one call, the GPU's Hinv
+    from that H, and the sweep of all 4096 rows with that Hinv, against the
+    oracle's fp64 H from the same tokens, its Hinv and its sweep on 1024
+    sampled rows."""
+    torch, gq = env
+    L = synth.LAYERS["mlp_down"]
+    n = 131072
+    X = down_inputs[:n]
+    W = synth.weights(L.w)
+    out = _gpu_layer(env, W, X, 4, 128)
+    Href = _hessian(X, L.x.d)
+    U, _ = oracle.hinv_upper(Href, 0.01)
+    hinv_err = float(np.abs(out["U"] - U).max() / np.abs(U).max())
+    assert hinv_err <= 1e-4, hinv_err
+    rows = np.sort(np.random.default_rng(4).choice(L.w.rows, 1024, replace=False))
+    rep = _check_layer(W, out, 4, 128, Href, U=U, rows=rows)
+    rep["hinv_rel_max"] = hinv_err
+    rep["h_rel"] = h_rel_error(out["H"], Href)
+    _summary("mlp_down chain", rep)
+    print("  H rel", rep["h_rel"], "Hinv rel max", hinv_err)
+
+
+# ------------------------------------------------------------ the block
+def _block_layers(scale=None):
+    """The seven layers of the Llama-7B-shaped block, optionally at reduced
+    width: scale = (d_model, d_ff, tokens)."""
+    if scale is None:
+        return list(synth.BLOCK)
+    dm, dff, n = scale
+    out = []
+    for L in synth.BLOCK:
+        rows = dff if L.w.rows == 11008 else dm
+        cols = dff if L.w.cols == 11008 else dm
+        out.append(L.scaled(rows=rows, cols=cols, n=n))
+    return out
+
+
+def _gpu_block(env, layers):
+    """The benchmark's call sequence (block.quantize_streams): streams in
+    order, one H and one Hinv per stream, layers in order q, k, v, o, gate,
+    up, down, one workspace for every call. Returns the host copies of every
+    stream's H and Hinv and every layer's outputs."""
+    torch, gq = env
+    from post_weight_quantization_02_amd import block
+    streams, Xs = [], []
+    for L in layers:
+        if streams and Xs[-1][0] == L.x:
+            st = streams[-1]
+        else:
+            X = synth.activations(L.x, threads=16)
+            Xs.append((L.x, X))
+            d = L.x.d
+            st = block.BlockStream(X=torch.from_numpy(X).cuda(),
+                                   H=torch.empty((d, d), dtype=torch.float32, device="cuda"),
+                                   U=torch.empty((d, d), dtype=torch.float32, device="cuda"),
+                                   layers=[], percdamp=L.percdamp)
+            streams.append(st)
+        Wd = torch.from_numpy(synth.weights(L.w)).cuda()
+        st.layers.append(block.BlockLayer(W=Wd, bits=L.bits, groupsize=L.groupsize,
+                                          blocksize=L.blocksize,
+                                          out=block.allocate_outputs(torch, Wd, L.groupsize)))
+    nb = block.workspace_bytes(streams)
+    raw = torch.empty(nb + 256, dtype=torch.uint8, device="cuda")
+    off = (-raw.data_ptr()) % 256
+    block.quantize_streams(streams, raw[off:off + nb])
     torch.cuda.synchronize()
-    err = np.abs(Ug.cpu().numpy() - U).max() / np.abs(U).max()
-    assert err <= 2e-6, err
-    del Ug
-    U32 = U.astype(np.float32)
-    codes, scales, zeros, _ = gq.quantize_layer(torch.from_numpy(W).cuda(),
-                                                torch.from_numpy(U32).cuda(), 4, 128, 128)
-    torch.cuda.synchronize()
-    codes, scales, zeros = codes.cpu().numpy(), scales.cpu().numpy(), zeros.cpu().numpy()
-    rows = np.sort(rng.choice(L.w.rows, 128, replace=False))
-    ref = oracle.gptq(W[rows], U32.astype(np.float64), 4, 128, 128, precision="f32",
-                      tie_distance=True)
-    rep = assert_sweep_parity(codes[rows], scales[rows], zeros[rows], ref, 128)
-    Hs64 = Hs.astype(np.float64)
-    Wr = W[rows]
-    e_gpu = output_error(Wr, dequant(codes[rows], scales[rows], zeros[rows], 128), Hs64)
-    e_ref = oracle.output_error(Wr, oracle.dequantize(ref["codes"], ref["scales"], ref["zeros"],
-                                                      128), Hs64)
-    assert abs(e_gpu - e_ref) <= 0.01 * e_ref, (e_gpu, e_ref)
-    rep.update(e_gpu=e_gpu, e_ref=e_ref, hinv_err=err)
-    print("mlp_down full", rep)
+    res = []
+    for (xs, X), st in zip(Xs, streams):
+        lay = [dict(codes=ly.out[0].cpu().numpy(), scales=ly.out[1].cpu().numpy(),
+                    zeros=ly.out[2].cpu().numpy(), H=None) for ly in st.layers]
+        res.append(dict(x=xs, X=X, H=st.H.cpu().numpy(), U=st.U.cpu().numpy(), layers=lay))
+    del streams, raw
+    torch.cuda.empty_cache()
+    return res
+
+
+def _check_stream(res, layers, rows_per_layer=None, seed=0, oracle_h=None):
+    """One stream of the block: its H, then every layer on it against the
+    oracle's sweep with the oracle's Hinv (all rows, or a sample).
+    `oracle_h` = (H, Hinv) of the oracle when already formed from the same X."""
+    if oracle_h is None:
+        Href = _hessian(res["X"], res["x"].d)
+        U, _ = oracle.hinv_upper(Href, 0.01)
+    else:
+        Href, U = oracle_h
+    assert h_rel_error(res["H"], Href) <= 1e-4
+    reps = []
+    for L, out in zip(layers, res["layers"]):
+        W = synth.weights(L.w)
+        rows = None
+        if rows_per_layer is not None and rows_per_layer < L.w.rows:
+            rows = np.sort(np.random.default_rng(seed).choice(L.w.rows, rows_per_layer,
+                                                              replace=False))
+        rep = _check_layer(W, out, L.bits, L.groupsize, Href, U=U, rows=rows)
+        _summary(f"block {L.name}", rep)
+        reps.append(rep)
+    return reps
+
+
+def _split(layers):
+    groups = []
+    for L in layers:
+        if groups and groups[-1][0].x == L.x:
+            groups[-1].append(L)
+        else:
+            groups.append([L])
+    return groups
+
+
+def test_block_reduced_width_all_rows(env):
+    """The seven-layer block at reduced width (d_model 512, d_ff 1376, 16384
+    tokens per stream; four streams, Hinv shared by q/k/v and by gate/up, one
+    workspace), every row of every layer against the oracle."""
+    layers = _block_layers((512, 1376, 16384))
+    res = _gpu_block(env, layers)
+    groups = _split(layers)
+    assert [len(g) for g in groups] == [3, 1, 2, 1]
+    for r, g in zip(res, groups):
+        _check_stream(r, g)
+
+
+@pytest.fixture(scope="module")
+def full_block(env):
+    layers = _block_layers()
+    return layers, _gpu_block(env, layers)
+
+
+def test_full_block_attention_and_mlp_input_streams(env, full_block, attn_inputs):
+    """The full-size block on the GPU in the benchmark's call sequence; the
+    q/k/v (attention input), o and gate/up (MLP input) streams against the
+    oracle's fp64 H over all 262144 tokens, 1024 sampled rows per layer."""
+    layers, res = full_block
+    groups = _split(layers)
+    assert res[0]["x"] == synth.LAYERS["attn"].x  # the attention workload's stream
+    for i, (r, g) in enumerate(list(zip(res, groups))[:3]):
+        _check_stream(r, g, rows_per_layer=1024, seed=len(g),
+                      oracle_h=attn_inputs[1:] if i == 0 else None)
+
+
+@pytest.mark.timeout(300)
+def test_full_block_down_stream(env, full_block):
+    """The full-size block's down projection (4096x11008, the mlp_down stream
+    at 262144 tokens) against the oracle's fp64 H over all tokens, 512
+    sampled rows."""
+    layers, res = full_block
+    groups = _split(layers)
+    assert groups[3][0].name == "down"
+    _check_stream(res[3], groups[3], rows_per_layer=512, seed=7)

@@ -44,8 +44,9 @@ def _inputs(n, d, m, dout):
     return x, W1, W2
 
 
-def _layer_check(W, got, ref, H, g=128):
-    rep = assert_sweep_parity(got["codes"], got["scales"], got["zeros"], ref, g)
+def _layer_check(W, got, ref, H, g, bits):
+    rep = assert_sweep_parity(got["codes"], got["scales"], got["zeros"], ref, g, W=W,
+                              U=ref["U"], bits=bits)
     Wg = dequant(got["codes"], got["scales"], got["zeros"], g)
     Wo = oracle.dequantize(ref["codes"], ref["scales"], ref["zeros"], g)
     e_gpu, e_ref = output_error(W, Wg, H), oracle.output_error(W, Wo, H)
@@ -74,7 +75,7 @@ def test_relu_block_matches_oracle(env, n, d, m, dout, g, bits):
     g1 = d if g <= 0 else g  # the first layer's group width
 
     assert h_rel_error(got["first"]["H"], ref["first"]["H"]) <= 1e-4
-    r1 = _layer_check(W1, got["first"], ref["first"], ref["first"]["H"], g)
+    r1 = _layer_check(W1, got["first"], ref["first"], ref["first"]["H"], g, bits)
 
     # recorded inputs of the second layer, on channels whose first-layer codes agree
     c1, s1, z1 = got["first"]["codes"], got["first"]["scales"], got["first"]["zeros"]
@@ -97,7 +98,7 @@ def test_relu_block_matches_oracle(env, n, d, m, dout, g, bits):
     H2g, H2o = got["second"]["H"], ref["second"]["H"]
     if same_rows.all():
         assert h_rel_error(H2g, H2o) <= 1e-4
-        r2 = _layer_check(W2, got["second"], ref["second"], H2o, g)
+        r2 = _layer_check(W2, got["second"], ref["second"], H2o, g, bits)
     else:
         # A channel whose first-layer codes took a legitimate near-tie flip
         # records different (equally valid) inputs, so H2 differs in its row
