@@ -115,7 +115,11 @@ def _stream_ptr(stream, device) -> Optional[int]:
     return stream.cuda_stream
 
 
-def _workspace(nbytes: int, device, workspace=None):
+def _workspace(nbytes: int, device, workspace=None, stream=None):
+    """The caller's workspace (checked), or a temporary one. A temporary is
+    freed when the call returns while its kernels may still run; torch's
+    caching allocator keeps it from being reused before the work queued on
+    the current stream ends, and record_stream extends that to `stream`."""
     torch = _torch()
     if nbytes == 0:
         return None, 0
@@ -126,9 +130,21 @@ def _workspace(nbytes: int, device, workspace=None):
             raise ValueError("workspace must be 256-byte aligned")
         return workspace, workspace.numel() * workspace.element_size()
     ws = torch.empty(nbytes + 256, dtype=torch.uint8, device=device)
+    if stream is not None and stream != torch.cuda.current_stream(device):
+        ws.record_stream(stream)
     off = (-ws.data_ptr()) % 256
     ws = ws[off:off + nbytes]
     return ws, nbytes
+
+
+def _check_out(t, shape, dtype, device, name):
+    """A preallocated output must match exactly: the library writes
+    prod(shape) elements of dtype from its data pointer."""
+    if t is None or t.dtype != dtype or tuple(t.shape) != tuple(shape) or t.device != device \
+            or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor of shape {tuple(shape)} "
+                         f"on {device}")
+    return t
 
 
 def _check(status: int, where: str, info: int = 0):
@@ -149,7 +165,7 @@ def hessian_accumulate(H, X, alpha: float = 2.0, workspace=None, stream=None):
         raise ValueError("shape mismatch")
     n = X.shape[0]
     ldx = X.stride(0) if n > 1 else d
-    ws, wsb = _workspace(workspace_bytes(OP_ACCUMULATE, 0, d, n), H.device, workspace)
+    ws, wsb = _workspace(workspace_bytes(OP_ACCUMULATE, 0, d, n), H.device, workspace, stream)
     st = lib.gptq_hessian_accumulate(H.data_ptr(), d, X.data_ptr(), n, ldx, alpha,
                                      ws.data_ptr() if ws is not None else None, wsb,
                                      _stream_ptr(stream, H.device))
@@ -203,7 +219,8 @@ def prepare_hinv_perm(H, perm, percdamp: float = 0.01, out=None, workspace=None,
     perm = _check_perm(perm, d, H.device)
     if out is None:
         out = torch.empty((d, d), dtype=torch.float32, device=H.device)
-    ws, wsb = _workspace(workspace_bytes(OP_PREPARE, 0, d, 0), H.device, workspace)
+    _check_out(out, (d, d), torch.float32, H.device, "out")
+    ws, wsb = _workspace(workspace_bytes(OP_PREPARE, 0, d, 0), H.device, workspace, stream)
     info = ctypes.c_int64(0)
     st_ptr = _stream_ptr(stream, H.device)
     if perm is None:
@@ -247,7 +264,11 @@ def quantize_layer(W, Hinv, bits: int = 4, groupsize: int = 128, blocksize: int 
         losses = torch.empty((cols,), dtype=torch.float32, device=dev)
     else:
         codes, scales, zeros, losses = out
-    ws, wsb = _workspace(workspace_bytes(OP_QUANTIZE, rows, cols, 0), dev, workspace)
+    _check_out(codes, (rows, cols), torch.uint8, dev, "codes")
+    _check_out(scales, (rows, ng), torch.float32, dev, "scales")
+    _check_out(zeros, (rows, ng), torch.float32, dev, "zeros")
+    _check_out(losses, (cols,), torch.float32, dev, "losses")
+    ws, wsb = _workspace(workspace_bytes(OP_QUANTIZE, rows, cols, 0), dev, workspace, stream)
     ldw = W.stride(0) if rows > 1 else cols
     st = lib.gptq_quantize_layer(W.data_ptr(), wdt, rows, cols, ldw, Hinv.data_ptr(), bits,
                                  groupsize, blocksize, codes.data_ptr(), scales.data_ptr(),
@@ -289,7 +310,14 @@ def quantize_layer_perm(W, perm, Hinv, bits: int = 4, groupsize: int = 128, bloc
         g_idx = torch.empty((cols,), dtype=torch.int32, device=dev)
     else:
         codes, scales, zeros, losses, g_idx = out
-    ws, wsb = _workspace(workspace_bytes(OP_QUANTIZE_PERM, rows, cols, 0), dev, workspace)
+    _check_out(codes, (rows, cols), torch.uint8, dev, "codes")
+    _check_out(scales, (rows, ng), torch.float32, dev, "scales")
+    _check_out(zeros, (rows, ng), torch.float32, dev, "zeros")
+    _check_out(losses, (cols,), torch.float32, dev, "losses")
+    if g_idx is not None:
+        _check_out(g_idx, (cols,), torch.int32, dev, "g_idx")
+    ws, wsb = _workspace(workspace_bytes(OP_QUANTIZE_PERM, rows, cols, 0), dev, workspace,
+                         stream)
     ldw = W.stride(0) if rows > 1 else cols
     st = lib.gptq_quantize_layer_perm(W.data_ptr(), wdt, rows, cols, ldw,
                                       perm.data_ptr() if perm is not None else None,
@@ -317,6 +345,7 @@ def pack_codes(codes, bits: int, out=None, stream=None):
     nw = packed_words(cols, bits)
     if out is None:
         out = torch.empty((rows, nw), dtype=torch.int32, device=codes.device)
+    _check_out(out, (rows, nw), torch.int32, codes.device, "out")
     st = lib.gptq_pack_codes(codes.data_ptr(), rows, cols, bits, out.data_ptr(),
                              _stream_ptr(stream, codes.device))
     _check(st, "gptq_pack_codes")
@@ -345,6 +374,10 @@ def dequant_gemm(x, packed, bits: int, cols: int, scales, zeros, groupsize: int,
     m = x.shape[0]
     if out is None:
         out = torch.empty((m, rows), dtype=torch.float32, device=x.device)
+    if out.dtype != torch.float32 or tuple(out.shape) != (m, rows) or out.device != x.device \
+            or (m > 0 and out.stride(1) != 1):
+        raise ValueError(f"out must be an {m} x {rows} fp32 tensor with unit column stride "
+                         f"on {x.device}")
     ldx = x.stride(0) if m > 1 else cols
     st = lib.gptq_dequant_gemm(x.data_ptr(), m, cols, ldx, packed.data_ptr(), bits, rows,
                                scales.data_ptr(), zeros.data_ptr(), groupsize,
@@ -376,7 +409,8 @@ def linear_forward(x, packed, bits: int, cols: int, scales, zeros, groupsize: in
     m = x.shape[0]
     if out is None:
         out = torch.empty((m, rows), dtype=torch.float16, device=x.device)
-    elif out.dtype != torch.float16 or out.shape != (m, rows) or out.stride(1) != 1:
+    elif out.dtype != torch.float16 or out.shape != (m, rows) or out.stride(1) != 1 or \
+            out.device != x.device:
         raise ValueError("out must be an m x rows fp16 tensor with unit column stride")
     ldx = x.stride(0) if m > 1 else cols
     st = lib.gptq_linear_forward(x.data_ptr(), m, cols, ldx, packed.data_ptr(), bits, rows,
