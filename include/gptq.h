@@ -101,7 +101,8 @@ size_t gptq_workspace_bytes(int op, int64_t rows, int64_t cols, int64_t n);
  *   ldx    row stride of X in elements, >= d.
  *   alpha  scale applied to X^T X (2.0 for H = 2XX^T).
  *   Products of fp16 values are exact in fp32.  The tokens are cut into
- *   splits of at most 4096; each split's sums are accumulated in fp32, the
+ *   splits of at most 4096 (of n/128 above 524288 tokens per call); each
+ *   split's sums are accumulated in fp32, the
  *   split sums are added in fp64 in split order, and each entry is rounded
  *   once to fp32 when alpha times that sum is added into H.  The order
  *   depends only on (d, n), so results are bitwise reproducible.
@@ -353,6 +354,31 @@ gptq_status gptq_linear_forward(const void* x, int64_t m, int64_t cols, int64_t 
                                 const uint32_t* packed, int bits, int64_t rows,
                                 const float* scales, const float* zeros, int groupsize, int relu,
                                 void* y, int64_t ldy, void* stream);
+
+/*
+ * gptq_hessian_accumulate_noalloc -- gptq_hessian_accumulate without a
+ * workspace and without any allocation, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving or calibration
+ * loops, and harnesses that forbid hipMalloc.
+ *
+ * The split partial tiles go to a fixed array of 96 MiB that the library
+ * holds on every GPU it runs on, from load until the process ends; nothing
+ * is allocated or freed by the call.  H, d, X, n, ldx and alpha mean what
+ * they mean for gptq_hessian_accumulate, and the result is the same sum:
+ * the tokens are processed in passes of at most floor(384 / T) splits of at
+ * most 4096 tokens each (T = ceil(d/256)*(ceil(d/256)+1)/2 tiles), each
+ * pass adding its fp64 split sum into H with one fp32 rounding.  So it can
+ * differ from gptq_hessian_accumulate in the last bits when n spans
+ * several passes.
+ *
+ *   d > 6912 (more than 384 tiles): GPTQ_ERR_UNSUPPORTED, nothing launched.
+ *   stream must belong to the current device (GPTQ_ERR_INVALID_ARG).
+ *   All calls on one GPU share the array: calls that overlap on one GPU
+ *   (on different streams, or from different threads) race and give wrong
+ *   results; calls on one stream are ordered and safe.  Asynchronous.
+ */
+gptq_status gptq_hessian_accumulate_noalloc(float* H, int64_t d, const void* X, int64_t n,
+                                            int64_t ldx, float alpha, void* stream);
 
 #ifdef __cplusplus
 }

@@ -22,6 +22,7 @@ from ._lib import (  # noqa: F401
     act_order,
     dequant_gemm,
     hessian_accumulate,
+    hessian_accumulate_noalloc,
     lib,
     linear_forward,
     pack_codes,

@@ -74,6 +74,8 @@ lib.gptq_dequant_gemm.argtypes = [_p, _i64, _i64, _i64, _p, _int, _i64, _p, _p, 
 lib.gptq_linear_forward.restype = _int
 lib.gptq_linear_forward.argtypes = [_p, _i64, _i64, _i64, _p, _int, _i64, _p, _p, _int, _int, _p,
                                     _i64, _p]
+lib.gptq_hessian_accumulate_noalloc.restype = _int
+lib.gptq_hessian_accumulate_noalloc.argtypes = [_p, _i64, _p, _i64, _i64, ctypes.c_float, _p]
 lib.gptq_quantize_layer_perm.restype = _int
 lib.gptq_quantize_layer_perm.argtypes = [_p, _int, _i64, _i64, _i64, _p, _p, _int, _int, _int,
                                          _p, _p, _p, _p, _p, _p, _sz, _p]
@@ -170,6 +172,25 @@ def hessian_accumulate(H, X, alpha: float = 2.0, workspace=None, stream=None):
                                      ws.data_ptr() if ws is not None else None, wsb,
                                      _stream_ptr(stream, H.device))
     _check(st, "gptq_hessian_accumulate")
+    return H
+
+
+def hessian_accumulate_noalloc(H, X, alpha: float = 2.0, stream=None):
+    """H += alpha * X^T X like hessian_accumulate, with no workspace and no
+    allocation (gptq_hessian_accumulate_noalloc). Returns H."""
+    torch = _torch()
+    if H.dtype != torch.float32 or not H.is_cuda or not H.is_contiguous():
+        raise ValueError("H must be a contiguous fp32 CUDA tensor")
+    if X.dtype != torch.float16 or X.device != H.device or X.dim() != 2 or X.stride(1) != 1:
+        raise ValueError("X must be a 2-D fp16 CUDA tensor with unit column stride")
+    d = H.shape[0]
+    if H.shape != (d, d) or X.shape[1] != d:
+        raise ValueError("shape mismatch")
+    n = X.shape[0]
+    ldx = X.stride(0) if n > 1 else d
+    st = lib.gptq_hessian_accumulate_noalloc(H.data_ptr(), d, X.data_ptr(), n, ldx, alpha,
+                                             _stream_ptr(stream, H.device))
+    _check(st, "gptq_hessian_accumulate_noalloc")
     return H
 
 

@@ -13,7 +13,7 @@ LIB = os.path.join(HERE, "libgptq_mi355x.so")
 BUILD = os.path.join(HERE, "_build")
 
 SOURCES = ["gptq_abi.cpp", "syrk_f16.hip", "chol_f64.hip", "sweep.hip", "act_order.hip", "infer.hip",
-           "linear_mfma.hip"]
+           "linear_mfma.hip", "accumulate_noalloc.hip"]
 
 # Per-file code generation options.  The fp64 kernels keep their MFMA
 # accumulators in ordinary VGPRs: with the default AGPR form the compiler

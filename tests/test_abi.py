@@ -240,3 +240,19 @@ def test_relu_block_rejects_unsupported_bits_and_shapes():
         gq.quantize_relu_block(x, torch.zeros((8, 64)), W2)
     with pytest.raises(ValueError, match="shapes"):
         gq.quantize_relu_block(x, W1, torch.zeros((4, 9)))
+
+
+def test_noalloc_accumulate_validation():
+    """Rejected on the host, before any HIP call: oversized d (the fixed
+    partial array holds 384 tiles of 256x256), bad pointers and sizes; n = 0
+    is a no-op."""
+    f = lib.gptq_hessian_accumulate_noalloc
+    assert f(FAKE, 6913, FAKE, 10, 6913, 2.0, None) == gq.GPTQ_ERR_UNSUPPORTED
+    assert f(FAKE, 11008, FAKE, 10, 11008, 2.0, None) == gq.GPTQ_ERR_UNSUPPORTED
+    assert f(None, 64, FAKE, 10, 64, 2.0, None) == gq.GPTQ_ERR_INVALID_ARG
+    assert f(FAKE, 64, None, 10, 64, 2.0, None) == gq.GPTQ_ERR_INVALID_ARG
+    assert f(FAKE, 64, FAKE, 10, 63, 2.0, None) == gq.GPTQ_ERR_INVALID_ARG
+    assert f(FAKE, 0, FAKE, 10, 64, 2.0, None) == gq.GPTQ_ERR_INVALID_ARG
+    assert f(FAKE, 64, FAKE, -1, 64, 2.0, None) == gq.GPTQ_ERR_INVALID_ARG
+    assert f(FAKE + 2, 64, FAKE, 10, 64, 2.0, None) == gq.GPTQ_ERR_INVALID_ARG
+    assert f(FAKE, 6912, FAKE, 0, 6912, 2.0, None) == gq.GPTQ_OK
