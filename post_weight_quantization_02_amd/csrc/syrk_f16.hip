@@ -384,7 +384,21 @@ __global__ __launch_bounds__(256) void syrk_reduce_kernel(const float* __restric
     const int rr = 16 * pass + (tid >> 4);
     const float* src = P + (int64_t)tile * T * T + (int64_t)(64 * qr + rr) * T + 64 * qc + c4;
     double v0 = 0.0, v1 = 0.0, v2 = 0.0, v3 = 0.0;
-    for (int sp = 0; sp < splits; ++sp) {
+    // eight splits' loads in flight at a time; the sums stay in split order
+    int sp = 0;
+    for (; sp + 8 <= splits; sp += 8) {
+      float4 p[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) p[u] = *reinterpret_cast<const float4*>(src + (sp + u) * stride);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        v0 += (double)p[u].x;
+        v1 += (double)p[u].y;
+        v2 += (double)p[u].z;
+        v3 += (double)p[u].w;
+      }
+    }
+    for (; sp < splits; ++sp) {
       const float4 p = *reinterpret_cast<const float4*>(src + sp * stride);
       v0 += (double)p.x;
       v1 += (double)p.y;

@@ -24,7 +24,9 @@ def _hinv(env, H32, p=0.01):
 
 
 @pytest.mark.parametrize("d,n", [(256, 512), (64, 300), (1, 10), (200, 2000), (1000, 8000),
-                                 (333, 4000)])
+                                 (333, 4000),
+                                 # whole and ragged panels, and the benchmark's size
+                                 (1024, 8192), (1100, 8192), (2500, 12000), (4096, 16384)])
 def test_hinv_matches_oracle(env, d, n):
     x = synth.X_ATTN.scaled(d=d, n=n, rank=min(256, max(1, d // 4)))
     X = synth.activations(x)
@@ -63,6 +65,19 @@ def test_dead_channels_without_damping_report_first_pivot(env):
     U = _hinv(env, H32, 0.01)
     Uref, _ = oracle.hinv_upper(H32.astype(np.float64), 0.01)
     assert np.abs(U - Uref).max() / np.abs(Uref).max() <= 2e-6
+
+
+@pytest.mark.parametrize("bad", [77, 300, 511, 512, 900, 1199])
+def test_failed_pivot_anywhere(env, bad):
+    """d = 1200: a negative diagonal entry in an otherwise diagonal H fails
+    exactly at its own pivot, inside a 64-column panel, at its first or last
+    column, and in the last (ragged) panel."""
+    torch, gq = env
+    H = np.eye(1200, dtype=np.float32) * 2.0
+    H[bad, bad] = -1.0
+    with pytest.raises(gq.GPTQError) as ei:
+        _hinv(env, H, 0.0)
+    assert ei.value.status == gq.GPTQ_ERR_NOT_PD and ei.value.info == bad + 1
 
 
 def test_nan_reports_pivot_one(env):
