@@ -58,6 +58,15 @@ __device__ inline double rsqrt_f64(double p) {
   const double r = __builtin_amdgcn_rsq(p);
   return r * __builtin_fma(-0.5 * p * r, r, 1.5);
 }
+
+// 1/p: hardware estimate and one Newton step (relative error of order the
+// square of the estimate's, as for rsqrt_f64).  The pivot chain of the 16x16
+// factorization needs 1/p for its multipliers; taking it here rather than as
+// the square of rsqrt_f64 puts two fewer dependent operations on that chain.
+__device__ inline double rcp_f64(double p) {
+  const double r = __builtin_amdgcn_rcp(p);
+  return __builtin_fma(r, __builtin_fma(-p, r, 1.0), r);
+}
 constexpr int GT = 64;      // GEMM tile edge
 constexpr int GK = 16;      // GEMM K chunk
 
@@ -166,8 +175,8 @@ __device__ inline void factor16_step(double (&a)[4], double (&y)[4], double& ysc
   const double c = lane_gather(a[IJ], gaddr[QJ]);    // A[m][J], from lane group QJ
   const double p = lane_value<J + 16 * QJ>(a[IJ]);   // pivot A[J][J]
   bad = (p > 0.0) ? bad : min(bad, J);
-  const double rs = rsqrt_f64(p);
-  const double r2 = (m > J) ? rs * rs : 0.0;
+  const double rs = rsqrt_f64(p);                     // for L and the inverse, off the chain
+  const double r2 = (m > J) ? rcp_f64(p) : 0.0;
   const double t = c * r2;                            // multiplier of row J for rows below it
   // rows below J: the columns past J get the right-looking update with row J
 #pragma unroll
