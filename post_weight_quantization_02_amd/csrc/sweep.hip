@@ -62,16 +62,6 @@ __device__ inline void grid_params(float mn, float mx, float qm, float& s, float
   z = fminf(fmaxf(rintf(-mn / s), 0.f), qm);
 }
 
-// x / s correctly rounded (IEEE binary32), given rs = RN(1/s): the residual
-// x - q0*s is exact under FMA, and one correction step yields RN(x/s)
-// (Markstein's division theorem).  For |x| < 2^-100 the correction may be
-// off by an ulp, but then x/s + z rounds to the same integer either way.
-__device__ inline float div_rn(float x, float s, float rs) {
-  const float q0 = x * rs;
-  const float r = __builtin_fmaf(-q0, s, x);
-  return __builtin_fmaf(r, rs, q0);
-}
-
 // Row min/max of the current group across the 16 lanes of a row and the
 // resulting grid; lane 0 of the row records it.
 __device__ inline void group_stats(float mn, float mx, float qm, float& s, float& z, float& rs,
@@ -97,200 +87,201 @@ __device__ inline float row_bcast(float v) {
       float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x150 + LJ, 0xF, 0xF, true));
 }
 
-// Column step j = 16*kj + LJ of the sweep for this lane's row (see sweep_kernel).
+// Column step j = 16*kj + LJ of the sweep for this lane's row (see
+// sweep_columns).
+//
+// Every lane of the row quantizes column j itself, from c, the column's
+// current value (the same in all 16 lanes), so no broadcast sits on the
+// dependency chain, which is five operations: t = c/s + z as one fused
+// multiply-add with 1/s, rint, the clamp to [0, qm] (med3), the scaled error
+// e = (c - (q - z) s) / Hinv[j][j] as two fused multiply-adds (the first one,
+// off the chain, of c alone), and the next column's value
+// c' = bn - e Hinv[j][j+1].  bn is column j+1 with every earlier step's
+// update, broadcast from its owner one step earlier.  The owner's register
+// receives the same update, so c' equals the owner's copy bit for bit.
+// Registers kj and kj+1 are updated here (the next broadcasts read them).
+// The later groups' columns take a group's 16 errors in step order
+// elsewhere: register kj+2 at the end of the group (group_tail), registers
+// kj+3.. during the next group's steps (lag: step LJ of group kj applies
+// error LJ of group kj-1, egp, to registers kj+2..), where those multiply-adds
+// fill issue slots the dependency chain leaves free.
 template <int LJ>
-__device__ inline void sweep_step(int kj, int l, float s, float z, float rs, float qm, float rd,
-                                  const float* __restrict__ urow, float (&w)[CPL],
-                                  float (&u)[CPL], float (&qc)[CPL], float (&ev)[CPL]) {
-  // next step's Hinv row segment, off the dependency chain
-  float un[CPL];
-  if (LJ + 1 < RL) {
+__device__ inline void sweep_step(int kj, int l, float s, float z, float rs, float qm,
+                                  const float* __restrict__ urow, const float* __restrict__ rdg,
+                                  float (&w)[CPL], float& c, float& bn, float& rdj, float& ujn,
+                                  float& u0, float& u1, float (&eg)[RL], float (&qc)[CPL],
+                                  float (&ev)[CPL], bool lag, const float* __restrict__ uprev,
+                                  const float (&egp)[RL]) {
+  constexpr int J1 = LJ + 1;
+  // the previous group's row LJ for the lagged updates
+  float ul[CPL];
 #pragma unroll
-    for (int k = kj; k < CPL; ++k) un[k] = urow[(LJ + 1) * BC + l + RL * k];
-  }
-  const float x = w[kj];
-  const float t = div_rn(x, s, rs) + z;
-  const float q = fminf(fmaxf(rintf(t), 0.f), qm);
-  const float err = __builtin_fmaf(-(q - z), s, x);
-  const float eb = row_bcast<LJ>(err * rd);
+  for (int k = 0; k < CPL; ++k) ul[k] = (lag && k >= kj + 2) ? uprev[LJ * BC + l + RL * k] : 0.f;
+  // the next step's Hinv entries: its row of this lane's columns in
+  // registers kj and kj+1, and the shared 1 / Hinv[j][j] and Hinv[j][j+1]
+  const float* ujn1 = urow + J1 * BC;
+  const float u0n = (J1 < RL) ? ujn1[l + RL * kj] : 0.f;
+  const float u1n = (J1 < RL && kj + 1 < CPL) ? ujn1[l + RL * (kj + 1)] : 0.f;
+  const float rdn = (J1 < RL) ? rdg[J1] : 0.f;
+  const bool nx = J1 < RL && RL * kj + J1 + 1 < BC;  // the next step's U[j+1][j+2] exists
+  const float ujnn = nx ? urow[J1 * BC + RL * kj + J1 + 1] : 0.f;
+  const float srd = s * rdj;
+  const float zsrd = z * srd;
+  const float t = __builtin_fmaf(c, rs, z);
+  const float q = __builtin_amdgcn_fmed3f(rintf(t), 0.f, qm);
+  const float xr = __builtin_fmaf(c, rdj, zsrd);
+  const float eb = __builtin_fmaf(-q, srd, xr);
+  c = __builtin_fmaf(-eb, ujn, bn);
+  eg[LJ] = eb;
   if (l == LJ) {
     qc[kj] = q;
     ev[kj] = eb;
   }
+  w[kj] = __builtin_fmaf(-eb, u0, w[kj]);
+  if (kj + 1 < CPL) w[kj + 1] = __builtin_fmaf(-eb, u1, w[kj + 1]);
+  if (lag) {
 #pragma unroll
-  for (int k = kj; k < CPL; ++k) w[k] = __builtin_fmaf(-eb, u[k], w[k]);
-  if (LJ + 1 < RL) {
-#pragma unroll
-    for (int k = kj; k < CPL; ++k) u[k] = un[k];
+    for (int k = 0; k < CPL; ++k)
+      if (k >= kj + 2) w[k] = __builtin_fmaf(-egp[LJ], ul[k], w[k]);
   }
+  // column j + 2 after this step, for the step after next
+  if constexpr (LJ + 2 < RL)
+    bn = row_bcast<LJ + 2>(w[kj]);
+  else
+    bn = (kj + 1 < CPL) ? row_bcast<LJ + 2 - RL>(w[kj + 1 < CPL ? kj + 1 : kj]) : 0.f;
+  rdj = rdn;
+  ujn = ujnn;
+  u0 = u0n;
+  u1 = u1n;
   __builtin_amdgcn_sched_barrier(0);  // keep steps apart: bounded register pressure
 }
 
 template <int... LJ>
-__device__ inline void sweep_steps(int kj, int l, float s, float z, float rs, float qm, float rd,
-                                   const float* __restrict__ urow, float (&w)[CPL],
-                                   float (&u)[CPL], float (&qc)[CPL], float (&ev)[CPL],
-                                   std::integer_sequence<int, LJ...>) {
-  (sweep_step<LJ>(kj, l, s, z, rs, qm, rd, urow, w, u, qc, ev), ...);
+__device__ inline void sweep_steps(int kj, int l, float s, float z, float rs, float qm,
+                                   const float* __restrict__ urow, const float* __restrict__ rdg,
+                                   float (&w)[CPL], float& c, float& bn, float& rdj, float& ujn,
+                                   float& u0, float& u1, float (&eg)[RL], float (&qc)[CPL],
+                                   float (&ev)[CPL], bool lag, const float* __restrict__ uprev,
+                                   const float (&egp)[RL], std::integer_sequence<int, LJ...>) {
+  (sweep_step<LJ>(kj, l, s, z, rs, qm, urow, rdg, w, c, bn, rdj, ujn, u0, u1, eg, qc, ev, lag,
+                  uprev, egp),
+   ...);
 }
 
-// G: group size when it divides the block (16, 32, 64, 128); G == 0 means the
-// group spans several blocks (groupsize a multiple of 128).
-//
-// Column j = 16*kj + lj lives in register kj of lane lj.  Both loops are
-// unrolled, so every register index and the DPP source lane are compile-time
-// constants.  Steps past the end of a short last block run on zero weights
-// and zero Hinv entries and change nothing.
-// Hinv[r0 + j][i1 + c] for j < nrows, c < nbc (zero elsewhere) as the 16
-// float4 this thread moves into a 128x128 LDS tile (row j at U + 128 j).
-__device__ inline void hinv_tile_load(float4 (&v)[16], const float* __restrict__ Hinv, int64_t cols,
-                                      int64_t r0, int i1, int nbc, int nrows, int tid) {
-  const bool vec = (cols % 4 == 0) && (reinterpret_cast<uintptr_t>(Hinv) % 16 == 0);
+// End of group kj: registers kj+2 .. kmax-1 take the group's 16 errors,
+// w[k] -= sum_j eg[j] Hinv[16 kj + j][16 k + l] in step order (register kj+1
+// was updated step by step; registers kmax.. take them during the next
+// group's steps).  The empty asm statements pin each updated w[k] here:
+// otherwise the compiler defers these updates to the group that first reads
+// w[k] and keeps every earlier group's errors alive until then (hundreds of
+// registers).
+__device__ inline void group_tail(int kj, int kmax, int l, const float* __restrict__ urow,
+                                  float (&w)[CPL], const float (&eg)[RL]) {
+#pragma unroll
+  for (int k = kj + 2; k < CPL; ++k) {
+    if (k >= kmax) break;
+#pragma unroll
+    for (int j = 0; j < RL; ++j) w[k] = __builtin_fmaf(-eg[j], urow[j * BC + l + RL * k], w[k]);
+    asm volatile("" : "+v"(w[k]));
+  }
+}
+
+// Loads of a block's operands are branch-free: each reads from an address
+// clamped into the matrix and the value is masked only where it is consumed.
+// A load under a condition makes the compiler wait for it at the join of the
+// branches, so the loads of a tile would not be in flight together.
+
+// Hinv[r0 + j][c0 + c] for the 16 float4 this thread moves into a 128x128
+// LDS tile (row j at U + 128 j), raw: the row is clamped below r0 + nrows and
+// the column below c0 + nbc (both inside the matrix).  VEC: cols % 4 == 0 and
+// Hinv 16-byte aligned, so nbc % 4 == 0 and each float4 lies wholly inside
+// or wholly outside the block's columns.
+template <bool VEC>
+__device__ inline void hinv_tile_fetch(float4 (&v)[16], const float* __restrict__ Hinv,
+                                       int64_t cols, int64_t r0, int c0, int nbc, int nrows,
+                                       int tid) {
 #pragma unroll
   for (int q = 0; q < 16; ++q) {
     const int e = tid + 256 * q;  // float4 index: row e/32, columns 4*(e%32)..
     const int j = e >> 5, c = (e & 31) * 4;
-    const float* p = Hinv + (r0 + j) * cols + i1 + c;
-    float4 u = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (j < nrows) {
-      if (vec && c + 4 <= nbc) {
-        u = *reinterpret_cast<const float4*>(p);
-      } else {
-        if (c + 0 < nbc) u.x = p[0];
-        if (c + 1 < nbc) u.y = p[1];
-        if (c + 2 < nbc) u.z = p[2];
-        if (c + 3 < nbc) u.w = p[3];
-      }
+    const float* p = Hinv + (r0 + (j < nrows ? j : nrows - 1)) * cols + c0;
+    if constexpr (VEC) {
+      v[q] = *reinterpret_cast<const float4*>(p + (c < nbc ? c : nbc - 4));
+    } else {
+      const int cl = nbc - 1;
+      v[q].x = p[c < cl ? c : cl];
+      v[q].y = p[c + 1 < cl ? c + 1 : cl];
+      v[q].z = p[c + 2 < cl ? c + 2 : cl];
+      v[q].w = p[c + 3 < cl ? c + 3 : cl];
     }
-    v[q] = u;
   }
 }
 
-// The loaded tile into LDS; with TRI (the block's own diagonal tile) the part
-// left of the diagonal is zeroed.
+// The fetched tile into LDS with the entries outside rows < nrows and
+// columns < nbc zeroed.  With TRI (the block's own diagonal tile) the part
+// left of the diagonal is zeroed too, and rdiag[j] = 1 / Hinv[j][j] for the
+// block's columns (0 past the last one) comes from the same registers.
 template <bool TRI>
-__device__ inline void hinv_tile_store(float* __restrict__ U, const float4 (&v)[16], int tid) {
+__device__ inline void hinv_tile_put(float* __restrict__ U, float* __restrict__ rdiag,
+                                     const float4 (&v)[16], int nbc, int nrows, int tid) {
 #pragma unroll
   for (int q = 0; q < 16; ++q) {
     const int e = tid + 256 * q;
     const int j = e >> 5, c = (e & 31) * 4;
+    const bool in = j < nrows;
     float4 u = v[q];
-    if (TRI) {
-      if (c + 0 < j) u.x = 0.f;
-      if (c + 1 < j) u.y = 0.f;
-      if (c + 2 < j) u.z = 0.f;
-      if (c + 3 < j) u.w = 0.f;
-    }
+    u.x = (in && c + 0 < nbc && (!TRI || c + 0 >= j)) ? u.x : 0.f;
+    u.y = (in && c + 1 < nbc && (!TRI || c + 1 >= j)) ? u.y : 0.f;
+    u.z = (in && c + 2 < nbc && (!TRI || c + 2 >= j)) ? u.z : 0.f;
+    u.w = (in && c + 3 < nbc && (!TRI || c + 3 >= j)) ? u.w : 0.f;
     *reinterpret_cast<float4*>(U + j * BC + c) = u;
+    if (TRI) {
+      // selects, not a dynamic index (which would put v in scratch memory)
+      const int dj = j - c;
+      const float d = (dj == 0) ? u.x : (dj == 1) ? u.y : (dj == 2) ? u.z : u.w;
+      if (dj >= 0 && dj < 4) rdiag[j] = (j < nbc) ? 1.f / d : 0.f;
+    }
   }
 }
 
-// Err[row0 + r][c0 + c] for the workgroup's 16 rows x 128 columns: 2 float4
-// per thread (rows past `rows` read as zero).
-__device__ inline void err_slice_load(float4 (&v)[2], const float* __restrict__ Err, int64_t ldk,
-                                      int64_t rows, int64_t row0, int c0, int tid) {
+// Err[row0 + r][c0 + c] for the workgroup's 16 rows x 128 columns, raw (2
+// float4 per thread; rows clamped below `rows`); err_slice_put zeroes the
+// rows past `rows` on the way to LDS.
+__device__ inline void err_slice_fetch(float4 (&v)[2], const float* __restrict__ Err, int64_t ldk,
+                                       int64_t rows, int64_t row0, int c0, int tid) {
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
     const int e = tid + 256 * q;
-    const int r = e >> 5, c = (e & 31) * 4;
-    v[q] = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (row0 + r < rows) v[q] = *reinterpret_cast<const float4*>(Err + (row0 + r) * ldk + c0 + c);
+    const int64_t r = row0 + (e >> 5);
+    const int c = (e & 31) * 4;
+    v[q] = *reinterpret_cast<const float4*>(Err + (r < rows ? r : rows - 1) * ldk + c0 + c);
   }
 }
 
-// p0 < i1 (groups inside blocks only): the blocks [p0, i1) of this
-// superblock were swept by earlier launches and their errors have not yet
-// been applied to this block; the workgroup applies them to its own rows
-// first, W[rows, block] -= Err[rows, p0:i1] Hinv[p0:i1, block], one 128x128
-// Hinv tile at a time through LDS and fp32 MFMA.  This replaces a separate
-// small lazy-update launch per block (the result is the same sum).
-template <int G>
-__global__ __launch_bounds__(256) void sweep_kernel(float* __restrict__ Wk, int64_t ldk,
-                                                    int64_t rows, int64_t cols, int i1, int p0,
-                                                    const float* __restrict__ Hinv, int bits,
-                                                    int groupsize, uint8_t* __restrict__ codes,
-                                                    float* __restrict__ scales,
-                                                    float* __restrict__ zeros,
-                                                    float* __restrict__ Err,
-                                                    float* __restrict__ lpart) {
-  __shared__ __attribute__((aligned(16))) float Ub[BC * BC];  // Hinv block, row j at Ub + 128 j
-  __shared__ float rdiag[BC];
-  __shared__ float lsum[4][BC];
-  __shared__ __attribute__((aligned(16))) float Es[kSweepRows * (BC + 4)];  // Err slice / update tile
+constexpr int EP = BC + 4;  // row pitch of the pending-update tile
 
-  const int tid = threadIdx.x;
+template <typename F, int... K>
+__device__ inline void for_each_group(F& f, std::integer_sequence<int, K...>) {
+  (f(std::integral_constant<int, K>{}), ...);
+}
+
+// Group statistics, the 128 column steps and the outputs of the block at
+// column i1 (nbc columns), for this thread's row: the block's Hinv tile and
+// 1 / diagonal are in LDS (Ub, rdiag), its current weights in w.
+template <int G>
+__device__ __attribute__((always_inline)) inline void sweep_columns(
+    float (&w)[CPL], const float* __restrict__ Ub, const float* __restrict__ rdiag,
+    float (*lsum)[BC], float* __restrict__ Wk, int64_t ldk,
+    int64_t rows, int64_t cols, int i1, int nbc, int bits, int groupsize,
+    uint8_t* __restrict__ codes, float* __restrict__ scales, float* __restrict__ zeros,
+    float* __restrict__ Err, float* __restrict__ lpart, int tid) {
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int l = lane & 15;
   const int rg = lane >> 4;
   const int64_t row = (int64_t)blockIdx.x * kSweepRows + wave * 4 + rg;
   const bool rv = row < rows;
-  const int nbc = (int)((cols - i1) < BC ? (cols - i1) : BC);
   const int64_t ngroups = ceil_div(cols, groupsize);
-
-  float w[CPL];
-#pragma unroll
-  for (int k = 0; k < CPL; ++k) {
-    const int c = l + RL * k;
-    w[k] = (rv && c < nbc) ? Wk[row * ldk + i1 + c] : 0.f;
-  }
-
-  float4 hv[16];  // next Hinv tile on its way to LDS
-  if (G != 0 && p0 < i1) {
-    // pending errors of this superblock: dacc = Err[rows, p0:i1] Hinv[p0:i1, block],
-    // wave w forming columns 32w..32w+31 of the 16 rows; the next tile (and
-    // finally the block's own diagonal tile) is loaded during each tile's MFMAs
-    const int64_t row0 = (int64_t)blockIdx.x * kSweepRows;
-    constexpr int EP = BC + 4;
-    f32x4 dacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-    float4 ev4[2];
-    hinv_tile_load(hv, Hinv, cols, p0, i1, nbc, BC, tid);
-    err_slice_load(ev4, Err, ldk, rows, row0, p0, tid);
-    for (int c0 = p0; c0 < i1; c0 += BC) {
-      hinv_tile_store<false>(Ub, hv, tid);
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const int e = tid + 256 * q;
-        *reinterpret_cast<float4*>(Es + (e >> 5) * EP + (e & 31) * 4) = ev4[q];
-      }
-      __syncthreads();
-      if (c0 + BC < i1) {
-        hinv_tile_load(hv, Hinv, cols, c0 + BC, i1, nbc, BC, tid);
-        err_slice_load(ev4, Err, ldk, rows, row0, c0 + BC, tid);
-      } else {
-        hinv_tile_load(hv, Hinv, cols, i1, i1, nbc, nbc, tid);  // the diagonal tile
-      }
-#pragma unroll 8
-      for (int s4 = 0; s4 < BC / 4; ++s4) {
-        const int kr = 4 * s4 + (lane >> 4);
-        const float a = Es[(lane & 15) * EP + kr];
-#pragma unroll
-        for (int b = 0; b < 2; ++b)
-          dacc[b] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, Ub[kr * BC + 32 * wave + 16 * b + (lane & 15)],
-                                                        dacc[b], 0, 0, 0);
-      }
-      __syncthreads();  // Ub and Es are refilled next
-    }
-    // element i of dacc[b] at lane (n, q) is the update of row 4q + i, column 32w + 16b + n
-    // (the fp32 16x16x4 result layout)
-#pragma unroll
-    for (int b = 0; b < 2; ++b)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        Es[(4 * (lane >> 4) + i) * EP + 32 * wave + 16 * b + (lane & 15)] = dacc[b][i];
-    __syncthreads();
-#pragma unroll
-    for (int k = 0; k < CPL; ++k) w[k] -= Es[(wave * 4 + rg) * EP + l + RL * k];
-  } else {
-    hinv_tile_load(hv, Hinv, cols, i1, i1, nbc, nbc, tid);
-  }
-  // Hinv[i1:i1+128, i1:i1+128] with the part left of the diagonal (and past
-  // the last column) zeroed
-  hinv_tile_store<true>(Ub, hv, tid);
-  for (int j = tid; j < BC; j += 256)
-    rdiag[j] = (j < nbc) ? 1.f / Hinv[(int64_t)(i1 + j) * cols + i1 + j] : 0.f;
-
-  __syncthreads();
 
   const float qm = (float)((1 << bits) - 1);
   float s = 1.f, z = 0.f, rs = 1.f;
@@ -326,10 +317,20 @@ __global__ __launch_bounds__(256) void sweep_kernel(float* __restrict__ Wk, int6
     qc[k] = 0.f;
     ev[k] = 0.f;
   }
-
+  // the row's columns 0 and 1, in every lane of the row
+  float c = row_bcast<0>(w[0]);
+  float bn = row_bcast<1>(w[0]);
+  bool lag = false;  // the previous group's errors still owed to registers kj+2..
+  float egp[RL];
 #pragma unroll
-  for (int kj = 0; kj < CPL; ++kj) {
-    if (RL * kj >= nbc) break;
+  for (int j = 0; j < RL; ++j) egp[j] = 0.f;
+
+  // One group of 16 columns; expanded for kj = 0..7 at compile time (a loop
+  // this large is not unrolled by the compiler), so every register index is
+  // a constant.  Groups past a short last block are skipped.
+  auto group = [&](auto kjc) {
+    constexpr int kj = decltype(kjc)::value;
+    if (RL * kj >= nbc) return;
     if (G != 0 && (RL * kj) % (G > 0 ? G : 1) == 0) {
       // a group starts at column 16*kj: statistics over its current values
       float mn = INFINITY, mx = -INFINITY;
@@ -344,14 +345,28 @@ __global__ __launch_bounds__(256) void sweep_kernel(float* __restrict__ Wk, int6
       group_stats(mn, mx, qm, s, z, rs, rv, l, row, ngroups, (i1 + RL * kj) / groupsize, scales,
                   zeros);
     }
-    // this lane's column 16*kj + l: its 1/Hinv[j][j] (only the owner's is used)
-    const float rd = rdiag[RL * kj + l];
     const float* urow = Ub + (RL * kj) * BC;
-    float u[CPL];
+    const float* rdg = rdiag + RL * kj;
+    // the group's first step: 1 / Hinv[j][j], Hinv[j][j+1] and this lane's
+    // entries of row j in registers kj and kj+1
+    float rdj = rdg[0];
+    float ujn = urow[RL * kj + 1];
+    float u0 = urow[l + RL * kj];
+    float u1 = (kj + 1 < CPL) ? urow[l + RL * (kj + 1)] : 0.f;
+    float eg[RL];
+    sweep_steps(kj, l, s, z, rs, qm, urow, rdg, w, c, bn, rdj, ujn, u0, u1, eg, qc, ev, lag,
+                urow - RL * BC, egp, std::make_integer_sequence<int, RL>{});
+    // The next group's statistics read registers kj+1 .. kj+G/16: with more
+    // than two of them (G >= 64 and a group starting there) every update is
+    // applied now; otherwise registers kj+3.. take this group's errors during
+    // the next group's steps.
+    const bool flush = G >= 64 && (RL * (kj + 1)) % (G > 0 ? G : 1) == 0;
+    group_tail(kj, flush ? CPL : kj + 3, l, urow, w, eg);
+    lag = !flush;
 #pragma unroll
-    for (int k = kj; k < CPL; ++k) u[k] = urow[l + RL * k];
-    sweep_steps(kj, l, s, z, rs, qm, rd, urow, w, u, qc, ev, std::make_integer_sequence<int, RL>{});
-  }
+    for (int j = 0; j < RL; ++j) egp[j] = eg[j];
+  };
+  for_each_group(group, std::make_integer_sequence<int, CPL>{});
 
   // outputs
 #pragma unroll
@@ -375,6 +390,122 @@ __global__ __launch_bounds__(256) void sweep_kernel(float* __restrict__ Wk, int6
     const float tot = (lsum[0][tid] + lsum[1][tid]) + (lsum[2][tid] + lsum[3][tid]);
     if (tid < nbc) lpart[(int64_t)blockIdx.x * ldk + i1 + tid] = 0.5f * tot;
   }
+}
+
+// Pending errors of the superblock for one block: dacc += E Hinv[c0 block,
+// block] for the Hinv tile in Ub and the 16 x 128 error slice E (row pitch
+// ep), wave w forming columns 32w..32w+31 of the 16 rows.  Element i of
+// dacc[b] at lane (n, q) is row 4q + i, column 32w + 16b + n (the fp32
+// 16x16x4 result layout).
+__device__ inline void pending_tile_mma(const float* __restrict__ E, int ep,
+                                        const float* __restrict__ Ub, f32x4 (&dacc)[2], int lane,
+                                        int wave) {
+#pragma unroll 8
+  for (int s4 = 0; s4 < BC / 4; ++s4) {
+    const int kr = 4 * s4 + (lane >> 4);
+    const float a = E[(lane & 15) * ep + kr];
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+      dacc[b] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, Ub[kr * BC + 32 * wave + 16 * b + (lane & 15)],
+                                                    dacc[b], 0, 0, 0);
+  }
+}
+
+// w -= the pending update in dacc, through the tile Es.
+__device__ inline void apply_pending(float (&w)[CPL], const f32x4 (&dacc)[2], float* __restrict__ Es,
+                                     int lane, int wave, int rg, int l) {
+#pragma unroll
+  for (int b = 0; b < 2; ++b)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      Es[(4 * (lane >> 4) + i) * EP + 32 * wave + 16 * b + (lane & 15)] = dacc[b][i];
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < CPL; ++k) w[k] -= Es[(wave * 4 + rg) * EP + l + RL * k];
+}
+
+// One 128-column block at column i1 for the workgroup's 16 rows, one launch
+// per block (groups spanning blocks, G == 0; any group size works).  p0 < i1
+// (groups inside blocks only): the blocks [p0, i1) of this superblock were
+// swept by earlier launches and their errors have not yet been applied to
+// this block; the workgroup applies them to its own rows first,
+// W[rows, block] -= Err[rows, p0:i1] Hinv[p0:i1, block], one 128x128 Hinv
+// tile at a time through LDS and fp32 MFMA.
+template <int G, bool VEC>
+__global__ __launch_bounds__(256) void sweep_kernel(float* __restrict__ Wk, int64_t ldk,
+                                                    int64_t rows, int64_t cols, int i1, int p0,
+                                                    const float* __restrict__ Hinv, int bits,
+                                                    int groupsize, uint8_t* __restrict__ codes,
+                                                    float* __restrict__ scales,
+                                                    float* __restrict__ zeros,
+                                                    float* __restrict__ Err,
+                                                    float* __restrict__ lpart) {
+  __shared__ __attribute__((aligned(16))) float Ub[BC * BC];  // Hinv block, row j at Ub + 128 j
+  __shared__ float rdiag[BC];
+  __shared__ float lsum[4][BC];
+  __shared__ __attribute__((aligned(16))) float Es[kSweepRows * EP];  // Err slice / update tile
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int l = lane & 15;
+  const int rg = lane >> 4;
+  const int64_t row = (int64_t)blockIdx.x * kSweepRows + wave * 4 + rg;
+  const bool rv = row < rows;
+  const int nbc = (int)((cols - i1) < BC ? (cols - i1) : BC);
+
+  // this thread's weights (raw: row and column clamped), masked below
+  float wr[CPL];
+  {
+    const float* wp = Wk + (rv ? row : rows - 1) * ldk + i1;
+#pragma unroll
+    for (int k = 0; k < CPL; ++k) {
+      const int c = l + RL * k;
+      wr[k] = wp[c < nbc ? c : nbc - 1];
+    }
+  }
+
+  float4 hv[16];  // next Hinv tile on its way to LDS
+  f32x4 dacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+  const bool pending = G != 0 && p0 < i1;
+  if (pending) {
+    // the next tile (and finally the block's own diagonal tile) is loaded
+    // during each tile's MFMAs
+    const int64_t row0 = (int64_t)blockIdx.x * kSweepRows;
+    float4 ev4[2];
+    hinv_tile_fetch<VEC>(hv, Hinv, cols, p0, i1, nbc, BC, tid);
+    err_slice_fetch(ev4, Err, ldk, rows, row0, p0, tid);
+    for (int c0 = p0; c0 < i1; c0 += BC) {
+      hinv_tile_put<false>(Ub, rdiag, hv, nbc, BC, tid);
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int e = tid + 256 * q;
+        *reinterpret_cast<float4*>(Es + (e >> 5) * EP + (e & 31) * 4) =
+            (row0 + (e >> 5) < rows) ? ev4[q] : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+      __syncthreads();
+      if (c0 + BC < i1) {
+        hinv_tile_fetch<VEC>(hv, Hinv, cols, c0 + BC, i1, nbc, BC, tid);
+        err_slice_fetch(ev4, Err, ldk, rows, row0, c0 + BC, tid);
+      } else {
+        hinv_tile_fetch<VEC>(hv, Hinv, cols, i1, i1, nbc, nbc, tid);  // the diagonal tile
+      }
+      pending_tile_mma(Es, EP, Ub, dacc, lane, wave);
+      __syncthreads();  // Ub and Es are refilled next
+    }
+  } else {
+    hinv_tile_fetch<VEC>(hv, Hinv, cols, i1, i1, nbc, nbc, tid);
+  }
+  float w[CPL];
+#pragma unroll
+  for (int k = 0; k < CPL; ++k) w[k] = (rv && l + RL * k < nbc) ? wr[k] : 0.f;
+  if (pending) apply_pending(w, dacc, Es, lane, wave, rg, l);
+  // Hinv[i1:i1+128, i1:i1+128] with the part left of the diagonal (and past
+  // the last column) zeroed, and its 1 / diagonal
+  hinv_tile_put<true>(Ub, rdiag, hv, nbc, nbc, tid);
+  __syncthreads();
+  sweep_columns<G>(w, Ub, rdiag, lsum, Wk, ldk, rows, cols, i1, nbc, bits, groupsize, codes, scales,
+                   zeros, Err, lpart, tid);
 }
 
 // ---------------------------------------------------------------- lazy GEMM
@@ -665,9 +796,14 @@ hipError_t launch_sweep_block(float* Wk, int64_t ldk, int64_t rows, int64_t cols
                               float* scales, float* zeros, float* Err, float* lpart,
                               hipStream_t s) {
   dim3 grid((unsigned)ceil_div(rows, kSweepRows));
+  const bool vec = (cols % 4 == 0) && (reinterpret_cast<uintptr_t>(Hinv) % 16 == 0);
 #define GPTQ_SWEEP(G)                                                                          \
-  hipLaunchKernelGGL(sweep_kernel<G>, grid, dim3(256), 0, s, Wk, ldk, rows, cols, i1, p0,     \
-                     Hinv, bits, groupsize, codes, scales, zeros, Err, lpart)
+  if (vec)                                                                                     \
+    hipLaunchKernelGGL((sweep_kernel<G, true>), grid, dim3(256), 0, s, Wk, ldk, rows, cols,  \
+                       i1, p0, Hinv, bits, groupsize, codes, scales, zeros, Err, lpart);       \
+  else                                                                                         \
+    hipLaunchKernelGGL((sweep_kernel<G, false>), grid, dim3(256), 0, s, Wk, ldk, rows, cols, \
+                       i1, p0, Hinv, bits, groupsize, codes, scales, zeros, Err, lpart)
   switch (groupsize) {
     case 16: GPTQ_SWEEP(16); break;
     case 32: GPTQ_SWEEP(32); break;
