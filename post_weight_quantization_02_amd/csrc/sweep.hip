@@ -16,13 +16,16 @@
 //   * 16 lanes per row, 4 rows per wave.  Lane l holds columns l, l+16, ...,
 //     l+112 of its row in registers.  The 128 column steps are unrolled so
 //     every register index is a compile-time constant.
-//   * Step j: every lane evaluates the quantizer on its register j/16 (only
-//     lane j%16 holds column j), the owner's scaled error is broadcast inside
-//     the 16-lane group, and each lane applies the rank-1 update to the
-//     columns it holds.  Hinv's 128x128 diagonal block is in LDS row by row
-//     (lanes of a row read 16 consecutive floats, the four rows of a wave
-//     the same ones); entries left of the diagonal are zero, which makes the
-//     update of finished columns a no-op.
+//   * Step j: all 16 lanes of a row quantize column j themselves from its
+//     current value (held identically in every lane), so the dependency
+//     chain from one column to the next is five operations with no
+//     cross-lane step on it; the owner's copy of the next column arrives by
+//     DPP broadcast a step earlier (see sweep_step).  Hinv's 128x128
+//     diagonal block is in LDS row by row.
+//   * The columns of later 16-column groups take a group's errors at the
+//     end of the group or during the next group's steps, in step order.
+//   * Operand loads are branch-free (clamped addresses, masks at the point
+//     of use), so a tile's loads are all in flight together.
 //   * Group min/max is a per-lane reduction followed by a 4-step xor shuffle
 //     across the 16 lanes of the row.
 //   * Per-column loss partials are reduced inside the workgroup and written
