@@ -298,7 +298,8 @@ gptq_status gptq_pack_codes(const uint8_t* codes, int64_t rows, int64_t cols, in
  * gptq_dequant_gemm -- y = x W_hat^T, W_hat[r][c] = (code - zero[r][g]) *
  * scale[r][g] with g = g_idx[c] if g_idx is given (act-order), else
  * c / groupsize.  Written for decode (a few tokens): the weights are read
- * once per pass of up to 4 tokens.
+ * once per pass of up to 4 tokens, or of up to 32 tokens on the MFMA path
+ * below.
  *
  *   x          m x cols fp16, row t at x + t*ldx (ldx >= cols); m >= 0
  *              (0 is a no-op, and x and y may then be NULL).
@@ -313,7 +314,14 @@ gptq_status gptq_pack_codes(const uint8_t* codes, int64_t rows, int64_t cols, in
  *   of x are added up and the run contributes s * (sum x q - z * sum x);
  *   otherwise W_hat is formed in fp32 and x * W_hat summed.  Every output's
  *   error is at most F * 2^-24 * sum_c |x_c| (|q_c| + |z|) s with
- *   F = max(ceil(words / 64) * K, 4K + ceil(words / 256)) + 8.
+ *   F = max(ceil(words / 64) * K, 4K + ceil(words / 256)) + 8.  MFMA path
+ *   (m >= 2, 4 bits, no g_idx, cols % 128 == 0, groupsize a multiple of 128
+ *   or >= cols, x and packed 16-byte aligned, ldx % 8 == 0): per 128-column
+ *   chunk, fp16 MFMAs with fp32 accumulation add the exact products x * q
+ *   and the sum of x, and the chunk contributes s * (sum x q - z * sum x);
+ *   F = 128 + ceil(cols / 512) + 8, assuming each MFMA adds its 32
+ *   products and its accumulator no less accurately than sequential fp32
+ *   additions.
  *   Asynchronous.
  */
 gptq_status gptq_dequant_gemm(const void* x, int64_t m, int64_t cols, int64_t ldx,

@@ -20,7 +20,9 @@
 // with one 16-byte load (prefetched a batch ahead with the groups' scales and
 // zeros), sums x * code per run -- for 4 bits two codes per v_dot2_f32_f16 --
 // and applies scale and zero once per run.  The 64 lane sums of every output
-// are added by lane shuffles.
+// are added by lane shuffles.  For 2 to 32 tokens with 4-bit codes in groups
+// of a multiple of 128 columns, the MFMA kernel reads each packed word once
+// for all of the pass's tokens (see dequant_gemm_mfma_kernel).
 #include "common.h"
 
 namespace gptq {
@@ -384,6 +386,170 @@ __global__ __launch_bounds__(256) void dequant_gemv_fast_kernel(
   }
 }
 
+// ---------------------------------------------------------------- a few tokens on MFMA
+// y = x W_hat^T for 2..32 tokens in one pass over the weights: 4-bit codes,
+// groups of a multiple of 128 columns (or one group per row), cols % 128 ==
+// 0, x rows and the packed rows 16-byte aligned.
+//
+// A workgroup owns 16 output rows; its four waves split the row's 128-column
+// chunks into quarters and their partial tiles are added in a fixed order at
+// the end.  Per chunk a wave runs v_mfma_f32_16x16x32_f16 with A = x (16
+// tokens) and B = the codes as exact fp16 integers (16 rows): over a chunk,
+// lane group k (lanes 16k..16k+15) takes columns 32k..32k+31, so a lane's B
+// operands are the four words of one 16-byte load and its A operands four
+// 16-byte pieces of an x row.  A second MFMA against all-ones gives sum x over
+// the chunk in the same layout, and the chunk enters the running sums as
+// s * (sum x q - z * sum x), which equals sum x (q - z) s for any fp32 zero.
+// The products are exact in fp32, so the error is the fp32 summation error:
+// at most (128 + ceil(cols / 512) + 8) * 2^-24 * sum_c |x_c| (|q_c| + |z|) s
+// when each MFMA adds its 32 products and the accumulator no less accurately
+// than sequential fp32 additions.  Loads run four chunks ahead.
+constexpr int kMK = 128;   // columns per chunk
+constexpr int kMPf = 4;    // chunks in flight per wave
+
+typedef _Float16 mh2 __attribute__((ext_vector_type(2)));
+
+// The 8 codes of one 4-bit word as exact fp16 integers, in column order:
+// v_perm_b32 puts byte p in both halves (0x00bb00bb), an AND-OR makes the low
+// half 0x6400 | q_lo = 1024 + q_lo and the high half 0x6400 | 16 q_hi = 1024 +
+// 16 q_hi, and one packed fp16 FMA with (1, 1/16) and (-1024, -64) leaves
+// (q_lo, q_hi).
+__device__ inline half8 codes4_f16(uint32_t w) {
+  const mh2 mul = {(_Float16)1.f, (_Float16)0.0625f};
+  const mh2 off = {(_Float16)-1024.f, (_Float16)-64.f};
+  half8 r;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const uint32_t b = __builtin_amdgcn_perm(w, w, (12u << 24) | ((uint32_t)p << 16) | (12u << 8) | p);
+    const uint32_t m = (b & 0x00F0000Fu) | 0x64006400u;
+    const mh2 h = __builtin_bit_cast(mh2, m) * mul + off;
+    r[2 * p] = h[0];
+    r[2 * p + 1] = h[1];
+  }
+  return r;
+}
+
+template <int TT>  // token tiles of 16 per pass
+__global__ __launch_bounds__(256) void dequant_gemm_mfma_kernel(
+    const _Float16* __restrict__ x, int64_t ldx, int m, const uint32_t* __restrict__ packed,
+    int64_t nw, int64_t rows, int64_t cols, const float* __restrict__ scales,
+    const float* __restrict__ zeros, int64_t ngroups, int groupsize, float* __restrict__ y,
+    int64_t ldy) {
+  __shared__ float part[4][TT * 16][17];  // per-wave partial tiles [wave][token][row]
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 15, kg = lane >> 4;
+  const int64_t r0 = (int64_t)blockIdx.x * 16;
+  const int64_t rr = (r0 + n < rows) ? r0 + n : rows - 1;  // this lane's weight row (clamped)
+  const int nch = (int)(cols / kMK);
+  const int cb = (nch * wave) / 4, ce = (nch * (wave + 1)) / 4;  // this wave's chunks
+  const uint32_t* wrow = packed + rr * nw + 4 * kg;
+  const float* srow = scales + rr * ngroups;
+  const float* zrow = zeros + rr * ngroups;
+  const _Float16* xrow[TT];
+#pragma unroll
+  for (int t = 0; t < TT; ++t) xrow[t] = x + (int64_t)min(16 * t + n, m - 1) * ldx + 32 * kg;
+
+  // ring of kMPf chunks in flight: loads are unconditional, from chunk
+  // indices clamped into this wave's range (or the row, for an empty range)
+  uint4 wv[kMPf];
+  half8 xv[kMPf][TT][4];
+  float sv[kMPf], zv[kMPf];
+  auto fetch = [&](int slot, int c) {
+    const int cc = (c < ce) ? c : (ce > cb ? ce - 1 : (cb < nch ? cb : nch - 1));
+    wv[slot] = *reinterpret_cast<const uint4*>(wrow + 16 * cc);
+#pragma unroll
+    for (int t = 0; t < TT; ++t)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        xv[slot][t][q] = *reinterpret_cast<const half8*>(xrow[t] + (int64_t)kMK * cc + 8 * q);
+    const int64_t g = ((int64_t)kMK * cc) / groupsize;
+    sv[slot] = srow[g];
+    zv[slot] = zrow[g];
+  };
+#pragma unroll
+  for (int i = 0; i < kMPf; ++i) fetch(i, cb + i);
+
+  const half8 ones = {(_Float16)1.f, (_Float16)1.f, (_Float16)1.f, (_Float16)1.f,
+                      (_Float16)1.f, (_Float16)1.f, (_Float16)1.f, (_Float16)1.f};
+  f32x4 acc[TT];
+#pragma unroll
+  for (int t = 0; t < TT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int c0 = cb; c0 < ce; c0 += kMPf) {
+#pragma unroll
+    for (int i = 0; i < kMPf; ++i) {
+      const int c = c0 + i;
+      if (c < ce) {
+        const uint32_t wd[4] = {wv[i].x, wv[i].y, wv[i].z, wv[i].w};
+        f32x4 d[TT], dx[TT];
+#pragma unroll
+        for (int t = 0; t < TT; ++t) {
+          d[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+          dx[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const half8 b = codes4_f16(wd[q]);
+#pragma unroll
+          for (int t = 0; t < TT; ++t) {
+            d[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xv[i][t][q], b, d[t], 0, 0, 0);
+            dx[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xv[i][t][q], ones, dx[t], 0, 0, 0);
+          }
+        }
+        const float sc = sv[i], zc = zv[i];
+#pragma unroll
+        for (int t = 0; t < TT; ++t)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            acc[t][e] = __builtin_fmaf(sc, __builtin_fmaf(-zc, dx[t][e], d[t][e]), acc[t][e]);
+      }
+      fetch(i, c + kMPf);
+    }
+  }
+  // element e of acc[t] at lane (n, kg) is token 16 t + 4 kg + e, row r0 + n
+#pragma unroll
+  for (int t = 0; t < TT; ++t)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) part[wave][16 * t + 4 * kg + e][n] = acc[t][e];
+  __syncthreads();
+  for (int o = tid; o < TT * 256; o += 256) {
+    const int tok = o >> 4, rw = o & 15;
+    const float v = (part[0][tok][rw] + part[1][tok][rw]) + (part[2][tok][rw] + part[3][tok][rw]);
+    if (tok < m && r0 + rw < rows) y[(int64_t)tok * ldy + r0 + rw] = v;
+  }
+}
+
+bool dequant_mfma_ok(const _Float16* x, int64_t ldx, int64_t m, const uint32_t* packed, int bits,
+                     int64_t cols, int groupsize, const int* g_idx) {
+  return bits == 4 && m >= 2 && g_idx == nullptr && cols % kMK == 0 &&
+         (groupsize % kMK == 0 || groupsize >= cols) && ldx % 8 == 0 &&
+         (reinterpret_cast<uintptr_t>(x) & 15) == 0 &&
+         (reinterpret_cast<uintptr_t>(packed) & 15) == 0;
+}
+
+hipError_t launch_dequant_mfma(const _Float16* x, int64_t ldx, int64_t m, const uint32_t* packed,
+                               int64_t rows, int64_t cols, const float* scales,
+                               const float* zeros, int groupsize, float* y, int64_t ldy,
+                               hipStream_t s) {
+  const int64_t nw = packed_words(cols, 4);
+  const int64_t ngroups = ceil_div(cols, groupsize);
+  const dim3 grid((unsigned)ceil_div(rows, 16));
+  for (int64_t t0 = 0; t0 < m; t0 += 32) {
+    const int mt = (int)((m - t0 < 32) ? m - t0 : 32);
+    if (mt > 16)
+      hipLaunchKernelGGL(dequant_gemm_mfma_kernel<2>, grid, dim3(256), 0, s, x + t0 * ldx, ldx, mt,
+                         packed, nw, rows, cols, scales, zeros, ngroups, groupsize, y + t0 * ldy,
+                         ldy);
+    else
+      hipLaunchKernelGGL(dequant_gemm_mfma_kernel<1>, grid, dim3(256), 0, s, x + t0 * ldx, ldx, mt,
+                         packed, nw, rows, cols, scales, zeros, ngroups, groupsize, y + t0 * ldy,
+                         ldy);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
 constexpr int64_t kGemvLds = 64 * 1024;  // x staging limit of the fast path
 
 template <int BITS, int R>
@@ -476,6 +642,10 @@ hipError_t launch_dequant_gemv(const _Float16* x, int64_t ldx, int64_t m, const 
                                int64_t ldy, hipStream_t s) {
   const int64_t nw = packed_words(cols, bits);
   const int64_t ngroups = ceil_div(cols, groupsize);
+  // two tokens or more, 4 bits, whole 128-column chunks inside groups: MFMA,
+  // the weights read once per 32 tokens
+  if (dequant_mfma_ok(x, ldx, m, packed, bits, cols, groupsize, g_idx))
+    return launch_dequant_mfma(x, ldx, m, packed, rows, cols, scales, zeros, groupsize, y, ldy, s);
   // fast path: 2, 4 or 8 bits, whole 4-word runs inside groups, no g_idx,
   // 16-byte aligned rows, x of at least one token fits the LDS staging
   if ((bits == 2 || bits == 4 || bits == 8) && g_idx == nullptr && nw % 4 == 0 &&

@@ -11,12 +11,19 @@ added in a tree of depth 6):
   * the 2/4/8-bit one sums the exact products x * q and x over runs of 4K
     columns inside one group and adds s * (sum x q - z sum x) per run, a lane
     over at most ceil(nw / 256) runs.
-Both are within
+  * for two tokens or more with 4-bit codes, groups of whole 128-column
+    chunks and cols % 128 == 0, an MFMA kernel sums the exact products x * q
+    and x over each chunk (128 terms) and adds s * (sum x q - z sum x) per
+    chunk to sums over at most ceil(cols / 512) chunks, four of which are
+    added at the end.
+The first two are within
 
     |y_gpu - y| <= F * 2^-24 * sum_c |x_c| (|q_c| + |z_c|) s_c,
     F = max(ceil(nw / 64) K, 4K + ceil(nw / 256)) + 8,
 
-which bounds either sum since |q - z| <= |q| + |z|.
+which bounds either sum since |q - z| <= |q| + |z|; the MFMA kernel within
+the same form with F = 128 + ceil(cols / 512) + 8 (each MFMA's sum no less
+accurate than sequential fp32 additions).
 """
 import numpy as np
 import pytest
@@ -45,10 +52,18 @@ def _layer(rows, cols, bits, g, seed):
     return r["codes"], r["scales"], r["zeros"]
 
 
+def _mfma_path(m, cols, bits, g, g_idx):
+    gg = cols if g <= 0 else g
+    return bits == 4 and m >= 2 and g_idx is None and cols % 128 == 0 and \
+        (gg % 128 == 0 or gg >= cols)
+
+
 def _bound(x, codes, scales, zeros, cols, bits, g, g_idx=None):
     k = 32 // bits
     nw = -(-cols // k)
     f = max(-(-nw // 64) * k, 4 * k + -(-nw // 256)) + 8
+    if _mfma_path(np.asarray(x).shape[0], cols, bits, g, g_idx):
+        f = 128 + -(-cols // 512) + 8
     if g_idx is None:
         gi = np.arange(cols) // (cols if g <= 0 else g)
     else:
@@ -108,6 +123,21 @@ def test_dequant_gemm_matches_oracle(env, rows, cols, bits, g, m):
     _gemm_case(env, rows, cols, bits, g, m, seed=rows * 7 + cols)
 
 
+@pytest.mark.parametrize("rows,cols,g,m", [
+    (64, 256, 128, 2),         # two tokens: the MFMA path
+    (37, 384, 128, 5),         # ragged rows, three chunks over four waves
+    (50, 1024, 256, 17),       # two token tiles, groups of two chunks
+    (16, 512, 512, 3),         # one group per row
+    (9, 128, 128, 16),         # one chunk: three waves with nothing to do
+    (40, 640, 128, 40),        # two passes (32 + 8 tokens)
+])
+def test_dequant_gemm_mfma_path(env, rows, cols, g, m):
+    """Several tokens at 4 bits: the MFMA kernel, every output within the
+    bound of its arithmetic."""
+    assert _mfma_path(m, cols, 4, g, None)
+    _gemm_case(env, rows, cols, 4, g, m, seed=rows * 5 + cols + m)
+
+
 @pytest.mark.parametrize("bits", [3, 4])
 def test_dequant_gemm_with_g_idx(env, bits):
     """Act-order groups: the group of each column comes from g_idx."""
@@ -115,7 +145,8 @@ def test_dequant_gemm_with_g_idx(env, bits):
 
 
 @pytest.mark.parametrize("rows,cols,m", [(4096, 4096, 1), (4096, 4096, 4), (11008, 4096, 1),
-                                         (4096, 11008, 2)])
+                                         (4096, 11008, 2), (4096, 4096, 16), (11008, 4096, 32),
+                                         (4096, 11008, 16)])
 def test_dequant_gemm_full_layer_shapes(env, rows, cols, m):
     """The Llama-7B-shaped projections of the decode benchmark, int4 g128,
     every output compared."""
