@@ -823,10 +823,19 @@ hipError_t launch_lazy_update(float* Wk, int64_t ldk, int64_t rows, int64_t cols
   if (c1 <= c0 || k1 <= k0) return hipSuccess;
   const int64_t ncol = ceil_div(c1 - c0, LT);
   // big updates: 128x128 tiles; small ones: 32x128 tiles so more CUs take
-  // part, with all of K (at most 128) and the W tile loaded up front
-  if (ncol * ceil_div(rows, 128) >= 512) {
+  // part, with all of K (at most 128) and the W tile loaded up front.  The
+  // far updates (K > 128: a superblock's errors) keep 128x128 or 64x128
+  // tiles while those still give about one workgroup per CU: with K = 512 a
+  // narrow tile's K loop waits on every chunk's loads (measured at attn:
+  // 90, 58, 37 us against 108, 77, 41 us for the last three far updates).
+  const bool far = k1 - k0 > 4 * LK;
+  if (ncol * ceil_div(rows, 128) >= (far ? 256 : 512)) {
     dim3 grid((unsigned)ncol, (unsigned)ceil_div(rows, 128));
     hipLaunchKernelGGL((lazy_kernel<4, false>), grid, dim3(256), 0, s, Wk, ldk, rows, cols, k0, k1,
+                       c0, c1, Err, Hinv);
+  } else if (far && ncol * ceil_div(rows, 64) >= 256) {
+    dim3 grid((unsigned)ncol, (unsigned)ceil_div(rows, 64));
+    hipLaunchKernelGGL((lazy_kernel<2, false>), grid, dim3(256), 0, s, Wk, ldk, rows, cols, k0, k1,
                        c0, c1, Err, Hinv);
   } else {
     dim3 grid((unsigned)ncol, (unsigned)ceil_div(rows, 32));
