@@ -21,7 +21,11 @@
 //     inverse), then one MFMA kernel applies the rank-64 update to the lower
 //     triangle of the trailing matrix; its workgroup 0 updates the next
 //     diagonal block first and factors it while the others finish (lookahead
-//     of one panel).  Large matrices use two levels (see the host code).
+//     of one panel).  Once the trailing matrix is small, solve and update
+//     share one launch (potrf_fused_kernel).  Products with an inverted
+//     diagonal block skip the k-steps its triangle makes zero, and the
+//     diagonal update forms only the lower blocks.  Large matrices use two
+//     levels (see the host code).
 //   * The triangular inverse uses recursive doubling: the 64x64 diagonal
 //     blocks are inverted during the factorization, then each level combines
 //     neighbouring inverted blocks with X21 = -C^-1 (B A^-1), two batched MFMA
@@ -476,6 +480,63 @@ __device__ inline void mma64_f64(const double (*P)[PP], const double (*Q)[PP], i
 }
 
 
+// Row block w (rows 16w..16w+15, all 64 columns) of P X^T, with P and X
+// row-major 64x64 LDS tiles and X lower triangular (an inverted diagonal
+// block): column c of the product only takes k <= c, so column block cb runs
+// the first 16(cb + 1) k-steps.  Each wave issues 40 MFMAs instead of the 64
+// of a full product, and the k-steps left out would only add exact zeros, so
+// every element is the same as the full product's.  o[cb] holds block
+// (w, cb) in the 16x16 fp64 result layout.
+__device__ inline void panel_times_xt(const double (*P)[PP], const double (*X)[PP], f64x4 (&o)[4],
+                                      int lane, int w) {
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb) o[cb] = f64x4{0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+  for (int ks = 0; ks < NB; ks += 4) {
+    const int kr = ks + (lane >> 4);
+    const double a = P[16 * w + (lane & 15)][kr];
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb)
+      if (ks < 16 * (cb + 1))
+        o[cb] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, X[16 * cb + (lane & 15)][kr], o[cb], 0, 0,
+                                                     0);
+  }
+}
+
+// Element i of o[cb] from panel_times_xt: its row and column in the 64x64 tile.
+__device__ inline int strip_row(int w, int lane, int i) { return 16 * w + mfma64_row(lane, i); }
+__device__ inline int strip_col(int cb, int lane) { return 16 * cb + (lane & 15); }
+
+// The lower 16x16 blocks (ra >= cb) of the symmetric 64x64 product P P^T,
+// which is all a diagonal tile's factorization reads: ten blocks, three or
+// two per wave (48 MFMAs at most instead of 64).  Wave w forms block
+// (kSymRa[w][s], kSymCb[w][s]) for s < kSymCnt[w].
+constexpr int kSymCnt[4] = {3, 3, 2, 2};
+constexpr int kSymRa[4][3] = {{3, 3, 3}, {3, 2, 2}, {2, 1, 1}, {1, 0, 0}};
+constexpr int kSymCb[4][3] = {{3, 2, 1}, {0, 2, 1}, {0, 1, 1}, {0, 0, 0}};
+
+__device__ inline void sym_lower_product(const double (*P)[PP], f64x4 (&acc)[3], int lane, int w) {
+#pragma unroll
+  for (int s = 0; s < 3; ++s) acc[s] = f64x4{0.0, 0.0, 0.0, 0.0};
+  const int cnt = kSymCnt[w];
+  int ra[3], cb[3];
+#pragma unroll
+  for (int s = 0; s < 3; ++s) {
+    ra[s] = kSymRa[w][s];
+    cb[s] = kSymCb[w][s];
+  }
+#pragma unroll
+  for (int ks = 0; ks < NB; ks += 4) {
+    const int kr = ks + (lane >> 4);
+#pragma unroll
+    for (int s = 0; s < 3; ++s)
+      if (s < cnt)
+        acc[s] = __builtin_amdgcn_mfma_f64_16x16x4f64(P[16 * ra[s] + (lane & 15)][kr],
+                                                      P[16 * cb[s] + (lane & 15)][kr], acc[s], 0,
+                                                      0, 0);
+  }
+}
+
 // L_ik = A_ik X_kk^T for the 64-row blocks below the diagonal block
 // (one workgroup per block; X_kk = L_kk^-1 from the diagonal kernel).
 __global__ __launch_bounds__(256) void potrf_trsm_kernel(double* __restrict__ A, int lda, int d,
@@ -485,7 +546,6 @@ __global__ __launch_bounds__(256) void potrf_trsm_kernel(double* __restrict__ A,
   __shared__ double Xs[NB][PP];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
   const int kb = min(NB, d - k);
   const int row0 = k + NB * (blockIdx.x + 1);
   const int rb = min(NB, d - row0);
@@ -503,22 +563,108 @@ __global__ __launch_bounds__(256) void potrf_trsm_kernel(double* __restrict__ A,
     Xs[i0 + 4 * q][j] = xv[q];
   }
   __syncthreads();
-  f64x4 acc[2][2];
+  f64x4 o[4];
+  panel_times_xt(Bs, Xs, o, lane, wave);
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
-    for (int b = 0; b < 2; ++b) acc[a][b] = f64x4{0.0, 0.0, 0.0, 0.0};
-  mma64_f64(Bs, Xs, NB, acc, lane, wm, wn);
+    for (int i = 0; i < 4; ++i) {
+      const int r = strip_row(wave, lane, i), c = strip_col(cb, lane);
+      if (r < rb && c < kb) A[(int64_t)(row0 + r) * lda + k + c] = o[cb][i];
+    }
+}
+
+// Lower tile p of the trailing matrix A[t0:, t0:] numbered column by column
+// (column tj holds nt - tj tiles): its top-left corner, and whether it is a
+// diagonal tile.
+__device__ inline bool tile_coords(int p, int nt, int t0, int& r0, int& c0) {
+  int ti = p, tj = 0;
+  while (ti >= nt - tj) {
+    ti -= nt - tj;
+    ++tj;
+  }
+  ti += tj;
+  r0 = t0 + NB * ti;
+  c0 = t0 + NB * tj;
+  return ti == tj;
+}
+
+// Workgroup 0 of a panel step (lookahead): the next diagonal block
+// A(t0, t0), t0 = k + 64, takes the rank-64 update with L(t0, k), the panel
+// block below the diagonal, and is then factored and inverted in place
+// (diag_factor).  Only the lower 16x16 blocks of the update are formed.
+// FUSED: L(t0, k) is formed here from the raw block A(t0, k) and X_kk (the
+// inverted diagonal block at Xk) and also written to Lout (row pitch ldo);
+// otherwise it is read from A, where the panel solve left it.
+template <bool FUSED>
+__device__ __attribute__((always_inline)) inline void lookahead_diag(
+    DiagLds& sh, double* __restrict__ A, int lda, int d, int k, const double* __restrict__ Xk,
+    double* __restrict__ Lout, int ldo, int* flag, int info_offset, double* __restrict__ Xn,
+    int ldxn) {
+  const int t0 = k + NB;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int j = tid & 63, i0 = tid >> 6;
+  const int kb = min(NB, d - t0);
+  const int cnt = kSymCnt[wave];
+  // every load up front: the panel block (rows clamped; rows past the matrix
+  // reach only masked elements), X_kk, and this wave's C blocks
+  double pv[16], xv[16], cs[3][4];
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int q = 0; q < 16; ++q) {
+    const int i = i0 + 4 * q;
+    pv[q] = A[(int64_t)min(t0 + i, d - 1) * lda + k + j];
+    if (FUSED) xv[q] = Xk[(int64_t)i * ldo + j];
+  }
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+  for (int s = 0; s < 3; ++s)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * kSymRa[wave][s] + mfma64_row(lane, i);
+      const int c = 16 * kSymCb[wave][s] + (lane & 15);
+      cs[s][i] = (s < cnt) ? A[(int64_t)min(t0 + r, d - 1) * lda + min(t0 + c, d - 1)] : 0.0;
+    }
+  if (FUSED) {
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      sh.S[i0 + 4 * q][j] = pv[q];
+      sh.Xs[i0 + 4 * q][j] = xv[q];
+    }
+    __syncthreads();
+    f64x4 o[4];
+    panel_times_xt(sh.S, sh.Xs, o, lane, wave);
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int r = 32 * wm + 16 * a + mfma64_row(lane, i);
-        const int c = 32 * wn + 16 * b + (lane & 15);
-        if (r < rb && c < kb) A[(int64_t)(row0 + r) * lda + k + c] = acc[a][b][i];
+        const int r = strip_row(wave, lane, i), c = strip_col(cb, lane);
+        if (r < kb) Lout[(int64_t)r * ldo + c] = o[cb][i];
       }
+    __syncthreads();  // every wave is done with the raw block and X_kk
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sh.Xs[strip_row(wave, lane, i)][strip_col(cb, lane)] = o[cb][i];
+  } else {
+#pragma unroll
+    for (int q = 0; q < 16; ++q) sh.Xs[i0 + 4 * q][j] = pv[q];
+  }
+  __syncthreads();
+  f64x4 acc[3];
+  sym_lower_product(sh.Xs, acc, lane, wave);
+  // the updated block goes to sh.S (rows past the matrix become identity);
+  // diag_factor reads only its lower blocks and the lower triangle of the
+  // diagonal ones
+#pragma unroll
+  for (int s = 0; s < 3; ++s)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * kSymRa[wave][s] + mfma64_row(lane, i);
+      const int c = 16 * kSymCb[wave][s] + (lane & 15);
+      if (s < cnt) sh.S[r][c] = (r < kb && c < kb) ? cs[s][i] - acc[s][i] : ((r == c) ? 1.0 : 0.0);
+    }
+  __syncthreads();
+  diag_factor(sh, A, lda, t0, kb, flag, info_offset, Xn, ldxn);
 }
 
 // Update after panel k inside an outer panel: A_ij -= L_ik L_jk^T for the
@@ -538,6 +684,10 @@ __global__ __launch_bounds__(256, 2) void potrf_update_kernel(double* __restrict
                                                            int info_offset, double* __restrict__ Xn,
                                                            int ldxn) {
   __shared__ DiagLds sh;
+  if (blockIdx.x == 0) {
+    lookahead_diag<false>(sh, A, lda, d, k, nullptr, nullptr, 0, flag, info_offset, Xn, ldxn);
+    return;
+  }
   double (*Ps)[PP] = sh.S;
   double (*Qs)[PP] = sh.Xs;
   const int t0 = k + NB;
@@ -545,18 +695,7 @@ __global__ __launch_bounds__(256, 2) void potrf_update_kernel(double* __restrict
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int j = tid & 63, i0 = tid >> 6;
-  // tile p -> (r0, c0) and whether it is a diagonal tile; column tj holds nt - tj tiles
-  auto coords = [&](int p, int& r0, int& c0) {
-    int ti = p, tj = 0;
-    while (ti >= nt - tj) {
-      ti -= nt - tj;
-      ++tj;
-    }
-    ti += tj;
-    r0 = t0 + NB * ti;
-    c0 = t0 + NB * tj;
-    return ti == tj;
-  };
+  auto coords = [&](int p, int& r0, int& c0) { return tile_coords(p, nt, t0, r0, c0); };
   // Every load is issued, with its row and column clamped into the matrix,
   // so the compiler can count outstanding loads exactly and waits only for
   // the registers each use needs.  Clamped values are not masked: output
@@ -596,7 +735,7 @@ __global__ __launch_bounds__(256, 2) void potrf_update_kernel(double* __restrict
   load(r0, c0, pv, qv, cv);
   stage(pv, qv);
   __syncthreads();
-  if (blockIdx.x != 0) {
+  {
     const int stride = (int)gridDim.x - 1;
     // One tile: issue the next tile's loads (its C tile into cvn), multiply
     // from LDS, write this tile, then stage the next panel blocks.  The two C
@@ -639,29 +778,127 @@ __global__ __launch_bounds__(256, 2) void potrf_update_kernel(double* __restrict
     };
     while (step(cv, cv2) && step(cv2, cv)) {
     }
+  }
+}
+
+// One whole panel step for a small trailing matrix: the panel solve and the
+// rank-64 update in one launch, one lower 64x64 tile of A[t0:, t0:] per
+// workgroup (t0 = k + 64, nt block rows).  Each workgroup forms the two
+// panel blocks it needs, L(i, k) = A(i, k) X_kk^T and L(j, k), from the raw
+// panel and X_kk itself (the triangular product of panel_times_xt, the same
+// values the separate solve stores), then applies A_ij -= L(i, k) L(j, k)^T.
+// The raw panel stays in place while other workgroups read it, so L(i, k) is
+// written to the free block Lp(i, k) of the inverted-diagonal workspace (by
+// the workgroup of tile (i, t0)) and copied into A after the factorization.
+// Workgroup 0 does the lookahead of potrf_update_kernel.  With the solve
+// launch gone, each late step of the serial panel chain is one launch.
+__global__ __launch_bounds__(256, 2) void potrf_fused_kernel(double* __restrict__ A, int lda, int d,
+                                                          int k, int nt, double* __restrict__ Xi,
+                                                          int ldxi, int* flag, int info_offset) {
+  __shared__ DiagLds sh;
+  const int t0 = k + NB;
+  const double* Xk = Xi + (int64_t)k * ldxi + k;
+  double* Lp = Xi + k;  // Lp(i, k) at row i of column block k of the workspace
+  if (blockIdx.x == 0) {
+    lookahead_diag<true>(sh, A, lda, d, k, Xk, Lp + (int64_t)t0 * ldxi, ldxi, flag, info_offset,
+                         Xi + (int64_t)t0 * ldxi + t0, ldxi);
     return;
   }
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int j = tid & 63, i0 = tid >> 6;
+  int r0, c0;
+  const bool diag = tile_coords(blockIdx.x, nt, t0, r0, c0);
+  // every load up front; rows past the matrix are clamped and reach only
+  // elements that are never stored
+  double pa[16], qa[16], xv[16];
+  f64x4 cv[2][2];
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
-#pragma unroll
-    for (int b = 0; b < 2; ++b) acc[a][b] = f64x4{0.0, 0.0, 0.0, 0.0};
-  mma64_f64(Ps, Ps, NB, acc, lane, wm, wn);
-  // workgroup 0: the updated diagonal block of the next panel goes to sh.S
-  // (rows past the matrix become identity), then it is factored in place
-  const int kb = min(NB, d - t0);
-  __syncthreads();  // every wave is done reading the panel tiles
+  for (int q = 0; q < 16; ++q) {
+    const int i = i0 + 4 * q;
+    pa[q] = A[(int64_t)min(r0 + i, d - 1) * lda + k + j];
+    qa[q] = A[(int64_t)min(c0 + i, d - 1) * lda + k + j];
+    xv[q] = Xk[(int64_t)i * ldxi + j];
+  }
 #pragma unroll
   for (int a = 0; a < 2; ++a)
 #pragma unroll
     for (int b = 0; b < 2; ++b)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int r = 32 * wm + 16 * a + mfma64_row(lane, i);
-        const int c = 32 * wn + 16 * b + (lane & 15);
-        sh.S[r][c] = (r < kb && c < kb) ? cv[a][b][i] - acc[a][b][i] : ((r == c) ? 1.0 : 0.0);
+        const int r = r0 + 32 * wm + 16 * a + mfma64_row(lane, i);
+        const int c = c0 + 32 * wn + 16 * b + (lane & 15);
+        cv[a][b][i] = A[(int64_t)min(r, d - 1) * lda + min(c, d - 1)];
       }
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    sh.S[i0 + 4 * q][j] = pa[q];
+    sh.Xs[i0 + 4 * q][j] = xv[q];
+  }
   __syncthreads();
-  diag_factor(sh, A, lda, t0, kb, flag, info_offset, Xn, ldxn);
+  f64x4 oP[4], oQ[4];
+  panel_times_xt(sh.S, sh.Xs, oP, lane, wave);
+  if (!diag) {
+    __syncthreads();  // every wave is done with the raw row block
+#pragma unroll
+    for (int q = 0; q < 16; ++q) sh.S[i0 + 4 * q][j] = qa[q];
+    __syncthreads();
+    panel_times_xt(sh.S, sh.Xs, oQ, lane, wave);
+  }
+  if (c0 == t0) {
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = strip_row(wave, lane, i), c = strip_col(cb, lane);
+        if (r0 + r < d) Lp[(int64_t)(r0 + r) * ldxi + c] = oP[cb][i];
+      }
+  }
+  __syncthreads();  // every wave is done with the raw blocks and X_kk
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = strip_row(wave, lane, i), c = strip_col(cb, lane);
+      sh.S[r][c] = oP[cb][i];
+      if (!diag) sh.Xs[r][c] = oQ[cb][i];
+    }
+  __syncthreads();
+  f64x4 acc[2][2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b) acc[a][b] = f64x4{0.0, 0.0, 0.0, 0.0};
+  mma64_f64(sh.S, diag ? sh.S : sh.Xs, NB, acc, lane, wm, wn);
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = r0 + 32 * wm + 16 * a + mfma64_row(lane, i);
+        const int c = c0 + 32 * wn + 16 * b + (lane & 15);
+        if (r < d && c < d) A[(int64_t)r * lda + c] = cv[a][b][i] - acc[a][b][i];
+      }
+}
+
+// Panels k0, k0 + 64, ... that went through potrf_fused_kernel: their blocks
+// below the diagonal move from the workspace into A.  Workgroup (x, y) copies
+// block row k + 64 (x + 1) of panel k = k0 + 64 y.
+__global__ __launch_bounds__(256) void copy_panels_kernel(double* __restrict__ A, int lda, int d,
+                                                          int k0, const double* __restrict__ Xi,
+                                                          int ldxi) {
+  const int k = k0 + NB * (int)blockIdx.y;
+  const int r0 = k + NB * ((int)blockIdx.x + 1);
+  if (r0 >= d) return;
+  const int rb = min(NB, d - r0);
+  const int j = threadIdx.x & 63, i0 = threadIdx.x >> 6;
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    const int i = i0 + 4 * q;
+    if (i < rb) A[(int64_t)(r0 + i) * lda + k + j] = Xi[(int64_t)(r0 + i) * ldxi + k + j];
+  }
 }
 
 // -------------------------------------------------------------- MFMA GEMM
@@ -1134,6 +1371,25 @@ hipError_t launch_potrf_update(double* A, int lda, int d, int k, int ncol, int* 
   const int kn = k + NB;
   hipLaunchKernelGGL(potrf_update_kernel, dim3((unsigned)grid), dim3(256), 0, s, A, lda, d, k,
                      (int)nt, (int)tiles, flag, info_offset, Xi + (int64_t)kn * ldxi + kn, ldxi);
+  return hipGetLastError();
+}
+
+hipError_t launch_potrf_fused(double* A, int lda, int d, int k, int* flag, int info_offset,
+                              double* Xi, int ldxi, hipStream_t s) {
+  const int64_t nt = ceil_div(d - k - NB, NB);
+  if (nt <= 0) return hipSuccess;
+  const int64_t tiles = nt * (nt + 1) / 2;
+  hipLaunchKernelGGL(potrf_fused_kernel, dim3((unsigned)tiles), dim3(256), 0, s, A, lda, d, k,
+                     (int)nt, Xi, ldxi, flag, info_offset);
+  return hipGetLastError();
+}
+
+hipError_t launch_copy_panels(double* A, int lda, int d, int k0, const double* Xi, int ldxi,
+                              hipStream_t s) {
+  const int64_t below = ceil_div(d - k0, NB) - 1;  // block rows below panel k0 = panels to copy
+  if (below <= 0) return hipSuccess;
+  hipLaunchKernelGGL(copy_panels_kernel, dim3((unsigned)below, (unsigned)below), dim3(256), 0, s, A,
+                     lda, d, k0, Xi, ldxi);
   return hipGetLastError();
 }
 

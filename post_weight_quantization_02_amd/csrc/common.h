@@ -53,6 +53,10 @@ hipError_t launch_potrf_trsm(double* A, int lda, int d, int k, const double* Xi,
 hipError_t launch_potrf_update(double* A, int lda, int d, int k, int ncol, int* flag,
                                int info_offset, double* Xi, int ldxi, hipStream_t s);
 // rank-(k1-k0) update of A[k1:, k1:] by the finished outer block [k0, k1)
+hipError_t launch_potrf_fused(double* A, int lda, int d, int k, int* flag, int info_offset,
+                              double* Xi, int ldxi, hipStream_t s);
+hipError_t launch_copy_panels(double* A, int lda, int d, int k0, const double* Xi, int ldxi,
+                              hipStream_t s);
 hipError_t launch_potrf_outer_update(double* A, int lda, int d, int k0, int k1, hipStream_t s);
 hipError_t launch_trtri_level(const double* L, int ldl, double* X, int ldx, int d, int half,
                               hipStream_t s);

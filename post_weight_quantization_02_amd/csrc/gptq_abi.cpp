@@ -78,14 +78,27 @@ bool group_ok(int g) {
 // kOuterPanel columns are factored panel by panel (updates confined to the
 // outer block), then the trailing matrix takes one rank-kOuterPanel update.
 constexpr int kTwoLevelDim = 8192;
+constexpr int64_t kFusedStepTiles = 512;  // trailing 64x64 tiles below which a step is one launch
 hipError_t potrf(double* A, int d, int* flag, int info_offset, double* Xi, hipStream_t s) {
   hipError_t e = launch_potrf_diag(A, d, d, 0, flag, info_offset, Xi, d, s);
   if (d <= kTwoLevelDim) {
+    // Once the trailing matrix is small the steps are bound by the serial
+    // chain (panel solve, diagonal update, diagonal factorization), so the
+    // solve and the update share one launch; the panels of those steps are
+    // copied into A at the end.
+    int fused_from = d;
     for (int k = 0; k < d && e == hipSuccess; k += kPanel) {
+      const int64_t nt = ceil_div(d - k - kPanel, kPanel);
+      if (nt > 0 && nt * (nt + 1) / 2 <= kFusedStepTiles) {
+        e = launch_potrf_fused(A, d, d, k, flag, info_offset, Xi, d, s);
+        if (fused_from == d) fused_from = k;
+        continue;
+      }
       e = launch_potrf_trsm(A, d, d, k, Xi, d, s);
       if (e == hipSuccess && k + kPanel < d)
         e = launch_potrf_update(A, d, d, k, d, flag, info_offset, Xi, d, s);
     }
+    if (e == hipSuccess && fused_from < d) e = launch_copy_panels(A, d, d, fused_from, Xi, d, s);
     return e;
   }
   for (int K = 0; K < d && e == hipSuccess; K += kOuterPanel) {
