@@ -55,6 +55,14 @@ __device__ inline half8 tr_frag(const _Float16* tile, int kb, int c0, int lane) 
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
+// Partial tiles are stored sub-block by sub-block: the 64x64 sub-block
+// (r / 64, c / 64) of a 256x256 tile is one contiguous run of 4096 floats,
+// row-major, so the reduction streams 16 KB runs.  Diagonal tiles skip their
+// six strictly upper sub-blocks, which nothing reads.
+__device__ inline int64_t part_index(int r, int c) {
+  return (int64_t)(((r >> 6) * 4 + (c >> 6)) * 4096 + (r & 63) * 64 + (c & 63));
+}
+
 // Chunk layout: 32 rows (tokens) x 256 channels = 1024 16-byte pieces per
 // operand block; thread t takes pieces t, t+256, ... (row = piece / 32).
 template <bool VEC>
@@ -162,7 +170,7 @@ __global__ __launch_bounds__(256, 1) void syrk_partial_kernel(const _Float16* __
     buf ^= 1;
   }
 
-  // partial tile, row-major 256x256
+  // partial tile, sub-block by sub-block (part_index)
   float* out = P + ((int64_t)split * ntiles + tile) * ((int64_t)T * T);
 #pragma unroll
   for (int a = 0; a < 8; ++a)
@@ -172,7 +180,7 @@ __global__ __launch_bounds__(256, 1) void syrk_partial_kernel(const _Float16* __
       for (int i = 0; i < 4; ++i) {
         const int r = 128 * wm + 16 * a + 4 * (lane >> 4) + i;
         const int c = 128 * wn + 16 * b + (lane & 15);
-        out[r * T + c] = acc[a][b][i];
+        if (!diag || (r >> 6) >= (c >> 6)) out[part_index(r, c)] = acc[a][b][i];
       }
 }
 
@@ -345,6 +353,7 @@ __global__ __launch_bounds__(256, 1) void syrk_fast_kernel(const _Float16* __res
     fast_body<false>(X, ldx, kbeg, nk, bi * T, bj * T, ring, acc, wave, lane, wm, wn);
 
   float* out = P + ((int64_t)split * ntiles + tile) * ((int64_t)T * T);
+  const bool diag = bi == bj;
 #pragma unroll
   for (int a = 0; a < 8; ++a)
 #pragma unroll
@@ -353,14 +362,14 @@ __global__ __launch_bounds__(256, 1) void syrk_fast_kernel(const _Float16* __res
       for (int i = 0; i < 4; ++i) {
         const int r = 128 * wm + 16 * a + 4 * (lane >> 4) + i;
         const int c = 128 * wn + 16 * b + (lane & 15);
-        out[r * T + c] = acc[a][b][i];
+        if (!diag || (r >> 6) >= (c >> 6)) out[part_index(r, c)] = acc[a][b][i];
       }
 }
 
 // Sum the split partials of one 64x64 sub-block of a lower tile in split
 // order, in fp64 (one rounding to fp32 per element), add alpha * sum into H,
 // and mirror into the upper triangle.  Each thread reads float4 runs of four
-// columns.
+// columns; a pass over 16 rows reads 4 KB of one split contiguously.
 __global__ __launch_bounds__(256) void syrk_reduce_kernel(const float* __restrict__ P, int d,
                                                           int splits, int ntiles, float alpha,
                                                           float* __restrict__ H) {
@@ -382,7 +391,7 @@ __global__ __launch_bounds__(256) void syrk_reduce_kernel(const float* __restric
 #pragma unroll 1
   for (int pass = 0; pass < 4; ++pass) {
     const int rr = 16 * pass + (tid >> 4);
-    const float* src = P + (int64_t)tile * T * T + (int64_t)(64 * qr + rr) * T + 64 * qc + c4;
+    const float* src = P + (int64_t)tile * T * T + part_index(64 * qr + rr, 64 * qc + c4);
     double v0 = 0.0, v1 = 0.0, v2 = 0.0, v3 = 0.0;
     // eight splits' loads in flight at a time; the sums stay in split order
     int sp = 0;
