@@ -653,10 +653,6 @@ def main():
         if args.layer == "block":
             metric = metric.replace("block (", "block with act-order (")
 
-    peaks = None if args.no_peaks else measured_peaks(torch, dev)
-    if peaks:
-        log("measured peaks:", peaks)
-
     job = Job(torch, gq, synth, groups, dev, act_order=args.act_order)
     log(f"warmup {args.warmup}")
     for _ in range(args.warmup):
@@ -672,6 +668,11 @@ def main():
     per = {k: [a.elapsed_time(b) for a, b in v] for k, v in job.ev.items()}
     ph = {k: float(np.sum(v)) / args.steps for k, v in per.items()}  # ms per step per phase
     log("phase ms per step:", {k: round(v, 3) for k, v in ph.items()})
+    # library peaks after the timed steps, so their full-power GEMMs do not
+    # precede the measurement
+    peaks = None if args.no_peaks else measured_peaks(torch, dev)
+    if peaks:
+        log("measured peaks:", peaks)
 
     # algorithmic work per step
     work = dict(syrk=0.0, prep=0.0, lazy=0.0, sweep=0.0)
