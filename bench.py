@@ -27,6 +27,7 @@ import json
 import os
 import re
 import sys
+import threading
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -175,14 +176,18 @@ def cpu_baseline(layer, X, W, budget_s=8.0, act_order=False):
 
 class Job:
     """Device buffers of one workload and its per-step call sequence
-    (post_weight_quantization_02_amd.block.quantize_streams: one H and one
-    Hinv per activation stream, shared by that stream's layers, and one
-    workspace of the largest size for every call)."""
+    (post_weight_quantization_02_amd.block: one H and one Hinv per
+    activation stream, shared by that stream's layers). With several streams
+    (the block) and `concurrent`, the streams run in `lanes` lanes of their
+    own (quantize_streams_concurrent, a workspace per lane); otherwise in
+    order with one workspace of the largest size for every call
+    (quantize_streams)."""
 
-    def __init__(self, torch, gq, synth, groups, dev, act_order=False):
+    def __init__(self, torch, gq, synth, groups, dev, act_order=False, concurrent=False, lanes=2):
         from post_weight_quantization_02_amd import block
         self.torch, self.gq, self.block = torch, gq, block
         self.act_order = act_order
+        self.concurrent = concurrent and len(groups) > 1
         self.groups = []
         self.streams = []
         threads = min(16, len(os.sched_getaffinity(0)))
@@ -205,27 +210,42 @@ class Job:
                 layers=[block.BlockLayer(W=Wd, bits=L.bits, groupsize=L.groupsize,
                                          blocksize=L.blocksize, out=outs)
                         for L, _, Wd, outs in ls]))
-        ws_bytes = block.workspace_bytes(self.streams, act_order)
-        raw = torch.empty(ws_bytes + 256, dtype=torch.uint8, device=dev)
-        off = (-raw.data_ptr()) % 256
-        self.ws = raw[off:off + ws_bytes]
-        self.stream = torch.cuda.current_stream(dev)
+        def ws_of(nbytes):
+            raw = torch.empty(nbytes + 256, dtype=torch.uint8, device=dev)
+            off = (-raw.data_ptr()) % 256
+            return raw[off:off + nbytes]
+
+        if self.concurrent:
+            # one workspace and one device stream per lane of calibration streams
+            self.wss = [ws_of(b) for b in block.lane_workspace_bytes(self.streams, lanes, act_order)]
+            self.dstreams = [torch.cuda.Stream(device=dev) for _ in self.wss]
+        else:
+            self.ws = ws_of(block.workspace_bytes(self.streams, act_order))
         self.ev = {k: [] for k in ("acc", "prep", "quant")}
 
     def step(self, record):
         torch = self.torch
-        open_ev = {}
+        local = threading.local()
 
         def mark(phase, begin):
+            # events on the calling thread's current stream (its calibration
+            # stream's device stream in the concurrent block)
             e = torch.cuda.Event(enable_timing=True)
-            e.record(self.stream)
+            e.record(torch.cuda.current_stream())
+            if not hasattr(local, "open"):
+                local.open = {}
             if begin:
-                open_ev[phase] = e
+                local.open[phase] = e
             else:
-                self.ev[phase].append((open_ev.pop(phase), e))
+                self.ev[phase].append((local.open.pop(phase), e))
 
-        self.block.quantize_streams(self.streams, self.ws, self.act_order,
-                                    mark=mark if record else None)
+        if self.concurrent:
+            self.block.quantize_streams_concurrent(self.streams, self.wss, self.act_order,
+                                                   device_streams=self.dstreams,
+                                                   mark=mark if record else None)
+        else:
+            self.block.quantize_streams(self.streams, self.ws, self.act_order,
+                                        mark=mark if record else None)
 
 
 DECODE_SHAPES = (("q", 4096, 4096), ("k", 4096, 4096), ("v", 4096, 4096), ("o", 4096, 4096),
@@ -581,6 +601,11 @@ def main():
     ap.add_argument("--groupsize", type=int, default=None,
                     help="override the layer's group size (0: one group per row, per-channel)")
     ap.add_argument("--bits", type=int, default=None, help="override the layer's bit width")
+    ap.add_argument("--lanes", type=int, default=2,
+                    help="block: calibration streams run in this many concurrent lanes")
+    ap.add_argument("--serial", action="store_true",
+                    help="block: quantize the calibration streams one after another on one "
+                         "stream (default: each on a stream and host thread of its own)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
     ap.add_argument("--no-peaks", action="store_true", help="skip the library peak probes")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -653,7 +678,8 @@ def main():
         if args.layer == "block":
             metric = metric.replace("block (", "block with act-order (")
 
-    job = Job(torch, gq, synth, groups, dev, act_order=args.act_order)
+    job = Job(torch, gq, synth, groups, dev, act_order=args.act_order,
+              concurrent=not args.serial, lanes=args.lanes)
     log(f"warmup {args.warmup}")
     for _ in range(args.warmup):
         job.step(False)
@@ -728,6 +754,11 @@ def main():
                    "effective_tflops": round(eff_tflops, 2),
                    "roofline_floor_ms": round(floor_ms, 3),
                    "frac_of_floor": round(floor_ms / ms_step, 4),
+                   "streams": (f"concurrent: calibration streams in {len(job.wss)} lanes, each "
+                               "lane on a device stream and host thread of its own; the phases "
+                               "of different lanes overlap, so phase_ms (summed over streams) "
+                               "exceeds ms_per_step and the accumulate calls in the roofline "
+                               "share the GPU" if job.concurrent else "serial"),
                    "peaks_measured": peaks},
         "roofline": {"bound": "mfma",
                      "kernel": "hessian accumulate call: syrk_fast_kernel + syrk_reduce_kernel",

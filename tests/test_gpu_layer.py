@@ -224,11 +224,14 @@ def _block_layers(scale=None):
     return out
 
 
-def _gpu_block(env, layers):
-    """The benchmark's call sequence (block.quantize_streams): streams in
-    order, one H and one Hinv per stream, layers in order q, k, v, o, gate,
-    up, down, one workspace for every call. Returns the host copies of every
-    stream's H and Hinv and every layer's outputs."""
+def _gpu_block(env, layers, concurrent=2):
+    """The benchmark's call sequence: one H and one Hinv per stream, layers
+    in order q, k, v, o, gate, up, down. concurrent > 0: the streams in that
+    many lanes, each on a device stream and host thread of its own with a
+    workspace of its own (block.quantize_streams_concurrent; the bench's
+    default is two lanes); 0: streams in order on one stream with one
+    workspace for every call (block.quantize_streams). Returns the host copies of every stream's H
+    and Hinv and every layer's outputs."""
     torch, gq = env
     from post_weight_quantization_02_amd import block
     streams, Xs = [], []
@@ -248,10 +251,17 @@ def _gpu_block(env, layers):
         st.layers.append(block.BlockLayer(W=Wd, bits=L.bits, groupsize=L.groupsize,
                                           blocksize=L.blocksize,
                                           out=block.allocate_outputs(torch, Wd, L.groupsize)))
-    nb = block.workspace_bytes(streams)
-    raw = torch.empty(nb + 256, dtype=torch.uint8, device="cuda")
-    off = (-raw.data_ptr()) % 256
-    block.quantize_streams(streams, raw[off:off + nb])
+    def ws_of(nb):
+        raw = torch.empty(nb + 256, dtype=torch.uint8, device="cuda")
+        off = (-raw.data_ptr()) % 256
+        return raw[off:off + nb]
+
+    if concurrent:
+        raw = [ws_of(b) for b in block.lane_workspace_bytes(streams, concurrent)]
+        block.quantize_streams_concurrent(streams, raw)
+    else:
+        raw = ws_of(block.workspace_bytes(streams))
+        block.quantize_streams(streams, raw)
     torch.cuda.synchronize()
     res = []
     for (xs, X), st in zip(Xs, streams):
@@ -296,12 +306,15 @@ def _split(layers):
     return groups
 
 
-def test_block_reduced_width_all_rows(env):
+@pytest.mark.parametrize("concurrent", [0, 2, 4], ids=["serial", "two-lanes", "four-lanes"])
+def test_block_reduced_width_all_rows(env, concurrent):
     """The seven-layer block at reduced width (d_model 512, d_ff 1376, 16384
-    tokens per stream; four streams, Hinv shared by q/k/v and by gate/up, one
-    workspace), every row of every layer against the oracle."""
+    tokens per stream; four streams, Hinv shared by q/k/v and by gate/up), in
+    the serial call sequence (one workspace) and with the streams in two and
+    four concurrent lanes (a workspace each), every row of every layer
+    against the oracle."""
     layers = _block_layers((512, 1376, 16384))
-    res = _gpu_block(env, layers)
+    res = _gpu_block(env, layers, concurrent)
     groups = _split(layers)
     assert [len(g) for g in groups] == [3, 1, 2, 1]
     for r, g in zip(res, groups):
