@@ -63,7 +63,7 @@ hipError_t launch_trtri_level(const double* L, int ldl, double* X, int ldx, int 
 hipError_t launch_lauum(const double* X, int ldx, double* S, int lds, int d, hipStream_t s);
 hipError_t launch_store_upper_f32(const double* L2, int ld2, float* Hinv, int d, hipStream_t s);
 constexpr int kPanel = 64;
-constexpr int kOuterPanel = 512;  // columns per outer block of the two-level Cholesky
+constexpr int kOuterPanel = 1024;  // columns per outer block of the two-level Cholesky
 
 // sweep
 // perm != nullptr gathers W's columns into processing order (act-order)
