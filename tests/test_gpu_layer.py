@@ -321,6 +321,39 @@ def test_block_reduced_width_all_rows(env, concurrent):
         _check_stream(r, g)
 
 
+def test_block_lanes_report_a_failed_preparation(env):
+    """A stream whose H is singular (dead channels, no damping) fails its
+    preparation inside its lane: the caller gets the library's NOT_PD error
+    after every lane has ended, and the other lane's layer is still
+    quantized."""
+    torch, gq = env
+    from post_weight_quantization_02_amd import block
+    bad = synth.X_DOWN.scaled(d=256, n=4096)
+    assert synth.dead_channels(bad).size > 0
+    good = synth.X_ATTN.scaled(d=256, n=4096)
+    streams = []
+    for xs, p in ((good, 0.01), (bad, 0.0)):
+        d = xs.d
+        Wd = torch.from_numpy(synth.weights(synth.LAYERS["attn"].w.scaled(rows=64, cols=d))).cuda()
+        streams.append(block.BlockStream(
+            X=torch.from_numpy(synth.activations(xs)).cuda(),
+            H=torch.empty((d, d), dtype=torch.float32, device="cuda"),
+            U=torch.empty((d, d), dtype=torch.float32, device="cuda"),
+            layers=[block.BlockLayer(W=Wd, out=block.allocate_outputs(torch, Wd, 128))],
+            percdamp=p))
+    ws = []
+    for nb in block.lane_workspace_bytes(streams, 2):
+        raw = torch.empty(nb + 256, dtype=torch.uint8, device="cuda")
+        off = (-raw.data_ptr()) % 256
+        ws.append(raw[off:off + nb])
+    streams[0].layers[0].out[0].fill_(255)
+    with pytest.raises(gq.GPTQError) as ei:
+        block.quantize_streams_concurrent(streams, ws)
+    assert ei.value.status == gq.GPTQ_ERR_NOT_PD
+    torch.cuda.synchronize()
+    assert int(streams[0].layers[0].out[0].max()) <= 15  # the good stream's layer ran
+
+
 @pytest.fixture(scope="module")
 def full_block(env):
     layers = _block_layers()
