@@ -593,7 +593,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
-    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--layer", default="attn",
                     choices=["attn", "mlp_up", "mlp_down", "tiny", "block"])
     ap.add_argument("--act-order", action="store_true",
@@ -694,6 +694,9 @@ def main():
     per = {k: [a.elapsed_time(b) for a, b in v] for k, v in job.ev.items()}
     ph = {k: float(np.sum(v)) / args.steps for k, v in per.items()}  # ms per step per phase
     log("phase ms per step:", {k: round(v, 3) for k, v in ph.items()})
+    if len(job.groups) == 1:
+        log("ms per timed step (phase sum):",
+            [round(sum(per[k][i] for k in per), 3) for i in range(args.steps)])
     # library peaks after the timed steps, so their full-power GEMMs do not
     # precede the measurement
     peaks = None if args.no_peaks else measured_peaks(torch, dev)
