@@ -147,6 +147,8 @@ def quantize_streams_concurrent(streams: List[BlockStream], workspaces, act_orde
     caller = torch.cuda.current_stream(dev)
     if device_streams is None:
         device_streams = [torch.cuda.Stream(device=dev) for _ in lanes]
+    if len(device_streams) < len(lanes):
+        raise ValueError("one device stream per lane is needed")
     ready = torch.cuda.Event()
     ready.record(caller)
     errors = [None] * len(lanes)

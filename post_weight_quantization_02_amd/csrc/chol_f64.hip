@@ -170,38 +170,44 @@ __device__ inline double lane_gather(double v, int addr) {
   return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
 }
 
-// Step J of the in-wave 16x16 Cholesky and inverse (see factor16).  gaddr[q]
-// is the byte address of lane (m, q) for ds_bpermute.
-template <int J>
-__device__ inline void factor16_step(double (&a)[4], double (&y)[4], double& ysc, int& bad,
-                                     int m, int g, const int (&gaddr)[4]) {
-  constexpr int QJ = J & 3, IJ = J >> 2;
-  const double c = lane_gather(a[IJ], gaddr[QJ]);    // A[m][J], from lane group QJ
-  const double p = lane_value<J + 16 * QJ>(a[IJ]);   // pivot A[J][J]
-  bad = (p > 0.0) ? bad : min(bad, J);
-  const double rs = rsqrt_f64(p);                     // for L and the inverse, off the chain
-  const double r2 = (m > J) ? rcp_f64(p) : 0.0;
-  const double t = c * r2;                            // multiplier of row J for rows below it
+// Step J = 4Q + K of the in-wave 16x16 Cholesky and inverse (see factor16).
+// c[k] holds A[m][4Q + k] in every lane of row m; row J of anything held in
+// every lane group comes from lane J of the group (DPP row_newbcast).
+template <int Q, int K>
+__device__ inline void factor16_step(double (&a)[4], double (&y)[4], double (&c)[4], int m) {
+  constexpr int J = 4 * Q + K;
+  const double p = row_bcast<J>(c[K]);                // pivot A[J][J]
+  // multiplier of row J for the rows below it, and exactly 0 for the others
+  // (also when A[m][J] is not finite), so no step after a row's own touches
+  // its diagonal entry
+  const double t = (m > J) ? c[K] * rcp_f64(p) : 0.0;
   // rows below J: the columns past J get the right-looking update with row J
 #pragma unroll
-  for (int i = IJ; i < 4; ++i) {
-    if (i == IJ && QJ == 3) continue;                 // element IJ holds no column past J
-    double b = row_bcast<J>(a[i]);                    // A[J][g + 4i]
-    if (i == IJ) b = (g > QJ) ? b : 0.0;
-    a[i] = __builtin_fma(-t, b, a[i]);
-  }
-  if (g == QJ) a[IJ] = c * rs;                        // column J of L (L[J][J] = p / sqrt(p))
+  for (int k = K + 1; k < 4; ++k) c[k] = __builtin_fma(-t, row_bcast<J>(c[k]), c[k]);
+#pragma unroll
+  for (int i = Q + 1; i < 4; ++i) a[i] = __builtin_fma(-t, row_bcast<J>(a[i]), a[i]);
   // forward substitution L Y = I: rows below J lose t times row J of Y
 #pragma unroll
-  for (int i = 0; i <= IJ; ++i) y[i] = __builtin_fma(-t, row_bcast<J>(y[i]), y[i]);
-  if (m == J) ysc = rs;
+  for (int i = 0; i <= Q; ++i) y[i] = __builtin_fma(-t, row_bcast<J>(y[i]), y[i]);
 }
 
-template <int... J>
-__device__ inline void factor16_steps(double (&a)[4], double (&y)[4], double& ysc, int& bad, int m,
-                                      int g, const int (&gaddr)[4],
-                                      std::integer_sequence<int, J...>) {
-  (factor16_step<J>(a, y, ysc, bad, m, g, gaddr), ...);
+// Columns 4Q .. 4Q+3 (element Q of lane groups 0..3): gathered once into
+// every lane of each row, stepped there, and handed back to their owners.
+template <int Q>
+__device__ inline void factor16_quad(double (&a)[4], double (&y)[4], int m, int g,
+                                     const int (&gaddr)[4]) {
+  double c[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) c[k] = lane_gather(a[Q], gaddr[k]);
+  factor16_step<Q, 0>(a, y, c, m);
+  factor16_step<Q, 1>(a, y, c, m);
+  factor16_step<Q, 2>(a, y, c, m);
+  factor16_step<Q, 3>(a, y, c, m);
+  double v = c[0];
+  v = (g == 1) ? c[1] : v;
+  v = (g == 2) ? c[2] : v;
+  v = (g == 3) ? c[3] : v;
+  a[Q] = v;
 }
 
 // Cholesky factor and inverse of one symmetric 16x16 block held by a single
@@ -210,25 +216,44 @@ __device__ inline void factor16_steps(double (&a)[4], double (&y)[4], double& ys
 // (ds_bpermute) and row j from lane j of each group (DPP row_newbcast),
 // applies the right-looking update a[i][l] -= (a[i][j] / p) a[j][l] to the
 // columns past j, and the forward substitution of L Y = I: rows below j lose
-// (L[i][j] / L[j][j]) times row j of Y, which is scaled by 1 / L[j][j] at the
-// end.  On return a[] holds L (entries above the diagonal are meaningless)
-// and y[] holds L^-1 (exact zeros above the diagonal).  The first pivot that
-// is not > 0 (or NaN) is reported through atomicMin(flag, info_base + j + 1)
-// when `report` is set.
+// (L[i][j] / L[j][j]) times row j of Y.  Nothing a step does depends on
+// 1 / sqrt(p), so the scalings by it wait for the end: a column is final
+// once its step has passed (later steps change only columns past theirs, and
+// its diagonal entry is its pivot), so column j of L is that column times
+// 1 / sqrt(p_j), and row i of L^-1 is row i of Y times 1 / sqrt(p_i).  On
+// return a[] holds L (entries above the diagonal are meaningless) and y[]
+// holds L^-1 (exact zeros above the diagonal).  The first pivot that is not
+// > 0 (or NaN) is reported through atomicMin(flag, info_base + j + 1) when
+// `report` is set.
 __device__ __attribute__((always_inline)) inline void factor16(double (&a)[4], double (&y)[4],
                                                                int m, int g, int* flag,
                                                                int info_base, bool report) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) y[i] = (g + 4 * i == m) ? 1.0 : 0.0;
-  double ysc = 1.0;
-  int bad = 16;
   int gaddr[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) gaddr[q] = (m + 16 * q) * 4;
-  factor16_steps(a, y, ysc, bad, m, g, gaddr, std::make_integer_sequence<int, 16>{});
+  factor16_quad<0>(a, y, m, g, gaddr);
+  factor16_quad<1>(a, y, m, g, gaddr);
+  factor16_quad<2>(a, y, m, g, gaddr);
+  factor16_quad<3>(a, y, m, g, gaddr);
+  // pivot of row m: the diagonal entry, element m / 4 of lane (m, m % 4)
+  const int im = m >> 2;
+  double own = a[0];
+  own = (im == 1) ? a[1] : own;
+  own = (im == 2) ? a[2] : own;
+  own = (im == 3) ? a[3] : own;
+  const double pm = lane_gather(own, (m + 16 * (m & 3)) * 4);
+  const double ysc = rsqrt_f64(pm);
 #pragma unroll
   for (int i = 0; i < 4; ++i) y[i] *= ysc;
-  if (report && bad < 16 && (threadIdx.x & 63) == 0) atomicMin(flag, info_base + bad + 1);
+  // pivot of column g + 4i: element i of lane (g + 4i, g)
+#pragma unroll
+  for (int i = 0; i < 4; ++i) a[i] *= rsqrt_f64(lane_gather(a[i], (g + 4 * i + 16 * g) * 4));
+  // lanes 0..15 are rows 0..15 of lane group 0
+  const uint64_t badm = __builtin_amdgcn_ballot_w64(g == 0 && !(pm > 0.0));
+  if (report && badm != 0 && (threadIdx.x & 63) == 0)
+    atomicMin(flag, info_base + __builtin_ctzll(badm) + 1);
 }
 
 // LDS of the diagonal-block factorization; the trailing update reuses S and
@@ -286,9 +311,8 @@ __device__ inline void t_accum(const double (*S)[PP], const double (*Xs)[PP], in
     t = __builtin_amdgcn_mfma_f64_16x16x4f64(l[s], Xs[16 * K + g + 4 * s][16 * Jp + m], t, 0, 0, 0);
 }
 
-// X_JJ' = -X_JJ T, to Xs and to global Xd (rows and columns below kb).
-__device__ inline void x_block(double (*Xs)[PP], int J, int Jp, int m, int g, const f64x4& t,
-                               double* __restrict__ Xd, int ldxd, int kb) {
+// X_JJ' = -X_JJ T, to Xs.
+__device__ inline void x_block(double (*Xs)[PP], int J, int Jp, int m, int g, const f64x4& t) {
   double x[4];
   load_cs<false>(Xs, J, J, m, g, x);
   f64x4 r = {0.0, 0.0, 0.0, 0.0};
@@ -298,30 +322,13 @@ __device__ inline void x_block(double (*Xs)[PP], int J, int Jp, int m, int g, co
   for (int i = 0; i < 4; ++i) {
     const int row = 16 * J + g + 4 * i, col = 16 * Jp + m;
     Xs[row][col] = r[i];
-    if (row < kb && col < kb) Xd[(int64_t)row * ldxd + col] = r[i];
-  }
-}
-
-// Global store of block (I, K) in CS layout, rows and columns below kb (and
-// on or below the diagonal with LOWER).
-template <bool LOWER>
-__device__ inline void store_block_global(double* __restrict__ G, int64_t ld, int I, int K, int m,
-                                          int g, const double (&v)[4], int kb) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = 16 * I + m, col = 16 * K + g + 4 * i;
-    if (row < kb && col < kb && (!LOWER || col <= row)) G[(int64_t)row * ld + col] = v[i];
   }
 }
 
 struct DiagCtx {
   double (*S)[PP];
   double (*Xs)[PP];
-  double* Ak;   // A[k.., k..]
-  int lda;
-  double* Xd;
-  int ldxd;
-  int kb, w, m, g;
+  int w, m, g;
   int* flag;
   int info_base;  // info_offset + k
 };
@@ -335,8 +342,7 @@ __device__ __attribute__((always_inline)) inline void diag_phase(const DiagCtx& 
     double y[4];
     factor16(row[J], y, m, g, cx.flag, cx.info_base + 16 * J, true);
     store_cs(cx.Xs, J, J, m, g, y);
-    store_block_global<true>(cx.Ak, cx.lda, J, J, m, g, row[J], cx.kb);
-    store_block_global<false>(cx.Xd, cx.ldxd, J, J, m, g, y, cx.kb);
+    store_cs(cx.S, J, J, m, g, row[J]);
   }
   __syncthreads();  // X_JJ published
   if (w > J) {
@@ -344,14 +350,13 @@ __device__ __attribute__((always_inline)) inline void diag_phase(const DiagCtx& 
     load_cs<false>(cx.Xs, J, J, m, g, x);
     l_block(x, row[J], l);
     store_cs(cx.S, w, J, m, g, l);
-    store_block_global<false>(cx.Ak, cx.lda, w, J, m, g, l, cx.kb);
 #pragma unroll
     for (int i = 0; i < 4; ++i) row[J][i] = l[i];
     if constexpr (J + 1 < 4) {
       if (w == J + 1) rank16_update(row[J + 1], l, l);
     }
   } else if (w < J) {
-    x_block(cx.Xs, J, w, m, g, tsum, cx.Xd, cx.ldxd, cx.kb);
+    x_block(cx.Xs, J, w, m, g, tsum);
   }
   if constexpr (J < 3) {
     __syncthreads();  // L_wJ published
@@ -388,9 +393,10 @@ __device__ __attribute__((always_inline)) inline void diag_phase(const DiagCtx& 
 // others apply the remaining rank-16 updates of their rows.  The waves whose
 // rows are done build the blocks of L^-1 below the diagonal,
 // X_JJ' = -X_JJ sum_{K=J'..J-1} L_JK X_KJ', one block column each: the sum
-// before X_JJ is ready, the last product after.  Every block goes to global
-// memory as soon as it is final.  All 16x16 products are
-// v_mfma_f64_16x16x4f64.
+// before X_JJ is ready, the last product after.  Blocks are published in LDS
+// only (L in sh.S, L^-1 in sh.Xs); the whole workgroup copies both tiles to
+// global memory at the end, row by row, so no global store sits on the
+// serial chain of phases.  All 16x16 products are v_mfma_f64_16x16x4f64.
 __device__ __attribute__((always_inline)) inline void diag_factor(DiagLds& sh, double* __restrict__ A, int lda, int k, int kb,
                                    int* flag, int info_offset, double* __restrict__ Xd,
                                    int ldxd) {
@@ -399,12 +405,7 @@ __device__ __attribute__((always_inline)) inline void diag_factor(DiagLds& sh, d
   DiagCtx cx;
   cx.S = sh.S;
   cx.Xs = sh.Xs;
-  cx.Ak = A + (int64_t)k * lda + k;
-  cx.lda = lda;
-  cx.Xd = Xd;
-  cx.ldxd = ldxd;
-  cx.kb = kb;
-  cx.w = tid >> 6;
+  cx.w = __builtin_amdgcn_readfirstlane(tid >> 6);
   cx.m = lane & 15;
   cx.g = lane >> 4;
   cx.flag = flag;
@@ -415,20 +416,26 @@ __device__ __attribute__((always_inline)) inline void diag_factor(DiagLds& sh, d
 #pragma unroll
   for (int K = 0; K < 4; ++K)
     if (K <= cx.w) load_cs<true>(sh.S, cx.w, K, cx.m, cx.g, row[K]);
-  // the blocks of Xd above the block diagonal are zero
-#pragma unroll
-  for (int q = 0; q < 6; ++q) {
-    const int I = q < 3 ? 0 : (q < 5 ? 1 : 2);
-    const int K = q < 3 ? q + 1 : (q < 5 ? q - 1 : 3);
-    const int r = 16 * I + (tid >> 4), c = 16 * K + (tid & 15);
-    if (r < kb && c < kb) Xd[(int64_t)r * ldxd + c] = 0.0;
-  }
   __syncthreads();  // every wave has its row before L blocks overwrite S
   f64x4 tsum = {0.0, 0.0, 0.0, 0.0};
   diag_phase<0>(cx, row, tsum);
   diag_phase<1>(cx, row, tsum);
   diag_phase<2>(cx, row, tsum);
   diag_phase<3>(cx, row, tsum);
+  __syncthreads();  // every block of L and L^-1 is in LDS
+  // rows below kb: L's lower triangle to A, L^-1 to Xd with the blocks above
+  // its block diagonal zero (the diagonal blocks hold exact zeros above the
+  // diagonal); each store instruction writes 64 consecutive elements of a row
+  double* __restrict__ Ak = A + (int64_t)k * lda + k;
+  const int c = tid & 63, r0 = tid >> 6;
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    const int r = r0 + 4 * q;
+    if (r < kb && c < kb) {
+      if (c <= r) Ak[(int64_t)r * lda + c] = sh.S[r][c];
+      Xd[(int64_t)r * ldxd + c] = ((c >> 4) <= (r >> 4)) ? sh.Xs[r][c] : 0.0;
+    }
+  }
 }
 
 // One workgroup factors the 64x64 diagonal block of the panel at column k and
@@ -515,25 +522,30 @@ constexpr int kSymCnt[4] = {3, 3, 2, 2};
 constexpr int kSymRa[4][3] = {{3, 3, 3}, {3, 2, 2}, {2, 1, 1}, {1, 0, 0}};
 constexpr int kSymCb[4][3] = {{3, 2, 1}, {0, 2, 1}, {0, 1, 1}, {0, 0, 0}};
 
-__device__ inline void sym_lower_product(const double (*P)[PP], f64x4 (&acc)[3], int lane, int w) {
+template <int W>
+__device__ inline void sym_lower_product_w(const double (*P)[PP], f64x4 (&acc)[3], int lane) {
 #pragma unroll
   for (int s = 0; s < 3; ++s) acc[s] = f64x4{0.0, 0.0, 0.0, 0.0};
-  const int cnt = kSymCnt[w];
-  int ra[3], cb[3];
-#pragma unroll
-  for (int s = 0; s < 3; ++s) {
-    ra[s] = kSymRa[w][s];
-    cb[s] = kSymCb[w][s];
-  }
 #pragma unroll
   for (int ks = 0; ks < NB; ks += 4) {
     const int kr = ks + (lane >> 4);
 #pragma unroll
-    for (int s = 0; s < 3; ++s)
-      if (s < cnt)
-        acc[s] = __builtin_amdgcn_mfma_f64_16x16x4f64(P[16 * ra[s] + (lane & 15)][kr],
-                                                      P[16 * cb[s] + (lane & 15)][kr], acc[s], 0,
-                                                      0, 0);
+    for (int s = 0; s < kSymCnt[W]; ++s)
+      acc[s] = __builtin_amdgcn_mfma_f64_16x16x4f64(P[16 * kSymRa[W][s] + (lane & 15)][kr],
+                                                    P[16 * kSymCb[W][s] + (lane & 15)][kr], acc[s],
+                                                    0, 0, 0);
+  }
+}
+
+// w must be the same in every lane of the wave.  Each wave's blocks are fixed
+// at compile time, so its operand reads carry no branches and are issued
+// ahead of the products.
+__device__ inline void sym_lower_product(const double (*P)[PP], f64x4 (&acc)[3], int lane, int w) {
+  switch (w) {
+    case 0: sym_lower_product_w<0>(P, acc, lane); break;
+    case 1: sym_lower_product_w<1>(P, acc, lane); break;
+    case 2: sym_lower_product_w<2>(P, acc, lane); break;
+    default: sym_lower_product_w<3>(P, acc, lane); break;
   }
 }
 
@@ -603,7 +615,7 @@ __device__ __attribute__((always_inline)) inline void lookahead_diag(
     int ldxn) {
   const int t0 = k + NB;
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int j = tid & 63, i0 = tid >> 6;
   const int kb = min(NB, d - t0);
   const int cnt = kSymCnt[wave];
