@@ -71,49 +71,49 @@ bool group_ok(int g) {
 // Blocked Cholesky of the lower triangle of A (d x d), in place; the
 // inverted 64x64 diagonal blocks of L land at the diagonal of Xi.
 //
-// Up to kTwoLevelDim: right-looking with 64-column panels, each trailing
-// update (rank 64) also factoring the next diagonal block.  Above it the
-// trailing matrix no longer fits the Infinity Cache and rank-64 updates
-// become HBM-bound, so the factorization is two-level: outer blocks of
-// kOuterPanel columns are factored panel by panel (updates confined to the
-// outer block), then the trailing matrix takes one rank-kOuterPanel update.
-constexpr int kTwoLevelDim = 8192;
+// While more than kSingleLevelTail columns remain after an outer block, the
+// factorization is two-level: the outer block of kOuterPanel columns is
+// factored panel by panel with updates confined to it (the serial chain of
+// 64x64 diagonal blocks with small updates beside it), then the trailing
+// matrix takes one rank-kOuterPanel update (a GEMM, MFMA-bound).  Rank-64
+// updates of a large trailing matrix are bound by moving it (HBM, or the
+// Infinity Cache while it fits), so this moves it once per outer block
+// instead of once per panel.  The last kSingleLevelTail (or fewer) columns
+// are right-looking with 64-column panels, each trailing update (rank 64)
+// also factoring the next diagonal block; once the trailing matrix is small
+// the steps are bound by the serial chain (panel solve, diagonal update,
+// diagonal factorization), so the solve and the update share one launch and
+// the panels of those steps are copied into A at the end.
+constexpr int kSingleLevelTail = 3072;
 constexpr int64_t kFusedStepTiles = 512;  // trailing 64x64 tiles below which a step is one launch
 hipError_t potrf(double* A, int d, int* flag, int info_offset, double* Xi, hipStream_t s) {
   hipError_t e = launch_potrf_diag(A, d, d, 0, flag, info_offset, Xi, d, s);
-  if (d <= kTwoLevelDim) {
-    // Once the trailing matrix is small the steps are bound by the serial
-    // chain (panel solve, diagonal update, diagonal factorization), so the
-    // solve and the update share one launch; the panels of those steps are
-    // copied into A at the end.
-    int fused_from = d;
-    for (int k = 0; k < d && e == hipSuccess; k += kPanel) {
-      const int64_t nt = ceil_div(d - k - kPanel, kPanel);
-      if (nt > 0 && nt * (nt + 1) / 2 <= kFusedStepTiles) {
-        e = launch_potrf_fused(A, d, d, k, flag, info_offset, Xi, d, s);
-        if (fused_from == d) fused_from = k;
-        continue;
-      }
-      e = launch_potrf_trsm(A, d, d, k, Xi, d, s);
-      if (e == hipSuccess && k + kPanel < d)
-        e = launch_potrf_update(A, d, d, k, d, flag, info_offset, Xi, d, s);
-    }
-    if (e == hipSuccess && fused_from < d) e = launch_copy_panels(A, d, d, fused_from, Xi, d, s);
-    return e;
-  }
-  for (int K = 0; K < d && e == hipSuccess; K += kOuterPanel) {
-    const int Kend = (K + kOuterPanel < d) ? K + kOuterPanel : d;
+  int K = 0;
+  while (e == hipSuccess && d - K - kOuterPanel > kSingleLevelTail) {
+    const int Kend = K + kOuterPanel;
     for (int k = K; k < Kend && e == hipSuccess; k += kPanel) {
       e = launch_potrf_trsm(A, d, d, k, Xi, d, s);
       if (e == hipSuccess && k + kPanel < Kend)
         e = launch_potrf_update(A, d, d, k, (int)ceil_div(Kend - k - kPanel, kPanel), flag,
                                 info_offset, Xi, d, s);
     }
-    if (e == hipSuccess && Kend < d) {
-      e = launch_potrf_outer_update(A, d, d, K, Kend, s);
-      if (e == hipSuccess) e = launch_potrf_diag(A, d, d, Kend, flag, info_offset, Xi, d, s);
-    }
+    if (e == hipSuccess) e = launch_potrf_outer_update(A, d, d, K, Kend, s);
+    if (e == hipSuccess) e = launch_potrf_diag(A, d, d, Kend, flag, info_offset, Xi, d, s);
+    K = Kend;
   }
+  int fused_from = d;
+  for (int k = K; k < d && e == hipSuccess; k += kPanel) {
+    const int64_t nt = ceil_div(d - k - kPanel, kPanel);
+    if (nt > 0 && nt * (nt + 1) / 2 <= kFusedStepTiles) {
+      e = launch_potrf_fused(A, d, d, k, flag, info_offset, Xi, d, s);
+      if (fused_from == d) fused_from = k;
+      continue;
+    }
+    e = launch_potrf_trsm(A, d, d, k, Xi, d, s);
+    if (e == hipSuccess && k + kPanel < d)
+      e = launch_potrf_update(A, d, d, k, d, flag, info_offset, Xi, d, s);
+  }
+  if (e == hipSuccess && fused_from < d) e = launch_copy_panels(A, d, d, fused_from, Xi, d, s);
   return e;
 }
 

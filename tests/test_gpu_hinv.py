@@ -99,8 +99,11 @@ def test_upper_triangle_of_H_is_not_read(env):
 
 
 def test_two_level_cholesky_matches_oracle(env):
-    """Dimensions above 8192 take the two-level factorization (outer blocks of
-    512 columns); 8250 is ragged against both the 64- and 512-column blocks.
+    """While more than 3072 columns remain after an outer block, the
+    factorization is two-level (outer blocks of 1024 columns, then a rank-1024
+    update of the trailing matrix); at d = 8250 five outer blocks run and the
+    last 3130 columns take the single-level panels, fused late steps
+    included.  8250 is ragged against both the 64- and 1024-column blocks.
     H = Z Z^T + 0.05 I from a seeded Gaussian Z keeps the oracle fast."""
     d, r = 8250, 384
     rng = np.random.default_rng(8250)
