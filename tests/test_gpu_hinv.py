@@ -89,6 +89,27 @@ def test_nan_reports_pivot_one(env):
     assert ei.value.status == gq.GPTQ_ERR_NOT_PD and ei.value.info == 1
 
 
+@pytest.mark.parametrize("r,c,v", [(6, 4, np.nan), (9, 8, np.nan), (20, 3, np.nan),
+                                   (63, 0, np.inf), (64, 10, np.nan), (130, 129, -np.inf)])
+def test_non_finite_entry_fails_at_its_row(env, r, c, v):
+    """d = 200, H = 2I with one non-finite entry below the diagonal at (r, c):
+    row r's pivot is the first that is not > 0 (the oracle reports r + 1).
+    The rows above r see the entry only through their own upper entries,
+    which must not reach their pivots: cases inside one 16-column block of
+    the in-wave factorization (the same group of four columns, or across
+    two), across 16-column blocks, across 64-column panels, and infinities
+    of either sign."""
+    torch, gq = env
+    H = np.eye(200, dtype=np.float32) * 2.0
+    H[r, c] = v
+    with pytest.raises(oracle.NotPositiveDefinite) as ref:
+        oracle.hinv_upper(H.astype(np.float64), 0.0)
+    with pytest.raises(gq.GPTQError) as ei:
+        _hinv(env, H, 0.0)
+    assert ei.value.status == gq.GPTQ_ERR_NOT_PD
+    assert ei.value.info == ref.value.info == r + 1
+
+
 def test_upper_triangle_of_H_is_not_read(env):
     rng = np.random.default_rng(4)
     A = rng.standard_normal((150, 150))
