@@ -714,24 +714,22 @@ __global__ __launch_bounds__(256, 2) void potrf_update_kernel(double* __restrict
   // element (r, c) reads only P row r, Q row c and C(r, c), so they reach
   // only elements with r >= d or c >= d, which are never stored (the
   // diagonal block of workgroup 0 is masked when it goes to LDS).  A diagonal
-  // tile's Q rows are its P rows; its multiply reads P twice.
+  // tile's Q rows are its P rows; its multiply reads P twice.  Part q of a
+  // tile's loads (q = 0..15): panel rows i0 + 4q of P and Q, and one of this
+  // lane's sixteen C elements.
+  auto load_part = [&](int q, int r0, int c0, double (&pv)[16], double (&qv)[16],
+                       f64x4 (&cv)[2][2]) {
+    const int i = i0 + 4 * q;
+    pv[q] = A[(int64_t)min(r0 + i, d - 1) * lda + k + j];
+    qv[q] = A[(int64_t)min(c0 + i, d - 1) * lda + k + j];
+    const int a = q >> 3, b = (q >> 2) & 1, e = q & 3;
+    const int r = r0 + 32 * wm + 16 * a + mfma64_row(lane, e);
+    const int c = c0 + 32 * wn + 16 * b + (lane & 15);
+    cv[a][b][e] = A[(int64_t)min(r, d - 1) * lda + min(c, d - 1)];
+  };
   auto load = [&](int r0, int c0, double (&pv)[16], double (&qv)[16], f64x4 (&cv)[2][2]) {
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      const int i = i0 + 4 * q;
-      pv[q] = A[(int64_t)min(r0 + i, d - 1) * lda + k + j];
-      qv[q] = A[(int64_t)min(c0 + i, d - 1) * lda + k + j];
-    }
-#pragma unroll
-    for (int a = 0; a < 2; ++a)
-#pragma unroll
-      for (int b = 0; b < 2; ++b)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = r0 + 32 * wm + 16 * a + mfma64_row(lane, i);
-          const int c = c0 + 32 * wn + 16 * b + (lane & 15);
-          cv[a][b][i] = A[(int64_t)min(r, d - 1) * lda + min(c, d - 1)];
-        }
+    for (int q = 0; q < 16; ++q) load_part(q, r0, c0, pv, qv, cv);
   };
   auto stage = [&](const double (&pv)[16], const double (&qv)[16]) {
 #pragma unroll
@@ -749,10 +747,14 @@ __global__ __launch_bounds__(256, 2) void potrf_update_kernel(double* __restrict
   __syncthreads();
   {
     const int stride = (int)gridDim.x - 1;
-    // One tile: issue the next tile's loads (its C tile into cvn), multiply
-    // from LDS, write this tile, then stage the next panel blocks.  The two C
-    // register sets alternate (loop unrolled by two), so no wait covers the
-    // stores just issued.
+    // One tile: multiply from LDS while issuing the next tile's loads (its C
+    // tile into cvn), three per k-step, so the products run while the memory
+    // system takes the loads (issued up front, the loads stalled the wave
+    // until the previous tile's traffic drained, and the products waited
+    // behind them); then write this tile and stage the next panel blocks.
+    // The next k-step's operands are read from LDS while this one's products
+    // run.  The two C register sets alternate (loop unrolled by two), so no
+    // wait covers the stores just issued.
     f64x4 cv2[2][2];
     int p = blockIdx.x;
     auto step = [&](const f64x4 (&cvc)[2][2], f64x4 (&cvn)[2][2]) {
@@ -762,12 +764,39 @@ __global__ __launch_bounds__(256, 2) void potrf_update_kernel(double* __restrict
       // loads and the outstanding-load count stays exact
       int r0n, c0n;
       const bool diagn = coords(more ? pn : p, r0n, c0n);
-      load(r0n, c0n, pv, qv, cvn);
 #pragma unroll
       for (int a = 0; a < 2; ++a)
 #pragma unroll
         for (int b = 0; b < 2; ++b) acc[a][b] = f64x4{0.0, 0.0, 0.0, 0.0};
-      mma64_f64(Ps, diag ? Ps : Qs, NB, acc, lane, wm, wn);
+      const double (*Qt)[PP] = diag ? Ps : Qs;
+      double af[2], bf[2];
+#pragma unroll
+      for (int a = 0; a < 2; ++a) af[a] = Ps[32 * wm + 16 * a + (lane & 15)][lane >> 4];
+#pragma unroll
+      for (int b = 0; b < 2; ++b) bf[b] = Qt[32 * wn + 16 * b + (lane & 15)][lane >> 4];
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        load_part(q, r0n, c0n, pv, qv, cvn);
+        const int kn = 4 * ((q + 1) & 15) + (lane >> 4);
+        double afn[2], bfn[2];
+#pragma unroll
+        for (int a = 0; a < 2; ++a) afn[a] = Ps[32 * wm + 16 * a + (lane & 15)][kn];
+#pragma unroll
+        for (int b = 0; b < 2; ++b) bfn[b] = Qt[32 * wn + 16 * b + (lane & 15)][kn];
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+          for (int b = 0; b < 2; ++b)
+            acc[a][b] = __builtin_amdgcn_mfma_f64_16x16x4f64(af[a], bf[b], acc[a][b], 0, 0, 0);
+        // keep this order: three global loads, four LDS reads, four products
+        __builtin_amdgcn_sched_group_barrier(0x0020, 3, 0);
+        __builtin_amdgcn_sched_group_barrier(0x0100, 4, 0);
+        __builtin_amdgcn_sched_group_barrier(0x0008, 4, 0);
+#pragma unroll
+        for (int a = 0; a < 2; ++a) af[a] = afn[a];
+#pragma unroll
+        for (int b = 0; b < 2; ++b) bf[b] = bfn[b];
+      }
 #pragma unroll
       for (int a = 0; a < 2; ++a)
 #pragma unroll
