@@ -958,13 +958,18 @@ struct GemmDesc {
   int64_t bsa, bsb, bsc;  // per-batch (blockIdx.y) element offsets
 };
 
+// v where c holds, else +0.0, as a select on the bits (no branch).
+__device__ inline double keep_if(bool c, double v) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  return __builtin_bit_cast(double, c ? u : (uint64_t)0);
+}
+
 // Zero an operand element outside its triangle (the K-range of a tile is
 // only tile-aligned, so a triangular operand's other half may be read):
 // tr 1 keeps row >= col, tr 2 keeps row <= col.
 __device__ inline double tri_mask(double v, int tr, int row, int col) {
-  if (tr == 1 && col > row) return 0.0;
-  if (tr == 2 && col < row) return 0.0;
-  return v;
+  const bool zero = (tr == 1 && col > row) || (tr == 2 && col < row);
+  return keep_if(!zero, v);
 }
 
 // Tile of a GEMM launch for workgroup `p`.  When the K range depends on the
@@ -1082,12 +1087,12 @@ __global__ __launch_bounds__(256) void gemm64_f64_kernel(GemmDesc g) {
       const int mm = AK ? (e / GK) : (e % GT);
       const int gm = m0 + mm, gk = kc + kk;
       const bool va = gm < g.M && gk < k1;
-      a_at(buf, mm, kk) = va ? tri_mask(av[q], g.trA, gm, gk) : 0.0;
+      a_at(buf, mm, kk) = keep_if(va, tri_mask(av[q], g.trA, gm, gk));
       const int kb = BN ? (e / GT) : (e % GK);
       const int nn = BN ? (e % GT) : (e / GK);
       const int gn = n0 + nn, gk2 = kc + kb;
       const bool vb = gn < g.N && gk2 < k1;
-      b_at(buf, kb, nn) = vb ? tri_mask(bv[q], g.trB, gk2, gn) : 0.0;
+      b_at(buf, kb, nn) = keep_if(vb, tri_mask(bv[q], g.trB, gk2, gn));
     }
   };
   if (k0 < k1) {
@@ -1099,20 +1104,28 @@ __global__ __launch_bounds__(256) void gemm64_f64_kernel(GemmDesc g) {
   for (int kc = k0; kc < k1; kc += GK) {
     const bool more = kc + GK < k1;
     if (more) gload(kc + GK);
+    // every k-step's operands of the chunk first, then the products (held in
+    // that order by scheduling barriers), so only the first k-step waits for
+    // its LDS reads; read per k-step, each k-step waited for its own
+    constexpr int NS = GK / 4;
+    double af[NS][2], bf[NS][2];
 #pragma unroll
-    for (int ks = 0; ks < GK; ks += 4) {
-      const int kr = ks + (lane >> 4);
-      double af[2], bf[2];
+    for (int s = 0; s < NS; ++s) {
+      const int kr = 4 * s + (lane >> 4);
 #pragma unroll
-      for (int a = 0; a < 2; ++a) af[a] = a_at(buf, 32 * wm + 16 * a + (lane & 15), kr);
+      for (int a = 0; a < 2; ++a) af[s][a] = a_at(buf, 32 * wm + 16 * a + (lane & 15), kr);
 #pragma unroll
-      for (int b = 0; b < 2; ++b) bf[b] = b_at(buf, kr, 32 * wn + 16 * b + (lane & 15));
+      for (int b = 0; b < 2; ++b) bf[s][b] = b_at(buf, kr, 32 * wn + 16 * b + (lane & 15));
+    }
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
 #pragma unroll
       for (int a = 0; a < 2; ++a)
 #pragma unroll
         for (int b = 0; b < 2; ++b)
-          acc[a][b] = __builtin_amdgcn_mfma_f64_16x16x4f64(af[a], bf[b], acc[a][b], 0, 0, 0);
-    }
+          acc[a][b] = __builtin_amdgcn_mfma_f64_16x16x4f64(af[s][a], bf[s][b], acc[a][b], 0, 0, 0);
+    __builtin_amdgcn_sched_group_barrier(0x0100, 4 * NS, 0);
+    __builtin_amdgcn_sched_group_barrier(0x0008, 4 * NS, 0);
     if (more) lstore(buf ^ 1, kc + GK);
     __syncthreads();
     buf ^= 1;
@@ -1245,12 +1258,12 @@ __global__ __launch_bounds__(256, 2) void gemm128_f64_kernel(GemmDesc g) {
       const int mm = AK ? (e / GK) : (e % GT2);
       const int gm = m0 + mm, gk = kc + kk;
       const bool va = gm < g.M && gk < k1;
-      a_at(buf, mm, kk) = va ? tri_mask(av[q], g.trA, gm, gk) : 0.0;
+      a_at(buf, mm, kk) = keep_if(va, tri_mask(av[q], g.trA, gm, gk));
       const int kb = BN ? (e / GT2) : (e % GK);
       const int nn = BN ? (e % GT2) : (e / GK);
       const int gn = n0 + nn, gk2 = kc + kb;
       const bool vb = gn < g.N && gk2 < k1;
-      b_at(buf, kb, nn) = vb ? tri_mask(bv[q], g.trB, gk2, gn) : 0.0;
+      b_at(buf, kb, nn) = keep_if(vb, tri_mask(bv[q], g.trB, gk2, gn));
     }
   };
   if (k0 < k1) {
