@@ -403,14 +403,29 @@ __device__ __attribute__((always_inline)) inline void sweep_columns(
 __device__ inline void pending_tile_mma(const float* __restrict__ E, int ep,
                                         const float* __restrict__ Ub, f32x4 (&dacc)[2], int lane,
                                         int wave) {
+  // the operands of the k-step two ahead are read while this one's products
+  // run (held in that order by scheduling barriers): read right before their
+  // products, every k-step waited for its own LDS reads
+  constexpr int NK = BC / 4;
+  const float* ub = Ub + 32 * wave + (lane & 15) + (lane >> 4) * BC;
+  const float* ea = E + (lane & 15) * ep + (lane >> 4);
+  float a0 = ea[0], a1 = ea[4];
+  float b00 = ub[0], b01 = ub[16], b10 = ub[4 * BC], b11 = ub[4 * BC + 16];
 #pragma unroll 8
-  for (int s4 = 0; s4 < BC / 4; ++s4) {
-    const int kr = 4 * s4 + (lane >> 4);
-    const float a = E[(lane & 15) * ep + kr];
-#pragma unroll
-    for (int b = 0; b < 2; ++b)
-      dacc[b] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, Ub[kr * BC + 32 * wave + 16 * b + (lane & 15)],
-                                                    dacc[b], 0, 0, 0);
+  for (int s4 = 0; s4 < NK; ++s4) {
+    const int kn = 4 * ((s4 + 2) & (NK - 1));
+    const float an = ea[kn];
+    const float bn0 = ub[kn * BC], bn1 = ub[kn * BC + 16];
+    dacc[0] = __builtin_amdgcn_mfma_f32_16x16x4f32(a0, b00, dacc[0], 0, 0, 0);
+    dacc[1] = __builtin_amdgcn_mfma_f32_16x16x4f32(a0, b01, dacc[1], 0, 0, 0);
+    __builtin_amdgcn_sched_group_barrier(0x0100, 3, 0);
+    __builtin_amdgcn_sched_group_barrier(0x0008, 2, 0);
+    a0 = a1;
+    b00 = b10;
+    b01 = b11;
+    a1 = an;
+    b10 = bn0;
+    b11 = bn1;
   }
 }
 
