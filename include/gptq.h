@@ -116,13 +116,16 @@ gptq_status gptq_hessian_accumulate(float* H, int64_t d, const void* X, int64_t 
  * lambda = percdamp * mean(diag H).
  *
  * Damping: "GPTQ, Line by Line", percdamp question (percdamp times the mean
- * Hessian diagonal added to every diagonal entry).  The three-step route
- * (Cholesky factor L of H_d, H_d^{-1} = L^{-T} L^{-1}, then the upper
- * Cholesky factor of H_d^{-1}) follows the Cholesky question of the same page
- * and the cholesky / cholesky_inverse / cholesky(upper) calls of the
- * "GPTQ-style round-to-nearest ..." listing.  Row q of Hinv from column q on
- * is the direction the error of column q is pushed along, and Hinv[q,q] its
- * divisor ("GPTQ: fixing errors as you go", "The OBQ update").
+ * Hessian diagonal added to every diagonal entry).  The result is the factor
+ * the Cholesky question of the same page and the cholesky /
+ * cholesky_inverse / cholesky(upper) calls of the "GPTQ-style
+ * round-to-nearest ..." listing produce: the upper Cholesky factor U of
+ * H_d^{-1} (H_d^{-1} = U^T U).  It is computed as U = J L^{-1} J, where J
+ * reverses the order of rows and columns and L is the lower Cholesky factor
+ * of J H_d J: one factorization and one triangular inverse.  Row q of Hinv
+ * from column q on is the direction the error of column q is pushed along,
+ * and Hinv[q,q] its divisor ("GPTQ: fixing errors as you go", "The OBQ
+ * update").
  *
  *   H         d x d fp32 symmetric (only the lower triangle is read); not
  *             modified.
@@ -131,9 +134,14 @@ gptq_status gptq_hessian_accumulate(float* H, int64_t d, const void* X, int64_t 
  *   info      host int64 out: 0 on success; on GPTQ_ERR_NOT_PD the 1-based
  *             index of the first failing pivot, in [1, d] for the factor of
  *             the damped H and in [d+1, 2d] for the factor of its inverse.
+ *             When the factorization of J H_d J fails, the call repeats the
+ *             page's three steps in forward order (Cholesky factor of H_d,
+ *             its inverse, upper factor of the inverse) to find that pivot;
+ *             if those succeed, their result is returned with GPTQ_OK.
  *             May be NULL.
  *   The factorizations run in fp64 on the device; the result is rounded to
- *   fp32 once.  The call synchronizes `stream` once (to read the pivot flag).
+ *   fp32 once.  The call synchronizes `stream` once (to read the pivot flag),
+ *   twice when the forward route runs.
  *   On GPTQ_ERR_NOT_PD the contents of Hinv are undefined.
  */
 gptq_status gptq_prepare_hinv(const float* H, int64_t d, double percdamp, float* Hinv,

@@ -1,12 +1,21 @@
-// Hinv preparation in fp64: damp, Cholesky, triangular inverse, L^-T L^-1,
-// Cholesky again, and the fp32 upper factor.
+// Hinv preparation in fp64: damp, Cholesky, triangular inverse and the fp32
+// upper factor of the inverse.
 //
-// Route: "GPTQ, Line by Line: Hessian-Based Weight Quantization", percdamp
+// Result: "GPTQ, Line by Line: Hessian-Based Weight Quantization", percdamp
 // question (add percdamp * mean(diag H) to the diagonal) and Cholesky
-// question (factor, form the inverse through the factor, take the upper
-// Cholesky factor of the inverse); the same three calls appear in the
-// gptq_quantize_layer listing of "GPTQ-style round-to-nearest with Hessian
-// weighting".
+// question (the upper Cholesky factor of the damped inverse, which the page
+// forms by factoring, inverting through the factor and factoring the
+// inverse; the same three calls appear in the gptq_quantize_layer listing of
+// "GPTQ-style round-to-nearest with Hessian weighting").
+//
+// Route: with J the reversal permutation and L the lower Cholesky factor of
+// J H_d J, H_d^-1 = J L^-T L^-1 J = M^T M for M = J L^-1 J, which is upper
+// triangular with a positive diagonal, so M is that factor.  One
+// factorization and one triangular inverse (2/3 d^3 flops) replace two
+// factorizations, the inverse and the product L^-T L^-1 (4/3 d^3).  When the
+// factorization of J H_d J fails, the three-step route runs in forward order,
+// so the failing pivot reported is the one of the factor of H_d (or of its
+// inverse).
 //
 // gfx950 design:
 //   * Everything runs in fp64: the sweep's integer decisions are sensitive
@@ -106,27 +115,59 @@ __global__ __launch_bounds__(256) void damp_copy_kernel(const float* __restrict_
   }
 }
 
+// Reversed order: A[i][j] = H[d-1-i][d-1-j] + lambda [i == j] for j <= i,
+// read from H's lower triangle as H[d-1-j][d-1-i].  One workgroup per 64x64
+// tile of A's lower triangle; the source tile is read along H's rows and
+// transposed through LDS, so reads and writes are both coalesced.
+__global__ __launch_bounds__(256) void damp_copy_rev_kernel(const float* __restrict__ H, int d,
+                                                            const double* lam,
+                                                            double* __restrict__ A) {
+  __shared__ float t[64][65];
+  int bi, bj;
+  lower_tile(blockIdx.x, bi, bj);
+  const int i0 = bi * 64, j0 = bj * 64;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  // t[r][c] = H[d-1-(j0+r)][d-1-(i0+c)], the entry that lands at A[i0+c][j0+r]
+  for (int r = ty; r < 64; r += 4) {
+    const int j = j0 + r, i = i0 + tx;
+    t[r][tx] = (i < d && j <= i) ? H[(int64_t)(d - 1 - j) * d + (d - 1 - i)] : 0.f;
+  }
+  __syncthreads();
+  const double l = *lam;
+  for (int r = ty; r < 64; r += 4) {
+    const int i = i0 + r, j = j0 + tx;
+    if (i < d && j <= i) {
+      double v = (double)t[tx][r];
+      if (j == i) v += l;
+      A[(int64_t)i * d + j] = v;
+    }
+  }
+}
+
 // Act-order variant: A = P H P^T + lambda I with (P H P^T)[i][j] =
-// H[perm[i]][perm[j]], lower triangle; H must hold both triangles.  One
-// workgroup per row i; with `stage` row perm[i] of H is first copied to LDS
-// (dynamic, d floats) so the gather reads LDS.  perm entries are clamped into
-// [0, d).
+// H[q[i]][q[j]], lower triangle, q[i] = perm[i] (or perm[d-1-i] with `rev`);
+// H must hold both triangles.  One workgroup per row i; with `stage` row
+// q[i] of H is first copied to LDS (dynamic, d floats) so the gather reads
+// LDS.  perm entries are clamped into [0, d).
 __global__ __launch_bounds__(256) void damp_copy_perm_kernel(const float* __restrict__ H, int d,
                                                              const int* __restrict__ perm,
                                                              const double* lam,
-                                                             double* __restrict__ A, bool stage) {
+                                                             double* __restrict__ A, bool stage,
+                                                             bool rev) {
   extern __shared__ float hrowbuf[];
   const int64_t i = blockIdx.x;
   const double l = *lam;
-  const int64_t pi = min(max(perm[i], 0), d - 1);
-  const float* hrow = H + pi * d;
+  auto q = [&](int64_t k) -> int64_t {
+    return min(max(perm[rev ? d - 1 - k : k], 0), d - 1);
+  };
+  const float* hrow = H + q(i) * d;
   if (stage) {
     for (int64_t j = threadIdx.x; j < d; j += 256) hrowbuf[j] = hrow[j];
     __syncthreads();
     hrow = hrowbuf;
   }
   for (int64_t j = threadIdx.x; j <= i; j += 256) {
-    double v = (double)hrow[min(max(perm[j], 0), d - 1)];
+    double v = (double)hrow[q(j)];
     if (j == i) v += l;
     A[i * d + j] = v;
   }
@@ -1361,6 +1402,16 @@ __global__ __launch_bounds__(256) void store_upper_kernel(const double* __restri
   }
 }
 
+// Hinv[i][j] = X[d-1-i][d-1-j] for j >= i (row d-1-i of the lower
+// triangular X, read backwards), 0 below the diagonal.  One workgroup per row.
+__global__ __launch_bounds__(256) void store_reversed_kernel(const double* __restrict__ X, int ldx,
+                                                             float* __restrict__ Hinv, int d) {
+  const int i = blockIdx.x;
+  const double* xrow = X + (int64_t)(d - 1 - i) * ldx + (d - 1);
+  float* hrow = Hinv + (int64_t)i * d;
+  for (int j = threadIdx.x; j < d; j += 256) hrow[j] = (j >= i) ? (float)xrow[-j] : 0.f;
+}
+
 // Compute units of the current device (cached per device id; concurrent
 // callers may both query and store the same value).
 int device_cus() {
@@ -1378,8 +1429,8 @@ int device_cus() {
 
 }  // namespace
 
-hipError_t launch_damp_to_f64(const float* H, int d, double percdamp, const int* perm, double* A,
-                              int* flag, hipStream_t s) {
+hipError_t launch_damp_to_f64(const float* H, int d, double percdamp, const int* perm, bool reverse,
+                              double* A, int* flag, hipStream_t s) {
   double* lam = reinterpret_cast<double*>(reinterpret_cast<char*>(flag) + 8);
   hipLaunchKernelGGL(damp_lambda_kernel, dim3(1), dim3(256), 0, s, H, d, percdamp, lam, flag);
   hipError_t e = hipGetLastError();
@@ -1388,9 +1439,12 @@ hipError_t launch_damp_to_f64(const float* H, int d, double percdamp, const int*
     const bool stage = (int64_t)d * 4 <= kStageBytes;
     hipLaunchKernelGGL(damp_copy_perm_kernel, dim3((unsigned)d), dim3(256),
                        stage ? (unsigned)d * 4u : 0u, s, H, d, perm, (const double*)lam, A,
-                       stage);
-  }
-  else
+                       stage, reverse);
+  } else if (reverse) {
+    const int64_t nt = ceil_div(d, 64);
+    hipLaunchKernelGGL(damp_copy_rev_kernel, dim3((unsigned)(nt * (nt + 1) / 2)), dim3(256), 0, s,
+                       H, d, (const double*)lam, A);
+  } else
     hipLaunchKernelGGL(damp_copy_kernel, dim3((unsigned)d), dim3(256), 0, s, H, d,
                        (const double*)lam, A);
   return hipGetLastError();
@@ -1520,6 +1574,11 @@ hipError_t launch_lauum(const double* X, int ldx, double* S, int lds, int d, hip
 hipError_t launch_store_upper_f32(const double* L2, int ld2, float* Hinv, int d, hipStream_t s) {
   const int nt = (int)ceil_div(d, 64);
   hipLaunchKernelGGL(store_upper_kernel, dim3(nt, nt), dim3(256), 0, s, L2, ld2, Hinv, d);
+  return hipGetLastError();
+}
+
+hipError_t launch_store_reversed_f32(const double* X, int ldx, float* Hinv, int d, hipStream_t s) {
+  hipLaunchKernelGGL(store_reversed_kernel, dim3((unsigned)d), dim3(256), 0, s, X, ldx, Hinv, d);
   return hipGetLastError();
 }
 

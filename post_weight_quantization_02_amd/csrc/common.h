@@ -39,9 +39,11 @@ int64_t syrk_kper(int64_t n, int splits);
 constexpr int kSyrkTile = 256;
 
 // fp64 Cholesky route
-// perm == nullptr: A = H + lambda I; else A = P H P^T + lambda I (act-order)
-hipError_t launch_damp_to_f64(const float* H, int d, double percdamp, const int* perm, double* A,
-                              int* flag, hipStream_t s);
+// perm == nullptr: A = H + lambda I; else A = P H P^T + lambda I (act-order).
+// reverse: rows and columns in reversed order, A = J (...) J with J the
+// reversal permutation.
+hipError_t launch_damp_to_f64(const float* H, int d, double percdamp, const int* perm, bool reverse,
+                              double* A, int* flag, hipStream_t s);
 // Cholesky of panel k's 64x64 diagonal block, with its inverse stored in Xi
 hipError_t launch_potrf_diag(double* A, int lda, int d, int k, int* flag, int info_offset,
                              double* Xi, int ldxi, hipStream_t s);
@@ -52,16 +54,20 @@ hipError_t launch_potrf_trsm(double* A, int lda, int d, int k, const double* Xi,
 // with the diagonal block of panel k+1
 hipError_t launch_potrf_update(double* A, int lda, int d, int k, int ncol, int* flag,
                                int info_offset, double* Xi, int ldxi, hipStream_t s);
-// rank-(k1-k0) update of A[k1:, k1:] by the finished outer block [k0, k1)
+// one whole panel step (solve, update, next diagonal block) for a small
+// trailing matrix
 hipError_t launch_potrf_fused(double* A, int lda, int d, int k, int* flag, int info_offset,
                               double* Xi, int ldxi, hipStream_t s);
 hipError_t launch_copy_panels(double* A, int lda, int d, int k0, const double* Xi, int ldxi,
                               hipStream_t s);
+// rank-(k1-k0) update of A[k1:, k1:] by the finished outer block [k0, k1)
 hipError_t launch_potrf_outer_update(double* A, int lda, int d, int k0, int k1, hipStream_t s);
 hipError_t launch_trtri_level(const double* L, int ldl, double* X, int ldx, int d, int half,
                               hipStream_t s);
 hipError_t launch_lauum(const double* X, int ldx, double* S, int lds, int d, hipStream_t s);
 hipError_t launch_store_upper_f32(const double* L2, int ld2, float* Hinv, int d, hipStream_t s);
+// Hinv[i][j] = X[d-1-i][d-1-j] on and above the diagonal, 0 below (fp32)
+hipError_t launch_store_reversed_f32(const double* X, int ldx, float* Hinv, int d, hipStream_t s);
 constexpr int kPanel = 64;
 constexpr int kOuterPanel = 1024;  // columns per outer block of the two-level Cholesky
 

@@ -199,11 +199,26 @@ gptq_status prepare_impl(const float* H, int64_t d, const int* perm, double perc
   // act-order: check that perm is a permutation (Xi is free scratch until the
   // first factorization writes its block inverses)
   if (perm != nullptr) GPTQ_TRY(launch_perm_check(perm, d, reinterpret_cast<int*>(Xi), permbad, s));
-  // A = H + lambda I, or P H P^T + lambda I (fp64, lower triangle); resets the pivot flag.
-  GPTQ_TRY(launch_damp_to_f64(H, di, percdamp, perm, A, flag, s));
+  int hflag[5] = {0, 0, 0, 0, 0};
+  // A = J H_d J (H_d = H + lambda I, or P H P^T + lambda I; J the reversal),
+  // fp64, lower triangle; resets the pivot flag.
+  GPTQ_TRY(launch_damp_to_f64(H, di, percdamp, perm, true, A, flag, s));
   // L = chol(A), in place; the inverted 64x64 diagonal blocks of L land in Xi.
   GPTQ_TRY(potrf(A, di, flag, 0, Xi, s));
   // Xi = L^{-1}: combine the inverted diagonal blocks level by level
+  for (int half = kPanel; half < di; half *= 2) GPTQ_TRY(launch_trtri_level(A, di, Xi, di, di, half, s));
+  // Hinv = J L^{-1} J, the upper Cholesky factor of H_d^{-1}, fp32
+  GPTQ_TRY(launch_store_reversed_f32(Xi, di, Hinv, di, s));
+  GPTQ_TRY(hipMemcpyAsync(hflag, flag, sizeof(hflag), hipMemcpyDeviceToHost, s));
+  GPTQ_TRY(hipStreamSynchronize(s));
+  if (perm != nullptr && hflag[4] != 0) return GPTQ_ERR_INVALID_ARG;
+  if (hflag[0] == 0x7fffffff) return GPTQ_OK;
+
+  // H_d is not numerically positive definite in reversed order: the
+  // three-step route in forward order finds the first failing pivot of
+  // chol(H_d), or of chol(H_d^{-1}) (reported from d + 1 on).
+  GPTQ_TRY(launch_damp_to_f64(H, di, percdamp, perm, false, A, flag, s));
+  GPTQ_TRY(potrf(A, di, flag, 0, Xi, s));
   for (int half = kPanel; half < di; half *= 2) GPTQ_TRY(launch_trtri_level(A, di, Xi, di, di, half, s));
   // A = Xi^T Xi = H_d^{-1} (lower triangle)
   GPTQ_TRY(launch_lauum(Xi, di, A, di, di, s));
@@ -211,11 +226,9 @@ gptq_status prepare_impl(const float* H, int64_t d, const int* perm, double perc
   GPTQ_TRY(potrf(A, di, flag, di, Xi, s));
   // Hinv = L2^T (upper), fp32
   GPTQ_TRY(launch_store_upper_f32(A, di, Hinv, di, s));
-  int hflag[5] = {0, 0, 0, 0, 0};
   GPTQ_TRY(hipMemcpyAsync(hflag, flag, sizeof(hflag), hipMemcpyDeviceToHost, s));
   GPTQ_TRY(hipStreamSynchronize(s));
 #undef GPTQ_TRY
-  if (perm != nullptr && hflag[4] != 0) return GPTQ_ERR_INVALID_ARG;
   if (hflag[0] != 0x7fffffff) {
     if (info) *info = hflag[0];
     return GPTQ_ERR_NOT_PD;
