@@ -54,12 +54,14 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def algorithmic_work(rows, d, n, B=128):
-    """Flops of the method's own work: one triangle of H (with diagonal),
-    4d^3/3 for the three factorizations plus the product of the inverse, the
-    upper-triangular part of the lazy update and the in-block rank-1 updates."""
+def algorithmic_work(rows, d, n, B=128, three_step=False):
+    """Flops of the method's own work: one triangle of H (with diagonal); for
+    Hinv 2d^3/3 (one Cholesky factorization and one triangular inverse), or
+    4d^3/3 on the three-step route (two factorizations, the triangular
+    inverse and the product L^-T L^-1); the upper-triangular part of the lazy
+    update and the in-block rank-1 updates."""
     syrk = float(d) * (d + 1) * n
-    prep = 4.0 * d ** 3 / 3.0
+    prep = (4.0 if three_step else 2.0) * d ** 3 / 3.0
     nb = (d + B - 1) // B
     lazy = 2.0 * rows * B * sum(d - min((b + 1) * B, d) for b in range(nb))
     sweep = 2.0 * rows * (B * (B + 1) / 2.0) * nb
@@ -617,6 +619,10 @@ def main():
                     help="--decode: q|k|v and gate|up stored as one matrix each")
     ap.add_argument("--pipeline", action="store_true",
                     help="layer-by-layer quantization of the MLP up -> ReLU -> down pair")
+    ap.add_argument("--three-step", action="store_true",
+                    help="form Hinv by the pages' three steps (Cholesky, inverse through the "
+                         "factor, upper Cholesky of the inverse) instead of one factorization "
+                         "of the reversed H_d")
     ap.add_argument("--no-graph", action="store_true",
                     help="--decode: launch the step's products one by one instead of a graph")
     args = ap.parse_args()
@@ -671,6 +677,11 @@ def main():
         metric = "ms per 4096x4096 int4 g128 GPTQ layer (incl. H accumulate); % MFMA roofline"
         if args.layer != "attn" or args.groupsize is not None or args.bits is not None:
             metric = f"ms per {rows}x{d} int{L.bits} g{L.groupsize} GPTQ layer (incl. H accumulate)"
+    if args.three_step:
+        if args.act_order:
+            print("--three-step has no act-order variant", file=sys.stderr)
+            sys.exit(2)
+        workload += "; Hinv by the three-step route"
     if args.act_order:
         workload += "; act-order (columns in decreasing order of diag(H), groups in that order)"
         metric = metric.replace(" GPTQ layer", " GPTQ layer with act-order").replace(
@@ -680,6 +691,8 @@ def main():
 
     job = Job(torch, gq, synth, groups, dev, act_order=args.act_order,
               concurrent=not args.serial, lanes=args.lanes)
+    for st in job.streams:
+        st.three_step = args.three_step
     log(f"warmup {args.warmup}")
     for _ in range(args.warmup):
         job.step(False)
@@ -706,7 +719,7 @@ def main():
     # algorithmic work per step
     work = dict(syrk=0.0, prep=0.0, lazy=0.0, sweep=0.0)
     for xs, X, Xd, H, U, _, ls in job.groups:
-        w0 = algorithmic_work(0, xs.d, xs.n)
+        w0 = algorithmic_work(0, xs.d, xs.n, three_step=args.three_step)
         work["syrk"] += w0["syrk"]
         work["prep"] += w0["prep"]
         for Lq, *_ in ls:

@@ -7,7 +7,10 @@
  * little as possible.  The library exposes the three stages of that path:
  *
  *   gptq_hessian_accumulate  H += alpha * X^T X     (alpha = 2 gives H = 2XX^T)
- *   gptq_prepare_hinv        damp H, Cholesky, inverse, upper Cholesky -> Hinv
+ *   gptq_prepare_hinv        damp H -> Hinv, the upper Cholesky factor of
+ *                            the damped inverse (one factorization and one
+ *                            triangular inverse; gptq_prepare_hinv_three_step
+ *                            takes the pages' three steps)
  *   gptq_quantize_layer      blocked column sweep + lazy updates -> codes,
  *                            scales, zeros, per-column losses
  *
@@ -147,6 +150,21 @@ gptq_status gptq_hessian_accumulate(float* H, int64_t d, const void* X, int64_t 
 gptq_status gptq_prepare_hinv(const float* H, int64_t d, double percdamp, float* Hinv,
                               void* workspace, size_t workspace_bytes, int64_t* info,
                               void* stream);
+
+/*
+ * gptq_prepare_hinv_three_step -- the same Hinv as gptq_prepare_hinv, formed
+ * by the three steps the Cholesky question of "GPTQ, Line by Line" and the
+ * "GPTQ-style round-to-nearest ..." listing name: the lower Cholesky factor
+ * L of H_d, H_d^{-1} = L^{-T} L^{-1} (triangular inverse, then the product),
+ * and the upper Cholesky factor of H_d^{-1} (a second factorization).  Twice
+ * the fp64 work of gptq_prepare_hinv; the results agree to fp64 rounding.
+ *
+ *   Arguments, workspace, errors, info and synchronization as
+ *   gptq_prepare_hinv.
+ */
+gptq_status gptq_prepare_hinv_three_step(const float* H, int64_t d, double percdamp, float* Hinv,
+                                         void* workspace, size_t workspace_bytes,
+                                         int64_t* info, void* stream);
 
 /*
  * gptq_quantize_layer -- the GPTQ column sweep.

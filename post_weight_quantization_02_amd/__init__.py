@@ -29,6 +29,7 @@ from ._lib import (  # noqa: F401
     packed_words,
     prepare_hinv,
     prepare_hinv_perm,
+    prepare_hinv_three_step,
     quantize_layer,
     quantize_layer_perm,
     status_string,

@@ -61,6 +61,8 @@ lib.gptq_quantize_layer.argtypes = [_p, _int, _i64, _i64, _i64, _p, _int, _int, 
                                     _p, _p, _p, _p, _p, _sz, _p]
 lib.gptq_act_order.restype = _int
 lib.gptq_act_order.argtypes = [_p, _i64, _p, _p]
+lib.gptq_prepare_hinv_three_step.restype = _int
+lib.gptq_prepare_hinv_three_step.argtypes = lib.gptq_prepare_hinv.argtypes
 lib.gptq_prepare_hinv_perm.restype = _int
 lib.gptq_prepare_hinv_perm.argtypes = [_p, _i64, _p, ctypes.c_double, _p, _p, _sz,
                                        ctypes.POINTER(ctypes.c_int64), _p]
@@ -217,6 +219,23 @@ def prepare_hinv(H, percdamp: float = 0.01, out=None, workspace=None, stream=Non
     """Hinv (d x d fp32, upper triangular) from H. Raises GPTQError with
     status GPTQ_ERR_NOT_PD and the failing pivot in .info."""
     return prepare_hinv_perm(H, None, percdamp, out, workspace, stream)
+
+
+def prepare_hinv_three_step(H, percdamp: float = 0.01, out=None, workspace=None, stream=None):
+    """prepare_hinv through the pages' three steps (Cholesky, inverse through
+    the factor, upper Cholesky of the inverse): gptq_prepare_hinv_three_step."""
+    torch = _torch()
+    d = _check_H(H)
+    if out is None:
+        out = torch.empty((d, d), dtype=torch.float32, device=H.device)
+    _check_out(out, (d, d), torch.float32, H.device, "out")
+    ws, wsb = _workspace(workspace_bytes(OP_PREPARE, 0, d, 0), H.device, workspace, stream)
+    info = ctypes.c_int64(0)
+    st = lib.gptq_prepare_hinv_three_step(H.data_ptr(), d, float(percdamp), out.data_ptr(),
+                                          ws.data_ptr(), wsb, ctypes.byref(info),
+                                          _stream_ptr(stream, H.device))
+    _check(st, "gptq_prepare_hinv_three_step", info.value)
+    return out
 
 
 def act_order(H, out=None, stream=None):

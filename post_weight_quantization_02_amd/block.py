@@ -42,6 +42,7 @@ class BlockStream:
     layers: List[BlockLayer]
     percdamp: float = 0.01
     perm: object = None
+    three_step: bool = False  # Hinv by the pages' three steps (no act-order)
 
 
 def allocate_outputs(torch, W, groupsize: int, act_order: bool = False):
@@ -91,6 +92,9 @@ def quantize_streams(streams: List[BlockStream], workspace, act_order: bool = Fa
             _lib.act_order(st.H, out=st.perm, stream=stream)
             _lib.prepare_hinv_perm(st.H, st.perm, st.percdamp, out=st.U, workspace=workspace,
                                    stream=stream)
+        elif st.three_step:
+            _lib.prepare_hinv_three_step(st.H, st.percdamp, out=st.U, workspace=workspace,
+                                         stream=stream)
         else:
             _lib.prepare_hinv(st.H, st.percdamp, out=st.U, workspace=workspace, stream=stream)
         note("prep", False)

@@ -174,7 +174,8 @@ namespace {
 // The preparation with an optional act-order permutation (perm == nullptr:
 // the identity).  Validation of the scalar arguments is done by the callers.
 gptq_status prepare_impl(const float* H, int64_t d, const int* perm, double percdamp, float* Hinv,
-                         void* workspace, size_t workspace_bytes, int64_t* info, void* stream) {
+                         void* workspace, size_t workspace_bytes, int64_t* info, void* stream,
+                         bool three_step = false) {
   if (info) *info = 0;
   if (d < 1 || d > 65536 || H == nullptr || Hinv == nullptr) return GPTQ_ERR_INVALID_ARG;
   if (!(percdamp >= 0.0) || percdamp > 1e6) return GPTQ_ERR_INVALID_ARG;
@@ -200,23 +201,26 @@ gptq_status prepare_impl(const float* H, int64_t d, const int* perm, double perc
   // first factorization writes its block inverses)
   if (perm != nullptr) GPTQ_TRY(launch_perm_check(perm, d, reinterpret_cast<int*>(Xi), permbad, s));
   int hflag[5] = {0, 0, 0, 0, 0};
-  // A = J H_d J (H_d = H + lambda I, or P H P^T + lambda I; J the reversal),
-  // fp64, lower triangle; resets the pivot flag.
-  GPTQ_TRY(launch_damp_to_f64(H, di, percdamp, perm, true, A, flag, s));
-  // L = chol(A), in place; the inverted 64x64 diagonal blocks of L land in Xi.
-  GPTQ_TRY(potrf(A, di, flag, 0, Xi, s));
-  // Xi = L^{-1}: combine the inverted diagonal blocks level by level
-  for (int half = kPanel; half < di; half *= 2) GPTQ_TRY(launch_trtri_level(A, di, Xi, di, di, half, s));
-  // Hinv = J L^{-1} J, the upper Cholesky factor of H_d^{-1}, fp32
-  GPTQ_TRY(launch_store_reversed_f32(Xi, di, Hinv, di, s));
-  GPTQ_TRY(hipMemcpyAsync(hflag, flag, sizeof(hflag), hipMemcpyDeviceToHost, s));
-  GPTQ_TRY(hipStreamSynchronize(s));
-  if (perm != nullptr && hflag[4] != 0) return GPTQ_ERR_INVALID_ARG;
-  if (hflag[0] == 0x7fffffff) return GPTQ_OK;
+  if (!three_step) {
+    // A = J H_d J (H_d = H + lambda I, or P H P^T + lambda I; J the reversal),
+    // fp64, lower triangle; resets the pivot flag.
+    GPTQ_TRY(launch_damp_to_f64(H, di, percdamp, perm, true, A, flag, s));
+    // L = chol(A), in place; the inverted 64x64 diagonal blocks of L land in Xi.
+    GPTQ_TRY(potrf(A, di, flag, 0, Xi, s));
+    // Xi = L^{-1}: combine the inverted diagonal blocks level by level
+    for (int half = kPanel; half < di; half *= 2)
+      GPTQ_TRY(launch_trtri_level(A, di, Xi, di, di, half, s));
+    // Hinv = J L^{-1} J, the upper Cholesky factor of H_d^{-1}, fp32
+    GPTQ_TRY(launch_store_reversed_f32(Xi, di, Hinv, di, s));
+    GPTQ_TRY(hipMemcpyAsync(hflag, flag, sizeof(hflag), hipMemcpyDeviceToHost, s));
+    GPTQ_TRY(hipStreamSynchronize(s));
+    if (perm != nullptr && hflag[4] != 0) return GPTQ_ERR_INVALID_ARG;
+    if (hflag[0] == 0x7fffffff) return GPTQ_OK;
+  }
 
-  // H_d is not numerically positive definite in reversed order: the
-  // three-step route in forward order finds the first failing pivot of
-  // chol(H_d), or of chol(H_d^{-1}) (reported from d + 1 on).
+  // The pages' three steps in forward order: on request, or when H_d is
+  // not numerically positive definite in reversed order, to find the first
+  // failing pivot of chol(H_d), or of chol(H_d^{-1}) (reported from d + 1 on).
   GPTQ_TRY(launch_damp_to_f64(H, di, percdamp, perm, false, A, flag, s));
   GPTQ_TRY(potrf(A, di, flag, 0, Xi, s));
   for (int half = kPanel; half < di; half *= 2) GPTQ_TRY(launch_trtri_level(A, di, Xi, di, di, half, s));
@@ -229,6 +233,7 @@ gptq_status prepare_impl(const float* H, int64_t d, const int* perm, double perc
   GPTQ_TRY(hipMemcpyAsync(hflag, flag, sizeof(hflag), hipMemcpyDeviceToHost, s));
   GPTQ_TRY(hipStreamSynchronize(s));
 #undef GPTQ_TRY
+  if (perm != nullptr && hflag[4] != 0) return GPTQ_ERR_INVALID_ARG;
   if (hflag[0] != 0x7fffffff) {
     if (info) *info = hflag[0];
     return GPTQ_ERR_NOT_PD;
@@ -338,6 +343,13 @@ gptq_status gptq_prepare_hinv(const float* H, int64_t d, double percdamp, float*
                               void* workspace, size_t workspace_bytes, int64_t* info,
                               void* stream) {
   return prepare_impl(H, d, nullptr, percdamp, Hinv, workspace, workspace_bytes, info, stream);
+}
+
+gptq_status gptq_prepare_hinv_three_step(const float* H, int64_t d, double percdamp, float* Hinv,
+                                         void* workspace, size_t workspace_bytes, int64_t* info,
+                                         void* stream) {
+  return prepare_impl(H, d, nullptr, percdamp, Hinv, workspace, workspace_bytes, info, stream,
+                      true);
 }
 
 gptq_status gptq_quantize_layer(const void* W, int w_dtype, int64_t rows, int64_t cols,

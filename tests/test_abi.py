@@ -79,23 +79,24 @@ def test_accumulate_validation():
     assert _acc(n=0, X=None) == gq.GPTQ_OK  # empty chunk: nothing to do
 
 
-def _prep(H=FAKE, d=16, p=0.01, out=FAKE, ws=FAKE, wsb=None):
+def _prep(H=FAKE, d=16, p=0.01, out=FAKE, ws=FAKE, wsb=None, fn="gptq_prepare_hinv"):
     if wsb is None:
         wsb = gq.workspace_bytes(gq.OP_PREPARE, 0, d, 0)
     info = ctypes.c_int64(-5)
-    st = lib.gptq_prepare_hinv(H, d, p, out, ws, wsb, ctypes.byref(info), None)
+    st = getattr(lib, fn)(H, d, p, out, ws, wsb, ctypes.byref(info), None)
     return st, info.value
 
 
-def test_prepare_validation():
-    assert _prep(H=None)[0] == gq.GPTQ_ERR_INVALID_ARG
-    assert _prep(out=None)[0] == gq.GPTQ_ERR_INVALID_ARG
-    assert _prep(d=0)[0] == gq.GPTQ_ERR_INVALID_ARG
-    assert _prep(p=-0.1)[0] == gq.GPTQ_ERR_INVALID_ARG
-    assert _prep(p=float("nan"))[0] == gq.GPTQ_ERR_INVALID_ARG
-    assert _prep(ws=None)[0] == gq.GPTQ_ERR_WORKSPACE
-    assert _prep(wsb=100)[0] == gq.GPTQ_ERR_WORKSPACE
-    st, info = _prep(d=0)
+@pytest.mark.parametrize("fn", ["gptq_prepare_hinv", "gptq_prepare_hinv_three_step"])
+def test_prepare_validation(fn):
+    assert _prep(H=None, fn=fn)[0] == gq.GPTQ_ERR_INVALID_ARG
+    assert _prep(out=None, fn=fn)[0] == gq.GPTQ_ERR_INVALID_ARG
+    assert _prep(d=0, fn=fn)[0] == gq.GPTQ_ERR_INVALID_ARG
+    assert _prep(p=-0.1, fn=fn)[0] == gq.GPTQ_ERR_INVALID_ARG
+    assert _prep(p=float("nan"), fn=fn)[0] == gq.GPTQ_ERR_INVALID_ARG
+    assert _prep(ws=None, fn=fn)[0] == gq.GPTQ_ERR_WORKSPACE
+    assert _prep(wsb=100, fn=fn)[0] == gq.GPTQ_ERR_WORKSPACE
+    st, info = _prep(d=0, fn=fn)
     assert info == 0  # info is cleared on every call
 
 

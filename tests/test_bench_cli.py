@@ -21,6 +21,8 @@ def test_algorithmic_work_closed_forms():
     import bench
     w = bench.algorithmic_work(4096, 4096, 262144)
     assert w["syrk"] == 4096 * 4097 * 262144            # d(d+1)n flops: one triangle
-    assert w["prep"] == 4 * 4096 ** 3 / 3               # potrf, trtri, lauum, potrf
+    assert w["prep"] == 2 * 4096 ** 3 / 3               # potrf, trtri
+    assert bench.algorithmic_work(4096, 4096, 262144, three_step=True)["prep"] == \
+        4 * 4096 ** 3 / 3                                # potrf, trtri, lauum, potrf
     nb = 4096 // 128
     assert w["lazy"] == 4096 * 128 * 128 * nb * (nb - 1)  # rows * B^2 * nb (nb - 1)

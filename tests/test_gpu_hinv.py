@@ -15,10 +15,12 @@ def env():
     return torch, gq
 
 
-def _hinv(env, H32, p=0.01):
+def _hinv(env, H32, p=0.01, three_step=False):
+    """Hinv from gptq_prepare_hinv (one factorization of the reversed H_d),
+    or from gptq_prepare_hinv_three_step (the pages' three steps)."""
     torch, gq = env
     Ht = torch.from_numpy(np.ascontiguousarray(H32, dtype=np.float32)).cuda()
-    U = gq.prepare_hinv(Ht, p)
+    U = (gq.prepare_hinv_three_step if three_step else gq.prepare_hinv)(Ht, p)
     torch.cuda.synchronize()
     return U.cpu().numpy()
 
@@ -32,13 +34,15 @@ def test_hinv_matches_oracle(env, d, n):
     X = synth.activations(x)
     H32 = oracle.hessian([X], d).astype(np.float32)  # the GPU input: fp32 H
     Uref, lam = oracle.hinv_upper(H32.astype(np.float64), 0.01)
-    U = _hinv(env, H32)
-    assert np.all(np.tril(U, -1) == 0)
-    assert np.all(np.diag(U) > 0)
-    err = np.abs(U - Uref).max() / np.abs(Uref).max()
-    assert err <= 2e-6, err
-    rel = np.abs(U - Uref) / np.maximum(np.abs(Uref), 1e-30)
-    assert np.all(rel[np.triu_indices(d)][np.abs(Uref[np.triu_indices(d)]) > 1e-3 * np.abs(Uref).max()] < 1e-4)
+    big = np.abs(Uref[np.triu_indices(d)]) > 1e-3 * np.abs(Uref).max()
+    for three_step in (False, True):
+        U = _hinv(env, H32, three_step=three_step)
+        assert np.all(np.tril(U, -1) == 0)
+        assert np.all(np.diag(U) > 0)
+        err = np.abs(U - Uref).max() / np.abs(Uref).max()
+        assert err <= 2e-6, (three_step, err)
+        rel = np.abs(U - Uref) / np.maximum(np.abs(Uref), 1e-30)
+        assert np.all(rel[np.triu_indices(d)][big] < 1e-4), three_step
 
 
 def test_diagonal_H(env):
@@ -91,7 +95,8 @@ def test_nan_reports_pivot_one(env):
 
 @pytest.mark.parametrize("r,c,v", [(6, 4, np.nan), (9, 8, np.nan), (20, 3, np.nan),
                                    (63, 0, np.inf), (64, 10, np.nan), (130, 129, -np.inf)])
-def test_non_finite_entry_fails_at_its_row(env, r, c, v):
+@pytest.mark.parametrize("three_step", [False, True])
+def test_non_finite_entry_fails_at_its_row(env, r, c, v, three_step):
     """d = 200, H = 2I with one non-finite entry below the diagonal at (r, c):
     row r's pivot is the first that is not > 0 (the oracle reports r + 1).
     The rows above r see the entry only through their own upper entries,
@@ -105,7 +110,7 @@ def test_non_finite_entry_fails_at_its_row(env, r, c, v):
     with pytest.raises(oracle.NotPositiveDefinite) as ref:
         oracle.hinv_upper(H.astype(np.float64), 0.0)
     with pytest.raises(gq.GPTQError) as ei:
-        _hinv(env, H, 0.0)
+        _hinv(env, H, 0.0, three_step=three_step)
     assert ei.value.status == gq.GPTQ_ERR_NOT_PD
     assert ei.value.info == ref.value.info == r + 1
 
@@ -117,6 +122,24 @@ def test_upper_triangle_of_H_is_not_read(env):
     Hp = H.copy()
     Hp[np.triu_indices(150, 1)] = np.nan
     np.testing.assert_array_equal(_hinv(env, H), _hinv(env, Hp))
+    np.testing.assert_array_equal(_hinv(env, H, three_step=True),
+                                  _hinv(env, Hp, three_step=True))
+
+
+def test_routes_agree_on_an_ill_conditioned_hessian(env):
+    """Dead channels and 60% zeros (the MLP down projection's statistics), so
+    H_d is singular but for the damping.  The reversed one-factorization route
+    and the three-step route give the same Hinv to fp64 rounding, so the fp32
+    results differ by at most a few units in the last place of the largest
+    entry."""
+    x = synth.X_DOWN.scaled(d=1500, n=12000)
+    X = synth.activations(x)
+    H32 = oracle.hessian([X], 1500).astype(np.float32)
+    U1 = _hinv(env, H32)
+    U3 = _hinv(env, H32, three_step=True)
+    assert np.abs(U1 - U3).max() <= 1e-6 * np.abs(U3).max()
+    Uref, _ = oracle.hinv_upper(H32.astype(np.float64), 0.01)
+    assert np.abs(U1 - Uref).max() <= 2e-6 * np.abs(Uref).max()
 
 
 def test_two_level_cholesky_matches_oracle(env):
@@ -131,7 +154,8 @@ def test_two_level_cholesky_matches_oracle(env):
     Z = rng.standard_normal((d, r)) / np.sqrt(r)
     H32 = (Z @ Z.T + 0.05 * np.eye(d)).astype(np.float32)
     Uref, _ = oracle.hinv_upper(H32.astype(np.float64), 0.01)
-    U = _hinv(env, H32)
-    assert np.all(np.tril(U, -1) == 0)
-    err = np.abs(U - Uref).max() / np.abs(Uref).max()
-    assert err <= 2e-6, err
+    for three_step in (False, True):
+        U = _hinv(env, H32, three_step=three_step)
+        assert np.all(np.tril(U, -1) == 0)
+        err = np.abs(U - Uref).max() / np.abs(Uref).max()
+        assert err <= 2e-6, (three_step, err)
