@@ -710,6 +710,25 @@ def main():
     if len(job.groups) == 1:
         log("ms per timed step (phase sum):",
             [round(sum(per[k][i] for k in per), 3) for i in range(args.steps)])
+    # The other Hinv route on the same H, after the timed steps: the three-step
+    # preparation when the step used one factorization, and the other way
+    # round (event-timed, median of 3; not part of the step).
+    prep_other = None
+    if not args.act_order and len(job.groups) == 1:
+        st = job.streams[0]
+        fn = gq.prepare_hinv if args.three_step else gq.prepare_hinv_three_step
+        ts = []
+        for _ in range(3):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn(st.H, st.percdamp, out=st.U, workspace=job.ws)
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        prep_other = {"route": "one factorization of the reversed H_d" if args.three_step
+                      else "three steps (Cholesky, inverse through the factor, re-factorization)",
+                      "ms": round(sorted(ts)[1], 4)}
+        log("other Hinv route:", prep_other)
     # library peaks after the timed steps, so their full-power GEMMs do not
     # precede the measurement
     peaks = None if args.no_peaks else measured_peaks(torch, dev)
@@ -765,6 +784,12 @@ def main():
         "data": "synthetic (seeded low-rank-plus-noise activations, Gaussian weights)",
         "config": {"workload": workload,
                    "phase_ms": {k: round(v, 4) for k, v in ph.items()},
+                   "prep_route": ("three steps (Cholesky, inverse through the factor, "
+                                  "re-factorization; gptq_prepare_hinv_three_step)"
+                                  if args.three_step else
+                                  "one factorization of the reversed H_d and one triangular "
+                                  "inverse (gptq_prepare_hinv)"),
+                   "prep_other_route": prep_other,
                    "phase_floor_ms": {k: round(v, 4) for k, v in floor.items()},
                    "phase_frac_of_floor": {k: round(floor[k] / ph[k], 4) for k in floor},
                    "effective_tflops": round(eff_tflops, 2),
