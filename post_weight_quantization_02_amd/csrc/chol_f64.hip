@@ -1083,44 +1083,70 @@ __global__ __launch_bounds__(256) void gemm64_f64_kernel(GemmDesc g) {
     for (int b = 0; b < 2; ++b) acc[a][b] = f64x4{0.0, 0.0, 0.0, 0.0};
 
   // Loads: a uniform base per chunk plus a 32-bit per-thread byte offset
-  // (global_load with a scalar base).  The row part of each offset is fixed;
-  // the k part is clamped to the chunk's valid range, so every address is
-  // inside the operand (the bounds and triangle masks are applied at the LDS
-  // store), and the MFMAs of the current chunk never wait for these loads.
+  // (global_load with a scalar base).  The offsets are computed once, with the
+  // row clamped into the operand; only the last chunk clamps k to its valid
+  // range, so every address is inside the operand (the bounds and triangle
+  // masks are applied at the LDS store, and skipped for chunks that need
+  // none), and the MFMAs of the current chunk never wait for these loads.
   // Offsets stay below 2^31 for leading dimensions up to 65536.
   constexpr int NLD = GT * GK / 256;
   double av[NLD], bv[NLD];
-  uint32_t aro[NLD], bro[NLD];
-  int akk[NLD], bkk[NLD];
+  uint32_t aoff[NLD], boff[NLD];
   const uint32_t lda8 = (uint32_t)g.lda * 8u, ldb8 = (uint32_t)g.ldb * 8u;
+  const uint32_t ska = AK ? 8u : lda8, skb = BN ? ldb8 : 8u;  // byte stride of one k
 #pragma unroll
   for (int q = 0; q < NLD; ++q) {
     const int e = tid + 256 * q;
     const int kk = AK ? (e % GK) : (e / GT);
     const int mm = min(AK ? (e / GK) : (e % GT), g.M - 1 - m0);
-    aro[q] = AK ? (uint32_t)mm * lda8 : (uint32_t)mm * 8u;
-    akk[q] = kk;
+    aoff[q] = (AK ? (uint32_t)mm * lda8 : (uint32_t)mm * 8u) + (uint32_t)kk * ska;
     const int kb = BN ? (e / GT) : (e % GK);
     const int nn = min(BN ? (e % GT) : (e / GK), g.N - 1 - n0);
-    bro[q] = BN ? (uint32_t)nn * 8u : (uint32_t)nn * ldb8;
-    bkk[q] = kb;
+    boff[q] = (BN ? (uint32_t)nn * 8u : (uint32_t)nn * ldb8) + (uint32_t)kb * skb;
   }
   auto gload = [&](int kc) {
-    const int lim = k1 - 1 - kc;
     const char* abase = reinterpret_cast<const char*>(
         Ap + (AK ? (int64_t)m0 * g.lda + kc : (int64_t)kc * g.lda + m0));
     const char* bbase = reinterpret_cast<const char*>(
         Bp + (BN ? (int64_t)kc * g.ldb + n0 : (int64_t)n0 * g.ldb + kc));
+    if (kc + GK <= k1) {  // whole chunk: the fixed offsets
+#pragma unroll
+      for (int q = 0; q < NLD; ++q) {
+        av[q] = *reinterpret_cast<const double*>(abase + aoff[q]);
+        bv[q] = *reinterpret_cast<const double*>(bbase + boff[q]);
+      }
+      return;
+    }
+    const int lim = k1 - 1 - kc;  // last chunk: k clamped to lim
 #pragma unroll
     for (int q = 0; q < NLD; ++q) {
-      const uint32_t ka = (uint32_t)min(akk[q], lim), kb = (uint32_t)min(bkk[q], lim);
-      const uint32_t oa = aro[q] + (AK ? ka * 8u : ka * lda8);
-      const uint32_t ob = bro[q] + (BN ? kb * ldb8 : kb * 8u);
+      const int e = tid + 256 * q;
+      const int kk = AK ? (e % GK) : (e / GT);
+      const int kb = BN ? (e / GT) : (e % GK);
+      const uint32_t oa = aoff[q] - (uint32_t)(kk - min(kk, lim)) * ska;
+      const uint32_t ob = boff[q] - (uint32_t)(kb - min(kb, lim)) * skb;
       av[q] = *reinterpret_cast<const double*>(abase + oa);
       bv[q] = *reinterpret_cast<const double*>(bbase + ob);
     }
   };
   auto lstore = [&](int buf, int kc) {
+    // uniform: every element of the chunk in bounds and inside both triangles
+    const bool in_k = kc + GK <= k1;
+    const bool full_a = in_k && m0 + GT <= g.M &&
+                        (g.trA == 0 || (g.trA == 1 && m0 >= kc + GK - 1) ||
+                         (g.trA == 2 && m0 + GT - 1 <= kc));
+    const bool full_b = in_k && n0 + GT <= g.N &&
+                        (g.trB == 0 || (g.trB == 1 && kc >= n0 + GT - 1) ||
+                         (g.trB == 2 && kc + GK - 1 <= n0));
+    if (full_a && full_b) {
+#pragma unroll
+      for (int q = 0; q < NLD; ++q) {
+        const int e = tid + 256 * q;
+        a_at(buf, AK ? (e / GK) : (e % GT), AK ? (e % GK) : (e / GT)) = av[q];
+        b_at(buf, BN ? (e / GT) : (e % GK), BN ? (e % GT) : (e / GK)) = bv[q];
+      }
+      return;
+    }
 #pragma unroll
     for (int q = 0; q < NLD; ++q) {
       const int e = tid + 256 * q;
@@ -1254,44 +1280,70 @@ __global__ __launch_bounds__(256, 2) void gemm128_f64_kernel(GemmDesc g) {
     for (int b = 0; b < 4; ++b) acc[a][b] = f64x4{0.0, 0.0, 0.0, 0.0};
 
   // Loads: a uniform base per chunk plus a 32-bit per-thread byte offset
-  // (global_load with a scalar base).  The row part of each offset is fixed;
-  // the k part is clamped to the chunk's valid range, so every address is
-  // inside the operand (the bounds and triangle masks are applied at the LDS
-  // store), and the MFMAs of the current chunk never wait for these loads.
+  // (global_load with a scalar base).  The offsets are computed once, with the
+  // row clamped into the operand; only the last chunk clamps k to its valid
+  // range, so every address is inside the operand (the bounds and triangle
+  // masks are applied at the LDS store, and skipped for chunks that need
+  // none), and the MFMAs of the current chunk never wait for these loads.
   // Offsets stay below 2^31 for leading dimensions up to 65536.
   constexpr int NLD = GT2 * GK / 256;
   double av[NLD], bv[NLD];
-  uint32_t aro[NLD], bro[NLD];
-  int akk[NLD], bkk[NLD];
+  uint32_t aoff[NLD], boff[NLD];
   const uint32_t lda8 = (uint32_t)g.lda * 8u, ldb8 = (uint32_t)g.ldb * 8u;
+  const uint32_t ska = AK ? 8u : lda8, skb = BN ? ldb8 : 8u;  // byte stride of one k
 #pragma unroll
   for (int q = 0; q < NLD; ++q) {
     const int e = tid + 256 * q;
     const int kk = AK ? (e % GK) : (e / GT2);
     const int mm = min(AK ? (e / GK) : (e % GT2), g.M - 1 - m0);
-    aro[q] = AK ? (uint32_t)mm * lda8 : (uint32_t)mm * 8u;
-    akk[q] = kk;
+    aoff[q] = (AK ? (uint32_t)mm * lda8 : (uint32_t)mm * 8u) + (uint32_t)kk * ska;
     const int kb = BN ? (e / GT2) : (e % GK);
     const int nn = min(BN ? (e % GT2) : (e / GK), g.N - 1 - n0);
-    bro[q] = BN ? (uint32_t)nn * 8u : (uint32_t)nn * ldb8;
-    bkk[q] = kb;
+    boff[q] = (BN ? (uint32_t)nn * 8u : (uint32_t)nn * ldb8) + (uint32_t)kb * skb;
   }
   auto gload = [&](int kc) {
-    const int lim = k1 - 1 - kc;
     const char* abase = reinterpret_cast<const char*>(
         Ap + (AK ? (int64_t)m0 * g.lda + kc : (int64_t)kc * g.lda + m0));
     const char* bbase = reinterpret_cast<const char*>(
         Bp + (BN ? (int64_t)kc * g.ldb + n0 : (int64_t)n0 * g.ldb + kc));
+    if (kc + GK <= k1) {  // whole chunk: the fixed offsets
+#pragma unroll
+      for (int q = 0; q < NLD; ++q) {
+        av[q] = *reinterpret_cast<const double*>(abase + aoff[q]);
+        bv[q] = *reinterpret_cast<const double*>(bbase + boff[q]);
+      }
+      return;
+    }
+    const int lim = k1 - 1 - kc;  // last chunk: k clamped to lim
 #pragma unroll
     for (int q = 0; q < NLD; ++q) {
-      const uint32_t ka = (uint32_t)min(akk[q], lim), kb = (uint32_t)min(bkk[q], lim);
-      const uint32_t oa = aro[q] + (AK ? ka * 8u : ka * lda8);
-      const uint32_t ob = bro[q] + (BN ? kb * ldb8 : kb * 8u);
+      const int e = tid + 256 * q;
+      const int kk = AK ? (e % GK) : (e / GT2);
+      const int kb = BN ? (e / GT2) : (e % GK);
+      const uint32_t oa = aoff[q] - (uint32_t)(kk - min(kk, lim)) * ska;
+      const uint32_t ob = boff[q] - (uint32_t)(kb - min(kb, lim)) * skb;
       av[q] = *reinterpret_cast<const double*>(abase + oa);
       bv[q] = *reinterpret_cast<const double*>(bbase + ob);
     }
   };
   auto lstore = [&](int buf, int kc) {
+    // uniform: every element of the chunk in bounds and inside both triangles
+    const bool in_k = kc + GK <= k1;
+    const bool full_a = in_k && m0 + GT2 <= g.M &&
+                        (g.trA == 0 || (g.trA == 1 && m0 >= kc + GK - 1) ||
+                         (g.trA == 2 && m0 + GT2 - 1 <= kc));
+    const bool full_b = in_k && n0 + GT2 <= g.N &&
+                        (g.trB == 0 || (g.trB == 1 && kc >= n0 + GT2 - 1) ||
+                         (g.trB == 2 && kc + GK - 1 <= n0));
+    if (full_a && full_b) {
+#pragma unroll
+      for (int q = 0; q < NLD; ++q) {
+        const int e = tid + 256 * q;
+        a_at(buf, AK ? (e / GK) : (e % GT2), AK ? (e % GK) : (e / GT2)) = av[q];
+        b_at(buf, BN ? (e / GT2) : (e % GK), BN ? (e % GT2) : (e / GK)) = bv[q];
+      }
+      return;
+    }
 #pragma unroll
     for (int q = 0; q < NLD; ++q) {
       const int e = tid + 256 * q;
