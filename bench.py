@@ -623,6 +623,8 @@ def main():
                     help="form Hinv by the pages' three steps (Cholesky, inverse through the "
                          "factor, upper Cholesky of the inverse) instead of one factorization "
                          "of the reversed H_d")
+    ap.add_argument("--no-other-route", action="store_true",
+                    help="skip timing the other Hinv route after the timed steps (kernel traces)")
     ap.add_argument("--no-graph", action="store_true",
                     help="--decode: launch the step's products one by one instead of a graph")
     args = ap.parse_args()
@@ -714,7 +716,7 @@ def main():
     # preparation when the step used one factorization, and the other way
     # round (event-timed, median of 3; not part of the step).
     prep_other = None
-    if not args.act_order and len(job.groups) == 1:
+    if not args.act_order and not args.no_other_route and len(job.groups) == 1:
         st = job.streams[0]
         fn = gq.prepare_hinv if args.three_step else gq.prepare_hinv_three_step
         ts = []
