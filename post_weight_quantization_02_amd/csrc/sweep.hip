@@ -569,12 +569,34 @@ __global__ __launch_bounds__(256, 2) void lazy_kernel(float* __restrict__ Wk, in
   // Loads read in-bounds addresses unconditionally and keep the raw values;
   // entries past K, past c1 or past the last row are zeroed (or ignored)
   // when the chunk goes to LDS, so no MFMA waits for the next chunk's loads.
+  // Whole chunks of tiles inside the rows and columns skip the clamps and
+  // masks (vector loads of Hinv when its rows are 16-byte aligned).
   // A = Err[r0.., k0..k1]: the row stride ldk is a multiple of 128 and k0 a
   // multiple of 128, so a whole chunk stays inside each (clamped) row.
   // B = Hinv[k0..k1, n0..]: row and column indices are clamped.
   constexpr int NR = ALL ? 4 : 1;  // register sets of chunk loads in flight
   float4 av[NR][AV], bv[NR][4];
+  // uniform: the chunk is whole, the tile inside the rows and columns, and
+  // Hinv's rows 16-byte aligned, so loads and LDS stores need no clamps or masks
+  const bool vec_b = (reinterpret_cast<uintptr_t>(Hinv) % 16 == 0) && (cols % 4 == 0);
+  const bool tile_in = r0 + TM <= rows && n0 + LT <= c1 && vec_b;
+  auto whole = [&](int kc) { return tile_in && kc + LK <= K; };
   auto gload = [&](int set, int kc) {
+    if (whole(kc)) {
+#pragma unroll
+      for (int q = 0; q < AV; ++q) {
+        const int e = tid + 256 * q;
+        const int m = e >> 3, kk = (e & 7) * 4;
+        av[set][q] = *reinterpret_cast<const float4*>(Err + (r0 + m) * ldk + k0 + kc + kk);
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int e = tid + 256 * q;
+        const int kb = e >> 5, nn = (e & 31) * 4;
+        bv[set][q] = *reinterpret_cast<const float4*>(Hinv + (int64_t)(k0 + kc + kb) * cols + n0 + nn);
+      }
+      return;
+    }
 #pragma unroll
     for (int q = 0; q < AV; ++q) {
       const int e = tid + 256 * q;
@@ -595,6 +617,19 @@ __global__ __launch_bounds__(256, 2) void lazy_kernel(float* __restrict__ Wk, in
     }
   };
   auto lstore = [&](int set, int buf, int kc) {
+    if (whole(kc)) {
+#pragma unroll
+      for (int q = 0; q < AV; ++q) {
+        const int e = tid + 256 * q;
+        *reinterpret_cast<float4*>(&As[buf][(e >> 3) * PA + (e & 7) * 4]) = av[set][q];
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int e = tid + 256 * q;
+        *reinterpret_cast<float4*>(&Bs[buf][e >> 5][(e & 31) * 4]) = bv[set][q];
+      }
+      return;
+    }
 #pragma unroll
     for (int q = 0; q < AV; ++q) {
       const int e = tid + 256 * q;
