@@ -26,3 +26,11 @@ def test_algorithmic_work_closed_forms():
         4 * 4096 ** 3 / 3                                # potrf, trtri, lauum, potrf
     nb = 4096 // 128
     assert w["lazy"] == 4096 * 128 * 128 * nb * (nb - 1)  # rows * B^2 * nb (nb - 1)
+
+
+def test_three_step_has_no_act_order_variant():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--three-step",
+                        "--act-order"], capture_output=True, text=True, timeout=300)
+    assert r.returncode == 2
+    assert "--three-step has no act-order variant" in r.stderr
+    assert r.stdout.strip() == ""
